@@ -1,0 +1,272 @@
+"""CPU oracle for the quantized routed-expert MoE feed-forward (test infrastructure).
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline
+leg may import this package.  The GPU library never uses it.  All arithmetic
+lives in ``qre_oracle.c``; this module only marshals numpy arrays through
+ctypes.  Every function cites, in the C source, the passage of the pages it
+follows.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qre_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+GROUP = 128
+
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fopenmp", "-Wall"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain C, no intrinsics, no BLAS)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        L = C.CDLL(_LIB)
+        P = C.c_void_p
+        i64, i32 = C.c_int64, C.c_int32
+        L.orc_round_bf16.restype = C.c_double
+        L.orc_round_bf16.argtypes = [C.c_double]
+        L.orc_round_fp16.restype = C.c_double
+        L.orc_round_fp16.argtypes = [C.c_double]
+        L.orc_bf16_from_double.restype = C.c_uint16
+        L.orc_bf16_from_double.argtypes = [C.c_double]
+        L.orc_fp16_from_double.restype = C.c_uint16
+        L.orc_fp16_from_double.argtypes = [C.c_double]
+        L.orc_fp16_to_double.restype = C.c_double
+        L.orc_fp16_to_double.argtypes = [C.c_uint16]
+        L.orc_quantize_weights.restype = C.c_int
+        L.orc_quantize_weights.argtypes = [P, i64, i64, C.c_int, P, P]
+        L.orc_unpack_codes.argtypes = [P, i64, i64, C.c_int, P]
+        L.orc_dequantize.argtypes = [P, P, i64, i64, C.c_int, P]
+        L.orc_quantize_act.restype = C.c_int
+        L.orc_quantize_act.argtypes = [P, i64, i64, P, P]
+        L.orc_route.restype = C.c_int
+        L.orc_route.argtypes = [P, i32, i32, i32, P, P, P, P]
+        L.orc_gate_up.restype = C.c_int
+        L.orc_gate_up.argtypes = [P, P, P, P, P, P, P, P, P]
+        L.orc_down.restype = C.c_int
+        L.orc_down.argtypes = [P, P, P, P, P, P, P, P]
+        L.orc_combine.argtypes = [P, P, P, i32, i32, i32, P, i64, P, P]
+        L.orc_moe_forward.restype = C.c_int
+        L.orc_moe_forward.argtypes = [P, P, P, P, P, P, i64, P, P]
+        L.orc_num_threads.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+class _Shape(C.Structure):
+    _fields_ = [("T", C.c_int32), ("H", C.c_int32), ("I", C.c_int32), ("E", C.c_int32),
+                ("K", C.c_int32), ("bits", C.c_int32), ("act_int8", C.c_int32)]
+
+
+class _Weights(C.Structure):
+    _fields_ = [("gate_q", C.c_void_p), ("gate_s", C.c_void_p), ("up_q", C.c_void_p),
+                ("up_s", C.c_void_p), ("down_q", C.c_void_p), ("down_s", C.c_void_p)]
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()
+
+
+# ---- number formats --------------------------------------------------------
+
+def round_bf16(v: float) -> float:
+    return lib().orc_round_bf16(float(v))
+
+
+def round_fp16(v: float) -> float:
+    return lib().orc_round_fp16(float(v))
+
+
+def bf16_bits(v: float) -> int:
+    return lib().orc_bf16_from_double(float(v))
+
+
+def fp16_bits(v: float) -> int:
+    return lib().orc_fp16_from_double(float(v))
+
+
+def fp16_value(bits: int) -> float:
+    return lib().orc_fp16_to_double(int(bits))
+
+
+def bf16_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ---- weight format -----------------------------------------------------------
+
+def packed_cols(cols: int, bits: int) -> int:
+    return cols // 2 if bits == 4 else cols
+
+
+def quantize_weights(w: np.ndarray, bits: int):
+    """w float32 [..., rows, cols] -> (q uint8 [..., rows, packed], s uint16 fp16 bits [..., rows, cols/128])."""
+    w = _c(w, np.float32)
+    lead, (rows, cols) = w.shape[:-2], w.shape[-2:]
+    R = int(np.prod(lead, dtype=np.int64)) * rows
+    q = np.zeros(lead + (rows, packed_cols(cols, bits)), dtype=np.uint8)
+    s = np.zeros(lead + (rows, cols // GROUP), dtype=np.uint16)
+    rc = lib().orc_quantize_weights(_p(w), R, cols, bits, _p(q), _p(s))
+    if rc != 0:
+        raise ValueError(f"orc_quantize_weights: {rc}")
+    return q, s
+
+
+def unpack_codes(q: np.ndarray, cols: int, bits: int) -> np.ndarray:
+    q = _c(q, np.uint8)
+    rows = int(np.prod(q.shape[:-1], dtype=np.int64))
+    out = np.zeros(q.shape[:-1] + (cols,), dtype=np.int8)
+    lib().orc_unpack_codes(_p(q), rows, cols, bits, _p(out))
+    return out
+
+
+def dequantize(q: np.ndarray, s: np.ndarray, cols: int, bits: int) -> np.ndarray:
+    q, s = _c(q, np.uint8), _c(s, np.uint16)
+    rows = int(np.prod(q.shape[:-1], dtype=np.int64))
+    out = np.zeros(q.shape[:-1] + (cols,), dtype=np.float32)
+    lib().orc_dequantize(_p(q), _p(s), rows, cols, bits, _p(out))
+    return out
+
+
+# ---- activation quantizer ----------------------------------------------------
+
+def quantize_act(v_bf16: np.ndarray):
+    """v bf16 bits [rows, cols] -> (q int8 [rows, cols], s float32 [rows, cols/128])."""
+    v = _c(v_bf16, np.uint16)
+    rows, cols = v.shape
+    q = np.zeros((rows, cols), dtype=np.int8)
+    s = np.zeros((rows, cols // GROUP), dtype=np.float32)
+    rc = lib().orc_quantize_act(_p(v), rows, cols, _p(q), _p(s))
+    if rc != 0:
+        raise ValueError(f"orc_quantize_act: {rc}")
+    return q, s
+
+
+# ---- routing -------------------------------------------------------------------
+
+def route(topk_ids: np.ndarray, E: int):
+    ids = _c(topk_ids, np.int32)
+    T, K = ids.shape
+    S = T * K
+    counts = np.zeros(E, dtype=np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    sorted_slot = np.zeros(S, dtype=np.int32)
+    slot_row = np.zeros(S, dtype=np.int32)
+    nbad = lib().orc_route(_p(ids), T, K, E, _p(counts), _p(offsets), _p(sorted_slot), _p(slot_row))
+    return counts, offsets, sorted_slot, slot_row, nbad
+
+
+# ---- expert feed-forward -------------------------------------------------------
+
+class QWeights:
+    """Packed weights of all experts: gate/up [E][I][H*bits/8] + fp16 scales
+    [E][I][H/128]; down [E][H][I*bits/8] + [E][H][I/128]."""
+
+    def __init__(self, gate_q, gate_s, up_q, up_s, down_q, down_s):
+        self.gate_q, self.gate_s = _c(gate_q, np.uint8), _c(gate_s, np.uint16)
+        self.up_q, self.up_s = _c(up_q, np.uint8), _c(up_s, np.uint16)
+        self.down_q, self.down_s = _c(down_q, np.uint8), _c(down_s, np.uint16)
+
+    def _struct(self):
+        return _Weights(_p(self.gate_q), _p(self.gate_s), _p(self.up_q), _p(self.up_s),
+                        _p(self.down_q), _p(self.down_s))
+
+
+def _shape(T, H, I, E, K, bits, act_int8):
+    return _Shape(T, H, I, E, K, bits, int(bool(act_int8)))
+
+
+def gate_up(x_bf16, sorted_slot, offsets, W: QWeights, *, T, H, I, E, K, bits, act_int8=False,
+            xq=None, xs=None, row_mask=None):
+    """h bf16 bits [S, I] by sorted row (rows of experts not needed stay zero)."""
+    S = T * K
+    h = np.zeros((S, I), dtype=np.uint16)
+    d = _shape(T, H, I, E, K, bits, act_int8)
+    x = None if x_bf16 is None else _c(x_bf16, np.uint16)
+    xq = None if xq is None else _c(xq, np.int8)
+    xs = None if xs is None else _c(xs, np.float32)
+    m = None if row_mask is None else _c(row_mask, np.uint8)
+    rc = lib().orc_gate_up(C.byref(d), _p(x), _p(xq), _p(xs), _p(_c(sorted_slot, np.int32)),
+                           _p(_c(offsets, np.int32)), C.byref(W._struct()), _p(m), _p(h))
+    if rc != 0:
+        raise ValueError(f"orc_gate_up: {rc}")
+    return h
+
+
+def down(h_bf16, offsets, W: QWeights, *, T, H, I, E, K, bits, act_int8=False, hq=None, hs=None,
+         row_mask=None):
+    """y bf16 bits [S, H] by sorted row."""
+    S = T * K
+    y = np.zeros((S, H), dtype=np.uint16)
+    d = _shape(T, H, I, E, K, bits, act_int8)
+    h = None if h_bf16 is None else _c(h_bf16, np.uint16)
+    hq = None if hq is None else _c(hq, np.int8)
+    hs = None if hs is None else _c(hs, np.float32)
+    m = None if row_mask is None else _c(row_mask, np.uint8)
+    rc = lib().orc_down(C.byref(d), _p(h), _p(hq), _p(hs), _p(_c(offsets, np.int32)),
+                        C.byref(W._struct()), _p(m), _p(y))
+    if rc != 0:
+        raise ValueError(f"orc_down: {rc}")
+    return y
+
+
+def combine(y_bf16, slot_row, topk_w, *, T, K, H, tokens=None):
+    """(out float32 before rounding, out bf16 bits), rows = tokens (or all T)."""
+    y = _c(y_bf16, np.uint16)
+    tok = None if tokens is None else _c(tokens, np.int64)
+    n = T if tok is None else len(tok)
+    o32 = np.zeros((n, H), dtype=np.float32)
+    o16 = np.zeros((n, H), dtype=np.uint16)
+    lib().orc_combine(_p(y), _p(_c(slot_row, np.int32)), _p(_c(topk_w, np.float32)), T, K, H,
+                      _p(tok), 0 if tok is None else len(tok), _p(o32), _p(o16))
+    return o32, o16
+
+
+def moe_forward(x_bf16, topk_ids, topk_w, W: QWeights, *, E, bits, act_int8=False, I=None,
+                tokens=None):
+    """Whole feed-forward. Returns (out float32 before final rounding, out bf16
+    bits, number of dropped slots); rows follow `tokens` when given."""
+    x = _c(x_bf16, np.uint16)
+    ids = _c(topk_ids, np.int32)
+    T, H = x.shape
+    K = ids.shape[1]
+    if I is None:
+        I = W.gate_s.shape[-2]
+    tok = None if tokens is None else _c(tokens, np.int64)
+    n = T if tok is None else len(tok)
+    o32 = np.zeros((n, H), dtype=np.float32)
+    o16 = np.zeros((n, H), dtype=np.uint16)
+    d = _shape(T, H, I, E, K, bits, act_int8)
+    rc = lib().orc_moe_forward(C.byref(d), _p(x), _p(ids), _p(_c(topk_w, np.float32)),
+                               C.byref(W._struct()), _p(tok), 0 if tok is None else len(tok),
+                               _p(o32), _p(o16))
+    if rc < 0:
+        raise ValueError(f"orc_moe_forward: {rc}")
+    return o32, o16, rc

@@ -1,0 +1,520 @@
+/*
+ * CPU oracle for the quantized routed-expert MoE feed-forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, plain reference that the
+ * GPU library is checked against.  Only the test suite, the package smoke check
+ * and the CPU-baseline leg of the benchmark may load it; the GPU library never
+ * links, includes or calls it, and it shares no code with the GPU library.
+ *
+ * What it computes (sources are the minnow README, sections "Quantization" and
+ * "Build and run", and the LLaDA2.2-flash-minnow model card, section
+ * "Checkpoints and precision" and its precision table):
+ *
+ *  - routed-expert weights are signed INT4 or INT8 with one FP16 scale per 128
+ *    weights; the 128 weights of a group are contiguous along the input
+ *    (reduction) dimension of each projection (model card precision table,
+ *    INT8 and INT4 rows);
+ *  - default mode (W4A16 / W8A16): the expert matmuls take BF16 inputs and
+ *    dequantized weights, accumulating in floating point (README
+ *    "Quantization"; model card, paragraph after the table);
+ *  - INT8-activation mode (W4A8 / W8A8): expert inputs are quantized per 128
+ *    values to signed INT8 with an FP32 scale, group dot products are exact
+ *    INT32 sums, and scaled groups are combined in FP32; expert outputs return
+ *    to BF16 (model card, paragraph on --int8-expert-activations);
+ *  - each expert is a gate/up/down feed-forward with SiLU on the gate (README
+ *    "Quantization": fused gate/up/SiLU kernels; model card: gate, up and down
+ *    projection weights);
+ *  - the CPU path keeps experts compressed and expands one selected expert at a
+ *    time (README "Build and run"); this oracle does the same.
+ *
+ * Readings where the pages are silent (each one is a choice, listed with the
+ * design notes):
+ *  - weight scale s = fp16(max|w| / qmax) with qmax 7 (INT4) or 127 (INT8);
+ *    codes q = clamp(rint(w / s), -8..7 | -127..127), computed with the stored
+ *    FP16 scale, ties to even; an all-zero group (or a scale that underflows
+ *    FP16) stores s = 0 and q = 0;
+ *  - INT4 packing: element 2j in the low nibble of byte j, element 2j+1 in the
+ *    high nibble, two's complement; rows are [out][in];
+ *  - activation scale s = max|v| / 127 in FP32, q = clamp(rint(v / s), -127, 127);
+ *    s = 0 gives q = 0;
+ *  - INT8 activations feed all three projections: x into gate/up, the BF16
+ *    intermediate h into down;
+ *  - h = bf16(silu(g) * u) and y = bf16(W_down h) are materialized in BF16;
+ *  - the per-token combine is out = sum_k w_k * y_k in FP32, k ascending, with
+ *    one fused multiply-add per term, then a single rounding to BF16;
+ *  - a routed id outside [0, E) drops that slot (it contributes zero).
+ *
+ * Precision: where the pages do not fix it, sums are taken in double (the
+ * dequantized FP32 weights and BF16 inputs multiply exactly in double), so the
+ * oracle gives the exactly rounded value of each materialized BF16 quantity.
+ * The INT8-activation mode combines its scaled groups in FP32 because the model
+ * card says so.
+ *
+ * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off -fopenmp
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_GROUP 128
+
+/* ------------------------------------------------------------------------ */
+/* Number formats, from their IEEE-style definitions.                        */
+/* ------------------------------------------------------------------------ */
+
+/* Round v to a binary format with `sig` significant bits, smallest normal
+ * 2^emin and largest finite value `maxf`: nearest, ties to even, gradual
+ * underflow, overflow to infinity. */
+static double orc_round_format(double v, int sig, int emin, double maxf)
+{
+    if (isnan(v) || isinf(v) || v == 0.0) return v;
+    int ex;
+    frexp(v, &ex);                 /* |v| = m * 2^ex, m in [0.5, 1) */
+    int e = ex - 1;                /* |v| in [2^e, 2^(e+1)) */
+    if (e < emin) e = emin;        /* subnormal range: fixed quantum */
+    int qexp = e - (sig - 1);      /* weight of the last kept bit */
+    double r = nearbyint(ldexp(v, -qexp)); /* default rounding mode: ties to even */
+    double res = ldexp(r, qexp);
+    if (fabs(res) > maxf) return v > 0 ? INFINITY : -INFINITY;
+    return res;
+}
+
+static const double ORC_BF16_MAX = 3.38953138925153547590e+38; /* (2-2^-7)*2^127 */
+static const double ORC_FP16_MAX = 65504.0;
+
+double orc_round_bf16(double v) { return orc_round_format(v, 8, -126, ORC_BF16_MAX); }
+double orc_round_fp16(double v) { return orc_round_format(v, 11, -14, ORC_FP16_MAX); }
+
+/* Encode a value to bf16 bits by rounding it first. */
+uint16_t orc_bf16_from_double(double v)
+{
+    if (isnan(v)) return 0x7FC0;
+    float f = (float)orc_round_bf16(v); /* exactly representable: conversion is exact */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(u >> 16);
+}
+
+float orc_bf16_to_float(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+uint16_t orc_fp16_from_double(double v)
+{
+    if (isnan(v)) return 0x7E00;
+    double r = orc_round_fp16(v);
+    uint16_t sign = (signbit(r) ? 0x8000 : 0);
+    double a = fabs(r);
+    if (isinf(a)) return sign | 0x7C00;
+    if (a == 0.0) return sign;
+    if (a < ldexp(1.0, -14)) {           /* subnormal: a = mant * 2^-24 */
+        return sign | (uint16_t)ldexp(a, 24);
+    }
+    int ex;
+    double m = frexp(a, &ex);            /* a = m * 2^ex, m in [0.5,1) */
+    int e = ex - 1;                      /* a = (2m) * 2^e, 2m in [1,2) */
+    uint16_t mant = (uint16_t)((2.0 * m - 1.0) * 1024.0);
+    return sign | (uint16_t)((e + 15) << 10) | mant;
+}
+
+double orc_fp16_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int mant = h & 0x3FF;
+    double v;
+    if (e == 0) v = ldexp((double)mant, -24);
+    else if (e == 31) v = mant ? NAN : INFINITY;
+    else v = ldexp(1.0 + mant / 1024.0, e - 15);
+    return sign ? -v : v;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Weight format: symmetric signed INT4 / INT8, one FP16 scale per 128 inputs. */
+/* ------------------------------------------------------------------------ */
+
+static int orc_qmax(int bits) { return bits == 4 ? 7 : 127; }
+static int orc_qmin(int bits) { return bits == 4 ? -8 : -127; }
+
+/* Bytes of one packed row of `cols` codes. */
+int64_t orc_packed_row_bytes(int64_t cols, int bits) { return bits == 4 ? cols / 2 : cols; }
+
+static void orc_put_code(uint8_t* row, int64_t j, int bits, int q)
+{
+    if (bits == 8) {
+        row[j] = (uint8_t)(int8_t)q;
+    } else {
+        uint8_t nib = (uint8_t)(q & 0xF);
+        if (j % 2 == 0) row[j / 2] = (uint8_t)((row[j / 2] & 0xF0) | nib);
+        else            row[j / 2] = (uint8_t)((row[j / 2] & 0x0F) | (nib << 4));
+    }
+}
+
+static int orc_get_code(const uint8_t* row, int64_t j, int bits)
+{
+    if (bits == 8) return (int)(int8_t)row[j];
+    int nib = (j % 2 == 0) ? (row[j / 2] & 0xF) : (row[j / 2] >> 4);
+    return nib >= 8 ? nib - 16 : nib;    /* two's complement nibble */
+}
+
+/* Quantize w[rows][cols] (float32) into packed codes q[rows][row_bytes] and
+ * FP16 scales s[rows][cols/128].  Returns 0, or -1 on bad arguments. */
+int orc_quantize_weights(const float* w, int64_t rows, int64_t cols, int bits,
+                         uint8_t* q, uint16_t* s)
+{
+    if ((bits != 4 && bits != 8) || cols % ORC_GROUP != 0 || rows < 0) return -1;
+    const int64_t G = cols / ORC_GROUP, rb = orc_packed_row_bytes(cols, bits);
+    const int qmax = orc_qmax(bits), qmin = orc_qmin(bits);
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* wr = w + r * cols;
+        uint8_t* qr = q + r * rb;
+        for (int64_t g = 0; g < G; ++g) {
+            float m = 0.0f;
+            for (int64_t j = g * ORC_GROUP; j < (g + 1) * ORC_GROUP; ++j) {
+                float a = fabsf(wr[j]);
+                if (a > m) m = a;
+            }
+            float ratio = m / (float)qmax;                   /* FP32 division */
+            uint16_t s16 = orc_fp16_from_double((double)ratio);
+            s[r * G + g] = s16;
+            float sf = (float)orc_fp16_to_double(s16);
+            for (int64_t j = g * ORC_GROUP; j < (g + 1) * ORC_GROUP; ++j) {
+                int qv = 0;
+                if (sf != 0.0f) {
+                    float t = rintf(wr[j] / sf);
+                    if (t > (float)qmax) t = (float)qmax;
+                    if (t < (float)qmin) t = (float)qmin;
+                    qv = (int)t;
+                }
+                orc_put_code(qr, j, bits, qv);
+            }
+        }
+    }
+    return 0;
+}
+
+/* Unpack codes to int8 [rows][cols]. */
+void orc_unpack_codes(const uint8_t* q, int64_t rows, int64_t cols, int bits, int8_t* codes)
+{
+    const int64_t rb = orc_packed_row_bytes(cols, bits);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < cols; ++j)
+            codes[r * cols + j] = (int8_t)orc_get_code(q + r * rb, j, bits);
+}
+
+/* Dequantize to float32: w = s * q.  The product of an 11-bit FP16 significand
+ * and a code of at most 8 bits is exact in FP32. */
+void orc_dequantize(const uint8_t* q, const uint16_t* s, int64_t rows, int64_t cols, int bits, float* w)
+{
+    const int64_t G = cols / ORC_GROUP, rb = orc_packed_row_bytes(cols, bits);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < cols; ++j) {
+            double sc = orc_fp16_to_double(s[r * G + j / ORC_GROUP]);
+            w[r * cols + j] = (float)(sc * (double)orc_get_code(q + r * rb, j, bits));
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Activation quantizer: per row and 128-group, FP32 scale max|v|/127.        */
+/* ------------------------------------------------------------------------ */
+
+static void orc_quantize_act_row(const float* v, int64_t cols, int8_t* q, float* s)
+{
+    for (int64_t g = 0; g < cols / ORC_GROUP; ++g) {
+        float m = 0.0f;
+        for (int64_t j = g * ORC_GROUP; j < (g + 1) * ORC_GROUP; ++j) {
+            float a = fabsf(v[j]);
+            if (a > m) m = a;
+        }
+        float sc = m / 127.0f;                               /* FP32 division */
+        s[g] = sc;
+        for (int64_t j = g * ORC_GROUP; j < (g + 1) * ORC_GROUP; ++j) {
+            int qv = 0;
+            if (sc != 0.0f) {
+                float t = rintf(v[j] / sc);
+                if (t > 127.0f) t = 127.0f;
+                if (t < -127.0f) t = -127.0f;
+                qv = (int)t;
+            }
+            q[j] = (int8_t)qv;
+        }
+    }
+}
+
+/* v: bf16 bits [rows][cols] -> q int8 [rows][cols], s float [rows][cols/128]. */
+int orc_quantize_act(const uint16_t* v, int64_t rows, int64_t cols, int8_t* q, float* s)
+{
+    if (cols % ORC_GROUP != 0 || rows < 0) return -1;
+    float* row = (float*)malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
+    if (!row) return -2;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t j = 0; j < cols; ++j) row[j] = orc_bf16_to_float(v[r * cols + j]);
+        orc_quantize_act_row(row, cols, q + r * cols, s + r * (cols / ORC_GROUP));
+    }
+    free(row);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Routing permutation: stable counting sort of slots s = t*K + k by expert.  */
+/* ------------------------------------------------------------------------ */
+
+/* counts[E], offsets[E+1], sorted_slot[S] (first offsets[E] entries valid),
+ * slot_row[S] (-1 for a dropped slot).  Returns the number of dropped slots. */
+int orc_route(const int32_t* ids, int32_t T, int32_t K, int32_t E,
+              int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row)
+{
+    const int64_t S = (int64_t)T * K;
+    int bad = 0;
+    for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+    for (int64_t s = 0; s < S; ++s) {
+        int32_t id = ids[s];
+        if (id < 0 || id >= E) ++bad;
+        else ++counts[id];
+    }
+    offsets[0] = 0;
+    for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    int32_t* cursor = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+    for (int32_t e = 0; e < E; ++e) cursor[e] = offsets[e];
+    for (int64_t s = 0; s < S; ++s) {
+        int32_t id = ids[s];
+        if (id < 0 || id >= E) { slot_row[s] = -1; continue; }
+        int32_t pos = cursor[id]++;
+        sorted_slot[pos] = (int32_t)s;
+        slot_row[s] = pos;
+    }
+    for (int64_t p = offsets[E]; p < S; ++p) sorted_slot[p] = -1;
+    free(cursor);
+    return bad;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert feed-forward.                                                       */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    int32_t T, H, I, E, K;
+    int32_t bits;      /* 4 or 8 */
+    int32_t act_int8;  /* 0: BF16 activations; 1: INT8 activations */
+} orc_shape;
+
+typedef struct {
+    const uint8_t* gate_q; const uint16_t* gate_s;   /* [E][I][H*bits/8], [E][I][H/128] */
+    const uint8_t* up_q;   const uint16_t* up_s;
+    const uint8_t* down_q; const uint16_t* down_s;   /* [E][H][I*bits/8], [E][H][I/128] */
+} orc_weights;
+
+static double orc_silu(double g) { return g / (1.0 + exp(-g)); }
+
+static int64_t orc_mat_bytes(int64_t rows, int64_t cols, int bits) { return rows * orc_packed_row_bytes(cols, bits); }
+
+/* FP32 combination of scaled INT32 group dot products:
+ * acc = sum over groups (ascending) of float(isum_g) * (xs_g * ws_g). */
+static float orc_int8_dot(const int8_t* xq, const float* xs, const int8_t* wq, const uint16_t* ws,
+                          int64_t n, int* overflow)
+{
+    float acc = 0.0f;
+    for (int64_t g = 0; g < n / ORC_GROUP; ++g) {
+        int64_t isum = 0;
+        for (int64_t j = g * ORC_GROUP; j < (g + 1) * ORC_GROUP; ++j) isum += (int64_t)xq[j] * wq[j];
+        if (isum > INT32_MAX || isum < INT32_MIN) *overflow = 1;
+        float wsf = (float)orc_fp16_to_double(ws[g]);
+        float sc = xs[g] * wsf;
+        acc = acc + (float)isum * sc;
+    }
+    return acc;
+}
+
+/* Gate/up for every sorted row of every expert, or only for rows whose flag is
+ * set in row_mask (may be NULL).  A16: x bf16 [T][H].  A8: xq [T][H], xs [T][H/128].
+ * h: bf16 bits [S][I] indexed by sorted row. */
+int orc_gate_up(const orc_shape* d, const uint16_t* x, const int8_t* xq, const float* xs,
+                const int32_t* sorted_slot, const int32_t* offsets, const orc_weights* W,
+                const uint8_t* row_mask, uint16_t* h)
+{
+    const int64_t H = d->H, I = d->I, G_H = H / ORC_GROUP;
+    const int bits = d->bits;
+    int overflow = 0;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(|:overflow)
+    for (int32_t e = 0; e < d->E; ++e) {
+        int32_t r0 = offsets[e], r1 = offsets[e + 1];
+        int any = 0;
+        for (int32_t r = r0; r < r1; ++r) if (!row_mask || row_mask[r]) { any = 1; break; }
+        if (!any) continue;
+        const uint8_t* gq = W->gate_q + e * orc_mat_bytes(I, H, bits);
+        const uint8_t* uq = W->up_q + e * orc_mat_bytes(I, H, bits);
+        const uint16_t* gs = W->gate_s + e * I * G_H;
+        const uint16_t* us = W->up_s + e * I * G_H;
+        float* wg = NULL; float* wu = NULL; int8_t* cg = NULL; int8_t* cu = NULL;
+        float* xr = (float*)malloc(sizeof(float) * (size_t)H);
+        if (!d->act_int8) {    /* expand this expert: exact FP32 dequantized weights */
+            wg = (float*)malloc(sizeof(float) * (size_t)(I * H));
+            wu = (float*)malloc(sizeof(float) * (size_t)(I * H));
+            orc_dequantize(gq, gs, I, H, bits, wg);
+            orc_dequantize(uq, us, I, H, bits, wu);
+        } else {               /* expand codes only: the group dot products are integer */
+            cg = (int8_t*)malloc((size_t)(I * H));
+            cu = (int8_t*)malloc((size_t)(I * H));
+            orc_unpack_codes(gq, I, H, bits, cg);
+            orc_unpack_codes(uq, I, H, bits, cu);
+        }
+        for (int32_t r = r0; r < r1; ++r) {
+            if (row_mask && !row_mask[r]) continue;
+            const int64_t t = sorted_slot[r] / d->K;
+            if (!d->act_int8)
+                for (int64_t k = 0; k < H; ++k) xr[k] = orc_bf16_to_float(x[t * H + k]);
+            for (int64_t i = 0; i < I; ++i) {
+                double g, u;
+                if (!d->act_int8) {
+                    double sg = 0.0, su = 0.0;
+                    for (int64_t k = 0; k < H; ++k) {
+                        sg += (double)xr[k] * (double)wg[i * H + k];
+                        su += (double)xr[k] * (double)wu[i * H + k];
+                    }
+                    g = sg; u = su;
+                } else {
+                    g = orc_int8_dot(xq + t * H, xs + t * G_H, cg + i * H, gs + i * G_H, H, &overflow);
+                    u = orc_int8_dot(xq + t * H, xs + t * G_H, cu + i * H, us + i * G_H, H, &overflow);
+                }
+                h[(int64_t)r * I + i] = orc_bf16_from_double(orc_silu(g) * u);
+            }
+        }
+        free(xr); free(wg); free(wu); free(cg); free(cu);
+    }
+    return overflow ? -3 : 0;
+}
+
+/* Down projection for sorted rows.  A16: h bf16 [S][I].  A8: hq [S][I], hs [S][I/128].
+ * y: bf16 bits [S][H] indexed by sorted row. */
+int orc_down(const orc_shape* d, const uint16_t* h, const int8_t* hq, const float* hs,
+             const int32_t* offsets, const orc_weights* W, const uint8_t* row_mask, uint16_t* y)
+{
+    const int64_t H = d->H, I = d->I, G_I = I / ORC_GROUP;
+    const int bits = d->bits;
+    int overflow = 0;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(|:overflow)
+    for (int32_t e = 0; e < d->E; ++e) {
+        int32_t r0 = offsets[e], r1 = offsets[e + 1];
+        int any = 0;
+        for (int32_t r = r0; r < r1; ++r) if (!row_mask || row_mask[r]) { any = 1; break; }
+        if (!any) continue;
+        const uint8_t* dq = W->down_q + e * orc_mat_bytes(H, I, bits);
+        const uint16_t* ds = W->down_s + e * H * G_I;
+        float* wd = NULL; int8_t* cd = NULL;
+        float* hr = (float*)malloc(sizeof(float) * (size_t)I);
+        if (!d->act_int8) {
+            wd = (float*)malloc(sizeof(float) * (size_t)(H * I));
+            orc_dequantize(dq, ds, H, I, bits, wd);
+        } else {
+            cd = (int8_t*)malloc((size_t)(H * I));
+            orc_unpack_codes(dq, H, I, bits, cd);
+        }
+        for (int32_t r = r0; r < r1; ++r) {
+            if (row_mask && !row_mask[r]) continue;
+            if (!d->act_int8)
+                for (int64_t i = 0; i < I; ++i) hr[i] = orc_bf16_to_float(h[(int64_t)r * I + i]);
+            for (int64_t j = 0; j < H; ++j) {
+                double acc;
+                if (!d->act_int8) {
+                    double s = 0.0;
+                    for (int64_t i = 0; i < I; ++i) s += (double)hr[i] * (double)wd[j * I + i];
+                    acc = s;
+                } else {
+                    acc = orc_int8_dot(hq + (int64_t)r * I, hs + (int64_t)r * G_I, cd + j * I,
+                                       ds + j * G_I, I, &overflow);
+                }
+                y[(int64_t)r * H + j] = orc_bf16_from_double(acc);
+            }
+        }
+        free(hr); free(wd); free(cd);
+    }
+    return overflow ? -3 : 0;
+}
+
+/* Per-token weighted combine, k ascending, one FP32 fused multiply-add per
+ * term.  out_f32 (may be NULL) receives the FP32 sum before rounding; out_bf16
+ * (may be NULL) the BF16 result.  tokens (may be NULL = all T) lists the rows
+ * to produce; output row n belongs to tokens[n]. */
+void orc_combine(const uint16_t* y, const int32_t* slot_row, const float* topk_w,
+                 int32_t T, int32_t K, int32_t H, const int64_t* tokens, int64_t ntok,
+                 float* out_f32, uint16_t* out_bf16)
+{
+    const int64_t n_out = tokens ? ntok : T;
+    for (int64_t n = 0; n < n_out; ++n) {
+        const int64_t t = tokens ? tokens[n] : n;
+        for (int64_t j = 0; j < H; ++j) {
+            float acc = 0.0f;
+            for (int32_t k = 0; k < K; ++k) {
+                int32_t r = slot_row[t * K + k];
+                if (r < 0) continue;
+                acc = fmaf(topk_w[t * K + k], orc_bf16_to_float(y[(int64_t)r * H + j]), acc);
+            }
+            if (out_f32) out_f32[n * H + j] = acc;
+            if (out_bf16) out_bf16[n * H + j] = orc_bf16_from_double((double)acc);
+        }
+    }
+}
+
+/* The whole feed-forward.  tokens (may be NULL = all tokens) restricts the
+ * work to the listed tokens; out rows follow the list.  Scratch h/y are
+ * allocated here at [S][I] and [S][H] (only the needed rows are written).
+ * Returns the number of dropped slots (>= 0), or a negative error. */
+int orc_moe_forward(const orc_shape* d, const uint16_t* x, const int32_t* ids, const float* topk_w,
+                    const orc_weights* W, const int64_t* tokens, int64_t ntok,
+                    float* out_f32, uint16_t* out_bf16)
+{
+    const int64_t T = d->T, H = d->H, I = d->I, K = d->K, S = T * K;
+    if (H % ORC_GROUP || I % ORC_GROUP || (d->bits != 4 && d->bits != 8)) return -1;
+    int32_t* counts = (int32_t*)malloc(sizeof(int32_t) * (size_t)(d->E > 0 ? d->E : 1));
+    int32_t* offsets = (int32_t*)malloc(sizeof(int32_t) * (size_t)(d->E + 1));
+    int32_t* sorted_slot = (int32_t*)malloc(sizeof(int32_t) * (size_t)(S > 0 ? S : 1));
+    int32_t* slot_row = (int32_t*)malloc(sizeof(int32_t) * (size_t)(S > 0 ? S : 1));
+    uint8_t* mask = (uint8_t*)calloc((size_t)(S > 0 ? S : 1), 1);
+    uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(S * I > 0 ? S * I : 1));
+    uint16_t* y = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(S * H > 0 ? S * H : 1));
+    int8_t* xq = NULL; float* xs = NULL; int8_t* hq = NULL; float* hs = NULL;
+    int rc = orc_route(ids, d->T, d->K, d->E, counts, offsets, sorted_slot, slot_row);
+    const int nbad = rc;
+    const int64_t n_out = tokens ? ntok : T;
+    for (int64_t n = 0; n < n_out; ++n) {
+        const int64_t t = tokens ? tokens[n] : n;
+        for (int64_t k = 0; k < K; ++k) if (slot_row[t * K + k] >= 0) mask[slot_row[t * K + k]] = 1;
+    }
+    if (d->act_int8) {
+        xq = (int8_t*)calloc((size_t)(T * H > 0 ? T * H : 1), 1);
+        xs = (float*)calloc((size_t)(T * (H / ORC_GROUP) > 0 ? T * (H / ORC_GROUP) : 1), sizeof(float));
+        hq = (int8_t*)calloc((size_t)(S * I > 0 ? S * I : 1), 1);
+        hs = (float*)calloc((size_t)(S * (I / ORC_GROUP) > 0 ? S * (I / ORC_GROUP) : 1), sizeof(float));
+        for (int64_t n = 0; n < n_out; ++n) {
+            const int64_t t = tokens ? tokens[n] : n;
+            orc_quantize_act(x + t * H, 1, H, xq + t * H, xs + t * (H / ORC_GROUP));
+        }
+    }
+    rc = orc_gate_up(d, x, xq, xs, sorted_slot, offsets, W, mask, h);
+    if (rc == 0 && d->act_int8) {
+        for (int64_t r = 0; r < S; ++r)
+            if (mask[r]) orc_quantize_act(h + r * I, 1, I, hq + r * I, hs + r * (I / ORC_GROUP));
+    }
+    if (rc == 0) rc = orc_down(d, h, hq, hs, offsets, W, mask, y);
+    if (rc == 0) orc_combine(y, slot_row, topk_w, d->T, d->K, d->H, tokens, ntok, out_f32, out_bf16);
+    free(counts); free(offsets); free(sorted_slot); free(slot_row); free(mask);
+    free(h); free(y); free(xq); free(xs); free(hq); free(hs);
+    return rc == 0 ? nbad : rc;
+}
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
