@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE feed-forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_w4a16]
+
+A step is one whole qre_moe_forward (permutation, gate/up+SiLU GEMM, down GEMM,
+combine; plus the INT8 quantizers in INT8-activation mode) over one synthetic
+batch already resident in HBM.  Steps are replayed from HIP graphs (one per
+weight copy) and rotate over enough copies of the packed weights that the
+256 MB last-level cache cannot serve them.  Prints one JSON line.
+
+The roofline object is for the dominant kernel (the fused gate/up GEMM): its
+algorithmic bytes per launch (packed weights + scales of the touched experts)
+over its average duration, measured here with HIP events recorded on the
+kernel's stream around each launch.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, published
+I8_PEAK_TOPS = 5000.0
+METRIC = "routed-expert FFN tokens/s; % HBM peak (32-tok block) & % MFMA peak (prefill)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_{}.txt")
+GEMM_SRC = os.path.join(ROOT, "quantized_routed_expert_top_amd", "csrc", "gemm.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter
+    summary, or None if absent or taken on a different kernel source."""
+    path = TRAFFIC_FILE.format(workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("gemm_source_sha256") != source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, x_bits, ids, w, budget_s=12.0):
+    """The oracle as it stands, on this host's cores, over whole blocks of the
+    same workload (repeated until ~budget_s of CPU time, at least once)."""
+    import numpy as np
+    import oracle
+    from quantized_routed_expert_top_amd.synthetic import touched_experts
+    if wl.T > 512:
+        tokens = np.arange(min(wl.T, 64))
+        sample = f"first {len(tokens)} tokens of the {wl.T}-token batch"
+    else:
+        tokens = None
+        sample = f"whole {wl.T}-token batch"
+    tok = np.arange(wl.T) if tokens is None else tokens
+    Wo = oracle.workload_experts(wl, touched_experts(ids[tok], wl.E))
+    runs, t_total = 0, 0.0
+    while runs == 0 or t_total < budget_s:
+        t0 = time.perf_counter()
+        oracle.moe_forward(x_bits, ids, w, Wo, E=wl.E, bits=wl.weight_bits, act_int8=wl.act_int8, tokens=tokens)
+        t_total += time.perf_counter() - t0
+        runs += 1
+        if t_total > 3 * budget_s:
+            break
+    return {"value": runs * len(tok) / t_total, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": f"{sample}, {runs} run(s), {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="decode_w4a16")
+    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough for >= 1 GiB)")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration under rocprofv3 --pmc)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): this build has no "
+              f"multi-GPU path; the per-GPU kernel is what it measures.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import quantized_routed_expert_top_amd as qre
+    from quantized_routed_expert_top_amd.inputs import WORKLOADS
+    from quantized_routed_expert_top_amd.synthetic import algorithmic_bytes, gpu_problem
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {wl.name}: generating and quantizing weights on the GPU")
+    t0 = time.perf_counter()
+    P = gpu_problem(wl, dev)
+    log(f"[bench] problem ready in {time.perf_counter() - t0:.1f} s")
+    alg = algorithmic_bytes(wl, P["ids"])
+    W0 = P["W"]
+    R = args.copies or max(1, math.ceil((1 << 30) / max(alg["gate_up_weights"] + alg["down_weights"], 1)))
+    copies = [W0] + [W0.clone() for _ in range(R - 1)]
+    x, ids_t, w_t = P["x"], P["topk_ids"], P["topk_w"]
+    ws = torch.empty(qre.workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.K, wl.weight_bits, wl.act_int8),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        qre.moe_forward(x, ids_t, w_t, copies[i % R], act_int8=wl.act_int8, out=out, workspace=ws)
+
+    stream = torch.cuda.Stream()
+    graphs = []
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        eager_out = out.clone()
+        if not args.eager:
+            for r in range(R):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    step(r)
+                graphs.append(g)
+            for i in range(min(args.warmup, 2 * R)):
+                graphs[i % R].replay()
+            torch.cuda.synchronize()
+            if not torch.equal(out, eager_out):
+                raise RuntimeError("graph replay differs from eager output")
+
+        # ---- timed region: K whole steps ----
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(args.steps):
+            if args.eager:
+                step(i)
+            else:
+                graphs[i % R].replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu_ms = ev0.elapsed_time(ev1)
+        if not torch.equal(out, eager_out):
+            raise RuntimeError("timed steps changed the output")
+
+        # ---- per-kernel durations: stage entry points with events around each launch ----
+        sw = qre.stage_workspace(wl.T, wl.H, wl.I, wl.E, wl.K, wl.weight_bits, wl.act_int8, dev)
+        S = wl.T * wl.K
+        h = torch.empty((S, wl.I), dtype=torch.bfloat16, device=dev)
+        y = torch.empty((S, wl.H), dtype=torch.bfloat16, device=dev)
+        nk = max(20, min(args.steps, 200))
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(nk)]
+        for i in range(nk):
+            Wi = copies[i % R]
+            e = evs[i]
+            e[0].record(stream)
+            _, _, sorted_slot, slot_row, _ = qre.route(ids_t, wl.E, wl.H, wl.I, wl.weight_bits, wl.act_int8,
+                                                       workspace=sw)
+            if wl.act_int8:
+                xq, xs = qre.quantize_act(x)
+            e[1].record(stream)
+            qre.gate_up(x, sorted_slot, Wi, wl.K, sw, act_int8=wl.act_int8,
+                        xq=xq if wl.act_int8 else None, xs=xs if wl.act_int8 else None, h=h)
+            e[2].record(stream)
+            if wl.act_int8:
+                hq, hs = qre.quantize_act(h)
+            e[3].record(stream)
+            qre.down(h, Wi, wl.T, wl.K, sw, act_int8=wl.act_int8, hq=hq if wl.act_int8 else None,
+                     hs=hs if wl.act_int8 else None, y=y)
+            e[4].record(stream)
+            res = qre.combine(y, slot_row, w_t)
+            e[5].record(stream)
+        torch.cuda.synchronize()
+        if not torch.equal(res, eager_out):
+            raise RuntimeError("stage entry points disagree with qre_moe_forward")
+    dur = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(5)] for e in evs[2:]]).mean(axis=0) * 1e3  # us
+
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = wl.T * args.steps / wall
+    gu_us, dn_us = float(dur[1]), float(dur[3])
+    gu_bytes = alg["gate_up_weights"]
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(wl.name),
+                "kernel": "k_gemm16 gate/up (fused SiLU*mul)", "avg_us": round(gu_us, 2),
+                "alg_bytes_per_launch": int(gu_bytes)}
+    step_bytes = alg["total"]
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8" if wl.act_int8 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "K": wl.K,
+                   "weight_bits": wl.weight_bits, "act_int8": wl.act_int8, "weight_copies": R,
+                   "launch": "eager" if args.eager else "hipGraph replay", "touched_experts": alg["touched"]},
+        "roofline": roofline,
+        "step": {"gpu_ms_per_step": round(gpu_ms / args.steps, 5),
+                 "alg_bytes": int(step_bytes),
+                 "hbm_frac_whole_step": round(step_bytes / (wall / args.steps) / 1e9 / HBM_PEAK_GBS, 4),
+                 "mfma_frac_whole_step": round(alg["flops"] / (wall / args.steps) / 1e12 /
+                                               (I8_PEAK_TOPS if wl.act_int8 else BF16_PEAK_TFLOPS), 5)},
+        "kernels_us": {"route": round(float(dur[0]), 2), "gate_up": round(gu_us, 2),
+                       "quantize_h": round(float(dur[2]), 2), "down": round(dn_us, 2),
+                       "combine": round(float(dur[4]), 2)},
+    }
+    if args.copy_probe:
+        n = 256 << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = n
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(wl, P["x_bits"], P["ids"], P["w"])
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+/*
+ * qre.h — C ABI of the MI355X (gfx950) routed-expert MoE feed-forward with
+ * group-quantized expert weights.
+ *
+ * The operation is the routed-expert feed-forward of a block-diffusion LLM
+ * server ("coder543/minnow" README, opening paragraphs and section
+ * "Quantization"; "LLaDA2.2-flash for minnow" model card, section "Checkpoints
+ * and precision" and its precision table):
+ *
+ *   for every token t and each of its K routed experts e = topk_ids[t][k]:
+ *       g = W_gate[e] x_t,  u = W_up[e] x_t          (gate/up projections, I outputs)
+ *       h = bf16( silu(g) * u )                      (fused gate/up/SiLU)
+ *       y = bf16( W_down[e] h )                      (down projection, H outputs)
+ *   out_t = bf16( sum_k topk_w[t][k] * y_{t,k} )     (FP32, k ascending, one FMA per term)
+ *
+ * Weights are signed INT4 or INT8 with one FP16 scale per 128 consecutive
+ * weights along each projection's input (reduction) dimension; w = s * q.
+ * Activations are BF16 (W4A16 / W8A16), or, with act_int8, the expert inputs x
+ * and h are quantized per 128 values to signed INT8 with an FP32 scale
+ * s = max|v| / 127, group dot products are exact INT32 sums and the scaled
+ * groups are combined in FP32 (model card, paragraph on
+ * --int8-expert-activations).  Expert outputs return to BF16.
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument is a DEVICE pointer owned by the caller unless the
+ *    comment says "host".  The library never allocates, frees or retains
+ *    memory, keeps no mutable global state, and may be called from several
+ *    threads on different streams.
+ *  - Work is enqueued on `stream` and the call returns without synchronizing,
+ *    except qre_read_dropped_slots, which synchronizes `stream`.
+ *  - Arguments are validated on the host before anything is enqueued.  On any
+ *    error code nothing has been enqueued.  A problem with zero tokens is valid
+ *    and enqueues nothing (qre_route and qre_build_tiles still write their
+ *    per-expert outputs).
+ *  - Device pointers must be 16-byte aligned (QRE_ERR_ALIGN otherwise).
+ *  - A routed expert id outside [0, E) drops that slot: it contributes zero to
+ *    the output and is counted (see qre_read_dropped_slots).  Duplicate ids
+ *    within a token are legal; each slot is computed and summed.
+ *  - Non-finite inputs give unspecified (but memory-safe) results.
+ *
+ * Layouts (row-major, C order)
+ *    x                 bf16  [T][H]
+ *    topk_ids          int32 [T][K]     slot s = t*K + k
+ *    topk_w            fp32  [T][K]
+ *    out               bf16  [T][H]
+ *    gate_q, up_q      bytes [E][I][H*bits/8]   INT8: one code per byte;
+ *    down_q            bytes [E][H][I*bits/8]   INT4: element 2j in the low
+ *                                               nibble of byte j, 2j+1 in the
+ *                                               high nibble, two's complement
+ *    gate_s, up_s      fp16  [E][I][H/128]
+ *    down_s            fp16  [E][H][I/128]
+ */
+#ifndef QRE_H
+#define QRE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A hipStream_t.  Declared through its underlying struct so that this header
+ * needs no HIP include; pass NULL for the null stream. */
+struct ihipStream_t;
+typedef struct ihipStream_t* qre_stream_t;
+
+/* Status codes.  Every entry point returns one. */
+#define QRE_OK             0
+#define QRE_ERR_NULL      -1  /* a required pointer is NULL */
+#define QRE_ERR_SHAPE     -2  /* a size is negative, zero where it may not be, or not a multiple of 128 */
+#define QRE_ERR_BITS      -3  /* weight_bits is not 4 or 8 */
+#define QRE_ERR_GROUP     -4  /* group_size is not 128 */
+#define QRE_ERR_ALIGN     -5  /* a device pointer is not 16-byte aligned */
+#define QRE_ERR_WORKSPACE -6  /* workspace too small */
+#define QRE_ERR_HIP       -7  /* a HIP launch or call failed (see qre_last_hip_error) */
+#define QRE_ERR_MODE      -8  /* act_int8 is not 0 or 1, or an argument required by the mode is missing */
+#define QRE_ERR_LIMIT     -9  /* a size exceeds a library limit (E > QRE_MAX_EXPERTS, T*K >= 2^31, ...) */
+
+#define QRE_GROUP 128
+#define QRE_MAX_EXPERTS 512
+
+/* Problem descriptor (host memory). */
+typedef struct qre_desc {
+  int32_t T;            /* tokens, >= 0 */
+  int32_t H;            /* hidden size, multiple of 128 */
+  int32_t I;            /* expert intermediate size, multiple of 128 */
+  int32_t E;            /* routed experts, 1..QRE_MAX_EXPERTS */
+  int32_t K;            /* experts per token, 1..E */
+  int32_t weight_bits;  /* 4 or 8: signed symmetric codes, no zero-point */
+  int32_t group_size;   /* must be 128 */
+  int32_t act_int8;     /* 0: BF16 activations; 1: INT8 activations, FP32 scale per 128 */
+} qre_desc;
+
+/* Packed expert weights (device pointers, layouts above). */
+typedef struct qre_weights {
+  const void* gate_q; const void* gate_s;
+  const void* up_q;   const void* up_s;
+  const void* down_q; const void* down_s;
+} qre_weights;
+
+/* Bytes of device workspace qre_moe_forward needs for `desc` (host out). */
+int qre_workspace_bytes(const qre_desc* desc, size_t* bytes);
+
+/* The whole routed-expert feed-forward: x, topk_ids, topk_w, weights -> out.
+ * Runs the permutation, the INT8 activation quantizer (act_int8 only), the
+ * fused gate/up/SiLU grouped GEMM, the down grouped GEMM and the combine.
+ * `workspace` (>= qre_workspace_bytes) holds the permutation, h and y; after
+ * the call it also holds what qre_read_dropped_slots reads. */
+int qre_moe_forward(const qre_desc* desc, const void* x, const int32_t* topk_ids,
+                    const float* topk_w, const qre_weights* weights, void* out,
+                    void* workspace, size_t workspace_bytes, qre_stream_t stream);
+
+/* Number of slots whose expert id was outside [0, E) in the last
+ * qre_moe_forward that used `workspace` (host out).  Synchronizes `stream`. */
+int qre_read_dropped_slots(const qre_desc* desc, const void* workspace, int32_t* n_dropped,
+                           qre_stream_t stream);
+
+/* ---- Stage entry points (same conventions).  They compute exactly what the
+ * corresponding step of qre_moe_forward computes, with the same kernels. ---- */
+
+/* Token->expert permutation: a stable counting sort of the S = T*K slots by
+ * expert id (minnow README, "Quantization": GPU routing of decode blocks).
+ *   counts[E]        slots per expert
+ *   offsets[E+1]     exclusive prefix sum of counts; offsets[E] = valid slots
+ *   sorted_slot[S]   sorted_slot[offsets[e] + j] = j-th smallest slot with id e;
+ *                    entries at and past offsets[E] are -1
+ *   slot_row[S]      position of slot s in sorted_slot, or -1 if dropped
+ * Bit-exact and deterministic (no atomics decide any order).  Uses desc->T, K,
+ * E (and H, I, weight_bits, act_int8 to size the GEMM row tiles).  `workspace`
+ * (>= qre_stage_workspace_bytes) receives the routing scratch and the row-tile
+ * lists that qre_gate_up and qre_down read.  counts and offsets are written
+ * even when T == 0. */
+int qre_route(const qre_desc* desc, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
+              int32_t* sorted_slot, int32_t* slot_row, void* workspace, size_t workspace_bytes,
+              qre_stream_t stream);
+
+/* Rebuild the row-tile lists in `workspace` from offsets[E+1] alone, for a
+ * permutation that did not come from qre_route. */
+int qre_build_tiles(const qre_desc* desc, const int32_t* offsets, void* workspace,
+                    size_t workspace_bytes, qre_stream_t stream);
+
+/* Per-row, per-128 INT8 quantizer (model card, --int8-expert-activations):
+ * s = max|v| / 127 in FP32 (IEEE division), q = clamp(rint(v / s), -127, 127),
+ * ties to even; an all-zero group gives s = 0, q = 0.
+ *   v bf16 [rows][cols], q int8 [rows][cols], s fp32 [rows][cols/128]; cols % 128 == 0. */
+int qre_quantize_act(const void* v, int32_t rows, int32_t cols, int8_t* q, float* s,
+                     qre_stream_t stream);
+
+/* Fused gate/up projection and SiLU*mul for every valid sorted row r
+ * (expert e with offsets[e] <= r < offsets[e+1], token t = sorted_slot[r] / K):
+ *   h[r][i] = bf16( silu(g) * u ),  g = sum_h x[t][h] Wg[e][i][h],  u likewise.
+ * BF16 mode reads x (bf16 [T][H]); INT8 mode reads xq (int8 [T][H]) and xs
+ * (fp32 [T][H/128]) and combines INT32 group sums in FP32.  h: bf16 [T*K][I]
+ * (rows past offsets[E] are not written).  `workspace` must hold the row-tile
+ * lists of this routing, written by qre_route or qre_build_tiles.  One kernel. */
+int qre_gate_up(const qre_desc* desc, const void* x, const int8_t* xq, const float* xs,
+                const int32_t* sorted_slot, const qre_weights* weights, void* h,
+                const void* workspace, size_t workspace_bytes, qre_stream_t stream);
+
+/* Down projection for every valid sorted row r: y[r][j] = bf16( sum_i h[r][i] Wd[e][j][i] ).
+ * BF16 mode reads h (bf16 [T*K][I]); INT8 mode reads hq (int8 [T*K][I]) and hs
+ * (fp32 [T*K][I/128]).  y: bf16 [T*K][H].  Row tiles come from `workspace` as
+ * for qre_gate_up.  One kernel. */
+int qre_down(const qre_desc* desc, const void* h, const int8_t* hq, const float* hs,
+             const qre_weights* weights, void* y, const void* workspace, size_t workspace_bytes,
+             qre_stream_t stream);
+
+/* Workspace bytes the stage entry points need for `desc` (routing scratch and
+ * the two GEMM row-tile lists). */
+int qre_stage_workspace_bytes(const qre_desc* desc, size_t* bytes);
+
+/* Per-token combine: out[t][j] = bf16( fma chain over k ascending of
+ * topk_w[t][k] * y[slot_row[t*K+k]][j] ) in FP32, starting from 0; a slot with
+ * slot_row = -1 is skipped.  y bf16 [T*K][H] in sorted-row order. */
+int qre_combine(const void* y, const int32_t* slot_row, const float* topk_w, int32_t T, int32_t K,
+                int32_t H, void* out, qre_stream_t stream);
+
+/* Weight conversion (minnow README, "Quantization": convert --experts
+ * int4|int8): w fp32 [rows][cols] -> q [rows][cols*bits/8] bytes in the packed
+ * layout above and s fp16 [rows][cols/128] with s = fp16(max|w| / qmax),
+ * qmax = 7 (INT4) or 127 (INT8), q = clamp(rint(w / s), -8|-127, 7|127) using
+ * the stored FP16 scale; an all-zero group (or one whose scale rounds to 0)
+ * stores s = 0 and q = 0.  cols % 128 == 0. */
+int qre_quantize_weights(const float* w, int64_t rows, int64_t cols, int32_t bits, void* q,
+                         void* s, qre_stream_t stream);
+
+/* Human-readable name of a status code (static string). */
+const char* qre_status_string(int status);
+
+/* The HIP error code behind the last QRE_ERR_HIP on this thread (0 if none). */
+int qre_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QRE_H */

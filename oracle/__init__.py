@@ -270,3 +270,27 @@ def moe_forward(x_bf16, topk_ids, topk_w, W: QWeights, *, E, bits, act_int8=Fals
     if rc < 0:
         raise ValueError(f"orc_moe_forward: {rc}")
     return o32, o16, rc
+
+
+# ---- workload weights ------------------------------------------------------------
+
+def workload_experts(wl, experts, threads=None) -> QWeights:
+    """Oracle-quantized weights of the listed experts of a seeded workload
+    (the float32 weights come from the shared input generators); the other
+    experts are left zero."""
+    from concurrent.futures import ThreadPoolExecutor
+    from quantized_routed_expert_top_amd.inputs import GATE, UP, DOWN, default_threads, gen_expert_weight
+    b = wl.weight_bits
+    gq = np.zeros((wl.E, wl.I, packed_cols(wl.H, b)), np.uint8)
+    gs = np.zeros((wl.E, wl.I, wl.H // GROUP), np.uint16)
+    uq, us = np.zeros_like(gq), np.zeros_like(gs)
+    dq = np.zeros((wl.E, wl.H, packed_cols(wl.I, b)), np.uint8)
+    ds = np.zeros((wl.E, wl.H, wl.I // GROUP), np.uint16)
+
+    def one(e):
+        for m, (q, s) in ((GATE, (gq, gs)), (UP, (uq, us)), (DOWN, (dq, ds))):
+            q[e], s[e] = quantize_weights(gen_expert_weight(wl, e, m), b)
+
+    with ThreadPoolExecutor(threads or default_threads()) as ex:
+        list(ex.map(one, [int(e) for e in experts]))
+    return QWeights(gq, gs, uq, us, dq, ds)

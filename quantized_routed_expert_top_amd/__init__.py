@@ -1,0 +1,347 @@
+"""Python binding of libqre.so, the MI355X (gfx950) routed-expert MoE
+feed-forward with group-quantized expert weights.
+
+Argument marshalling only: every function checks dtypes, devices, shapes and
+contiguity of torch tensors, then calls the C entry point of the same name in
+``libqre.so`` (declared in ``include/qre.h``) on the current torch stream.  Every
+step of the computation runs in the library's HIP kernels; there is no CPU or
+PyTorch fallback, and importing this module fails if the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqre.so")
+GROUP = 128
+
+QRE_OK = 0
+_STATUS = {0: "ok", -1: "null pointer", -2: "bad shape", -3: "bad weight_bits", -4: "bad group_size",
+           -5: "misaligned pointer", -6: "workspace too small", -7: "HIP error", -8: "bad mode",
+           -9: "size limit"}
+
+
+class QreError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        extra = ""
+        if status == -7:
+            extra = f" (hipError {_lib().qre_last_hip_error()})"
+        super().__init__(f"{fn}: {_lib().qre_status_string(status).decode()} [{status}]{extra}")
+
+
+class _Desc(C.Structure):
+    _fields_ = [("T", C.c_int32), ("H", C.c_int32), ("I", C.c_int32), ("E", C.c_int32), ("K", C.c_int32),
+                ("weight_bits", C.c_int32), ("group_size", C.c_int32), ("act_int8", C.c_int32)]
+
+
+class _Weights(C.Structure):
+    _fields_ = [("gate_q", C.c_void_p), ("gate_s", C.c_void_p), ("up_q", C.c_void_p), ("up_s", C.c_void_p),
+                ("down_q", C.c_void_p), ("down_s", C.c_void_p)]
+
+
+_L = None
+
+
+def _lib():
+    global _L
+    if _L is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_routed_expert_top_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        P, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+        L.qre_status_string.restype = C.c_char_p
+        L.qre_status_string.argtypes = [C.c_int]
+        L.qre_last_hip_error.restype = C.c_int
+        L.qre_workspace_bytes.argtypes = [P, P]
+        L.qre_stage_workspace_bytes.argtypes = [P, P]
+        L.qre_moe_forward.argtypes = [P, P, P, P, P, P, P, sz, P]
+        L.qre_read_dropped_slots.argtypes = [P, P, P, P]
+        L.qre_route.argtypes = [P, P, P, P, P, P, P, sz, P]
+        L.qre_build_tiles.argtypes = [P, P, P, sz, P]
+        L.qre_quantize_act.argtypes = [P, i32, i32, P, P, P]
+        L.qre_gate_up.argtypes = [P, P, P, P, P, P, P, P, sz, P]
+        L.qre_down.argtypes = [P, P, P, P, P, P, P, sz, P]
+        L.qre_combine.argtypes = [P, P, P, i32, i32, i32, P, P]
+        L.qre_quantize_weights.argtypes = [P, i64, i64, i32, P, P, P]
+        _L = L
+    return _L
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def status_string(status: int) -> str:
+    return _lib().qre_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != QRE_OK:
+        raise QreError(fn, status)
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def packed_cols(cols: int, bits: int) -> int:
+    return cols // 2 if bits == 4 else cols
+
+
+@dataclass
+class QuantizedExperts:
+    """Packed routed-expert weights on the GPU (layouts of include/qre.h)."""
+    gate_q: torch.Tensor   # uint8 [E, I, H*bits/8]
+    gate_s: torch.Tensor   # float16 [E, I, H/128]
+    up_q: torch.Tensor
+    up_s: torch.Tensor
+    down_q: torch.Tensor   # uint8 [E, H, I*bits/8]
+    down_s: torch.Tensor   # float16 [E, H, I/128]
+    bits: int
+
+    @property
+    def E(self):
+        return self.gate_q.shape[0]
+
+    @property
+    def I(self):
+        return self.gate_q.shape[1]
+
+    @property
+    def H(self):
+        return self.down_q.shape[1]
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in
+                   (self.gate_q, self.gate_s, self.up_q, self.up_s, self.down_q, self.down_s))
+
+    def expert_nbytes(self) -> int:
+        return self.nbytes() // self.E
+
+    def _struct(self):
+        E, H, I, b = self.E, self.H, self.I, self.bits
+        _need(self.gate_q, "gate_q", torch.uint8, (E, I, packed_cols(H, b)))
+        _need(self.up_q, "up_q", torch.uint8, (E, I, packed_cols(H, b)))
+        _need(self.down_q, "down_q", torch.uint8, (E, H, packed_cols(I, b)))
+        _need(self.gate_s, "gate_s", torch.float16, (E, I, H // GROUP))
+        _need(self.up_s, "up_s", torch.float16, (E, I, H // GROUP))
+        _need(self.down_s, "down_s", torch.float16, (E, H, I // GROUP))
+        return _Weights(self.gate_q.data_ptr(), self.gate_s.data_ptr(), self.up_q.data_ptr(),
+                        self.up_s.data_ptr(), self.down_q.data_ptr(), self.down_s.data_ptr())
+
+    def clone(self) -> "QuantizedExperts":
+        return QuantizedExperts(*(t.clone() for t in (self.gate_q, self.gate_s, self.up_q, self.up_s,
+                                                      self.down_q, self.down_s)), self.bits)
+
+    @staticmethod
+    def empty(E, H, I, bits, device="cuda"):
+        u8, f16 = torch.uint8, torch.float16
+        return QuantizedExperts(
+            torch.empty((E, I, packed_cols(H, bits)), dtype=u8, device=device),
+            torch.empty((E, I, H // GROUP), dtype=f16, device=device),
+            torch.empty((E, I, packed_cols(H, bits)), dtype=u8, device=device),
+            torch.empty((E, I, H // GROUP), dtype=f16, device=device),
+            torch.empty((E, H, packed_cols(I, bits)), dtype=u8, device=device),
+            torch.empty((E, H, I // GROUP), dtype=f16, device=device), bits)
+
+
+def _desc(T, H, I, E, K, bits, act_int8):
+    return _Desc(T, H, I, E, K, bits, GROUP, int(bool(act_int8)))
+
+
+def workspace_bytes(T, H, I, E, K, bits, act_int8=False) -> int:
+    n = C.c_size_t(0)
+    _check("qre_workspace_bytes", _lib().qre_workspace_bytes(C.byref(_desc(T, H, I, E, K, bits, act_int8)),
+                                                             C.byref(n)))
+    return n.value
+
+
+def stage_workspace_bytes(T, H, I, E, K, bits=4, act_int8=False) -> int:
+    n = C.c_size_t(0)
+    _check("qre_stage_workspace_bytes",
+           _lib().qre_stage_workspace_bytes(C.byref(_desc(T, H, I, E, K, bits, act_int8)), C.byref(n)))
+    return n.value
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def moe_forward(x, topk_ids, topk_w, W: QuantizedExperts, act_int8=False, out=None, workspace=None):
+    """out[T,H] bf16 = routed-expert feed-forward of x[T,H] bf16."""
+    T, H = x.shape
+    K = topk_ids.shape[1]
+    _need(x, "x", torch.bfloat16, (T, H))
+    _need(topk_ids, "topk_ids", torch.int32, (T, K))
+    _need(topk_w, "topk_w", torch.float32, (T, K))
+    if W.H != H:
+        raise ValueError("weights and x disagree on H")
+    d = _desc(T, H, W.I, W.E, K, W.bits, act_int8)
+    nb = workspace_bytes(T, H, W.I, W.E, K, W.bits, act_int8)
+    if workspace is None:
+        workspace = _workspace(nb, x.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, (T, H))
+    _need(workspace, "workspace", torch.uint8)
+    ws_struct = W._struct()
+    _check("qre_moe_forward", _lib().qre_moe_forward(
+        C.byref(d), _ptr(x), _ptr(topk_ids), _ptr(topk_w), C.byref(ws_struct), _ptr(out), _ptr(workspace),
+        workspace.numel(), _stream()))
+    return out
+
+
+def read_dropped_slots(T, H, I, E, K, bits, act_int8, workspace) -> int:
+    n = C.c_int32(0)
+    _check("qre_read_dropped_slots", _lib().qre_read_dropped_slots(
+        C.byref(_desc(T, H, I, E, K, bits, act_int8)), _ptr(workspace), C.byref(n), _stream()))
+    return n.value
+
+
+def stage_workspace(T, H, I, E, K, bits=4, act_int8=False, device="cuda"):
+    """Workspace for the stage entry points (routing scratch, GEMM row tiles)."""
+    return _workspace(stage_workspace_bytes(T, H, I, E, K, bits, act_int8), device)
+
+
+def route(topk_ids, E, H=GROUP, I=GROUP, bits=4, act_int8=False, workspace=None):
+    """(counts[E], offsets[E+1], sorted_slot[S], slot_row[S], workspace).  The
+    workspace also receives the GEMM row tiles for a problem with these H, I,
+    bits and mode, for gate_up / down."""
+    T, K = topk_ids.shape
+    _need(topk_ids, "topk_ids", torch.int32, (T, K))
+    dev = topk_ids.device
+    S = T * K
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sorted_slot = torch.empty(max(S, 1), dtype=torch.int32, device=dev)[:S]
+    slot_row = torch.empty(max(S, 1), dtype=torch.int32, device=dev)[:S]
+    if workspace is None:
+        workspace = stage_workspace(T, H, I, E, K, bits, act_int8, dev)
+    d = _desc(T, H, I, E, K, bits, act_int8)
+    _check("qre_route", _lib().qre_route(C.byref(d), _ptr(topk_ids), _ptr(counts), _ptr(offsets), _ptr(sorted_slot),
+                                         _ptr(slot_row), _ptr(workspace), workspace.numel(), _stream()))
+    return counts, offsets, sorted_slot, slot_row, workspace
+
+
+def build_tiles(offsets, T, H, I, E, K, bits=4, act_int8=False, workspace=None):
+    """Write the GEMM row tiles of the permutation `offsets` into a stage workspace."""
+    _need(offsets, "offsets", torch.int32, (E + 1,))
+    if workspace is None:
+        workspace = stage_workspace(T, H, I, E, K, bits, act_int8, offsets.device)
+    d = _desc(T, H, I, E, K, bits, act_int8)
+    _check("qre_build_tiles", _lib().qre_build_tiles(C.byref(d), _ptr(offsets), _ptr(workspace), workspace.numel(),
+                                                     _stream()))
+    return workspace
+
+
+def quantize_act(v):
+    """v[rows, cols] bf16 -> (q int8 [rows, cols], s fp32 [rows, cols/128])."""
+    rows, cols = v.shape
+    _need(v, "v", torch.bfloat16)
+    q = torch.empty((rows, cols), dtype=torch.int8, device=v.device)
+    s = torch.empty((rows, cols // GROUP), dtype=torch.float32, device=v.device)
+    _check("qre_quantize_act", _lib().qre_quantize_act(_ptr(v), rows, cols, _ptr(q), _ptr(s), _stream()))
+    return q, s
+
+
+def quantize_weights(w, bits, out=None):
+    """w[..., rows, cols] fp32 -> (q uint8 [..., rows, cols*bits/8], s fp16 [..., rows, cols/128]).
+    `out` may give the (q, s) tensors to write."""
+    _need(w, "w", torch.float32)
+    lead, (rows, cols) = tuple(w.shape[:-2]), tuple(w.shape[-2:])
+    R = rows
+    for d in lead:
+        R *= d
+    if out is None:
+        q = torch.empty(lead + (rows, packed_cols(cols, bits)), dtype=torch.uint8, device=w.device)
+        s = torch.empty(lead + (rows, cols // GROUP), dtype=torch.float16, device=w.device)
+    else:
+        q, s = out
+        _need(q, "q", torch.uint8, lead + (rows, packed_cols(cols, bits)))
+        _need(s, "s", torch.float16, lead + (rows, cols // GROUP))
+    _check("qre_quantize_weights", _lib().qre_quantize_weights(_ptr(w), R, cols, bits, _ptr(q), _ptr(s), _stream()))
+    return q, s
+
+
+def gate_up(x, sorted_slot, W: QuantizedExperts, K, workspace, act_int8=False, xq=None, xs=None, h=None):
+    """h[S, I] bf16 by sorted row; `workspace` holds the row tiles (route / build_tiles)."""
+    if act_int8:
+        T, H = xq.shape
+        _need(xq, "xq", torch.int8, (T, H))
+        _need(xs, "xs", torch.float32, (T, H // GROUP))
+        dev = xq.device
+    else:
+        T, H = x.shape
+        _need(x, "x", torch.bfloat16, (T, H))
+        dev = x.device
+    S = T * K
+    _need(sorted_slot, "sorted_slot", torch.int32, (S,))
+    if h is None:
+        h = torch.empty((S, W.I), dtype=torch.bfloat16, device=dev)
+    _need(h, "h", torch.bfloat16, (S, W.I))
+    _need(workspace, "workspace", torch.uint8)
+    d = _desc(T, H, W.I, W.E, K, W.bits, act_int8)
+    ws_struct = W._struct()
+    _check("qre_gate_up", _lib().qre_gate_up(C.byref(d), _ptr(x), _ptr(xq), _ptr(xs), _ptr(sorted_slot),
+                                             C.byref(ws_struct), _ptr(h), _ptr(workspace), workspace.numel(),
+                                             _stream()))
+    return h
+
+
+def down(h, W: QuantizedExperts, T, K, workspace, act_int8=False, hq=None, hs=None, y=None):
+    """y[S, H] bf16 by sorted row; `workspace` holds the row tiles (route / build_tiles)."""
+    S = T * K
+    I, H = W.I, W.H
+    if act_int8:
+        _need(hq, "hq", torch.int8, (S, I))
+        _need(hs, "hs", torch.float32, (S, I // GROUP))
+        dev = hq.device
+    else:
+        _need(h, "h", torch.bfloat16, (S, I))
+        dev = h.device
+    if y is None:
+        y = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
+    _need(y, "y", torch.bfloat16, (S, H))
+    _need(workspace, "workspace", torch.uint8)
+    d = _desc(T, H, I, W.E, K, W.bits, act_int8)
+    ws_struct = W._struct()
+    _check("qre_down", _lib().qre_down(C.byref(d), _ptr(h), _ptr(hq), _ptr(hs), C.byref(ws_struct), _ptr(y),
+                                       _ptr(workspace), workspace.numel(), _stream()))
+    return y
+
+
+def combine(y, slot_row, topk_w, out=None):
+    """out[T, H] bf16 from y[S, H] bf16 (sorted rows), slot_row[S], topk_w[T, K]."""
+    T, K = topk_w.shape
+    S, H = y.shape
+    _need(y, "y", torch.bfloat16, (T * K, H))
+    _need(slot_row, "slot_row", torch.int32, (T * K,))
+    _need(topk_w, "topk_w", torch.float32, (T, K))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _need(out, "out", torch.bfloat16, (T, H))
+    _check("qre_combine", _lib().qre_combine(_ptr(y), _ptr(slot_row), _ptr(topk_w), T, K, H, _ptr(out), _stream()))
+    return out

@@ -1,0 +1,53 @@
+// Deterministic top-k weighted combine of the expert outputs.
+//
+// The expert outputs y return to BF16 (model card "LLaDA2.2-flash for
+// minnow", paragraph on --int8-expert-activations); each token's output is
+// the routing-weighted sum of its K expert outputs.  The order is fixed:
+// FP32, k ascending, one fused multiply-add per term starting from 0, then one
+// nearest-even rounding to BF16, so the result does not depend on scheduling.
+//
+// One workgroup per (token, 2048-column slab); each lane owns 8 consecutive
+// columns (16-byte loads of y, one 16-byte store of out).
+#include "qre_internal.h"
+
+namespace qre {
+namespace {
+
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y, const int32_t* __restrict__ slot_row,
+                                                 const float* __restrict__ topk_w, int K, int H,
+                                                 uint16_t* __restrict__ out) {
+  const int64_t t = blockIdx.x;
+  const int col = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
+  if (col >= H) return;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+  for (int k = 0; k < K; ++k) {
+    const int32_t r = slot_row[t * K + k];
+    if (r < 0) continue;
+    const float wk = topk_w[t * K + k];
+    const uint4 v = *reinterpret_cast<const uint4*>(y + (int64_t)r * H + col);
+    const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] = __builtin_fmaf(wk, bf16_bits_to_f32(p[j] & 0xffffu), acc[2 * j]);
+      acc[2 * j + 1] = __builtin_fmaf(wk, bf16_bits_to_f32(p[j] >> 16), acc[2 * j + 1]);
+    }
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = f32_to_bf16_bits(acc[2 * j]) | (f32_to_bf16_bits(acc[2 * j + 1]) << 16);
+  *reinterpret_cast<uint4*>(out + t * H + col) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+}  // namespace
+
+hipError_t launch_combine(const uint16_t* y, const int32_t* slot_row, const float* topk_w, int T, int K, int H,
+                          uint16_t* out, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int slabs = (H + 2047) / 2048;
+  hipLaunchKernelGGL(k_combine, dim3(T, slabs), dim3(256), 0, stream, y, slot_row, topk_w, K, H, out);
+  return hipGetLastError();
+}
+
+}  // namespace qre

@@ -1,0 +1,402 @@
+// Host side of the C ABI declared in include/qre.h: argument validation,
+// workspace layout and the launch sequence of the routed-expert feed-forward.
+// No entry point allocates memory or synchronizes (except
+// qre_read_dropped_slots); all validation happens before the first launch.
+#include <stdint.h>
+#include <string.h>
+
+#include "qre.h"
+#include "qre_internal.h"
+
+using namespace qre;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return QRE_OK;
+  g_last_hip_error = (int)e;
+  return QRE_ERR_HIP;
+}
+
+// Carves a workspace into 256-byte aligned pieces (or only measures it).
+struct Carver {
+  uint8_t* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<uint8_t*>(b)) {}
+  template <class T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off = align_up(off + count * sizeof(T));
+    return p;
+  }
+};
+
+// Scratch shared by qre_moe_forward and the stage entry points: the two GEMM
+// row-tile lists and the routing scratch.  qre_moe_forward's workspace starts
+// with the same block.
+struct StageLayout {
+  int32_t* ntiles;            // [2]: gate/up, down
+  Tile *tiles_gu, *tiles_dn;
+  void* route_scratch;
+  int bm_gu, bm_dn;
+  int64_t mt_gu, mt_dn;
+};
+
+void carve_stage(const qre_desc& d, Carver& c, StageLayout& L) {
+  const int64_t S = (int64_t)d.T * d.K;
+  L.bm_gu = gemm_tile_rows(S, d.E, 2 * d.I, d.H);
+  L.bm_dn = gemm_tile_rows(S, d.E, d.H, d.I);
+  L.mt_gu = max_tiles(S, d.E, L.bm_gu);
+  L.mt_dn = max_tiles(S, d.E, L.bm_dn);
+  L.ntiles = c.take<int32_t>(2);
+  L.tiles_gu = c.take<Tile>(L.mt_gu);
+  L.tiles_dn = c.take<Tile>(L.mt_dn);
+  L.route_scratch = c.take<uint8_t>(route_scratch_bytes(S, d.E));
+}
+
+struct Layout {
+  StageLayout st;
+  int32_t *counts, *offsets, *sorted_slot, *slot_row;
+  int8_t* xq; float* xs;      // INT8 activations of x
+  uint16_t* h;                // bf16 [S][I]
+  int8_t* hq; float* hs;      // INT8 activations of h
+  uint16_t* y;                // bf16 [S][H]
+  size_t bytes;
+};
+
+Layout make_layout(const qre_desc& d, void* ws) {
+  Layout L;
+  const int64_t S = (int64_t)d.T * d.K;
+  Carver c(ws);
+  carve_stage(d, c, L.st);
+  L.counts = c.take<int32_t>(d.E);
+  L.offsets = c.take<int32_t>(d.E + 1);
+  L.sorted_slot = c.take<int32_t>(S);
+  L.slot_row = c.take<int32_t>(S);
+  L.xq = nullptr; L.xs = nullptr; L.hq = nullptr; L.hs = nullptr;
+  if (d.act_int8) {
+    L.xq = c.take<int8_t>((size_t)d.T * d.H);
+    L.xs = c.take<float>((size_t)d.T * (d.H / kGroup));
+    L.hq = c.take<int8_t>((size_t)S * d.I);
+    L.hs = c.take<float>((size_t)S * (d.I / kGroup));
+  }
+  L.h = c.take<uint16_t>((size_t)S * d.I);
+  L.y = c.take<uint16_t>((size_t)S * d.H);
+  L.bytes = c.off;
+  return L;
+}
+
+size_t stage_bytes(const qre_desc& d) {
+  Carver c(nullptr);
+  StageLayout L;
+  carve_stage(d, c, L);
+  return c.off;
+}
+
+StageLayout stage_layout(const qre_desc& d, const void* ws) {
+  Carver c(const_cast<void*>(ws));
+  StageLayout L;
+  carve_stage(d, c, L);
+  return L;
+}
+
+int check_desc(const qre_desc* d) {
+  if (!d) return QRE_ERR_NULL;
+  if (d->weight_bits != 4 && d->weight_bits != 8) return QRE_ERR_BITS;
+  if (d->group_size != QRE_GROUP) return QRE_ERR_GROUP;
+  if (d->act_int8 != 0 && d->act_int8 != 1) return QRE_ERR_MODE;
+  if (d->T < 0 || d->H <= 0 || d->I <= 0 || d->E <= 0 || d->K <= 0) return QRE_ERR_SHAPE;
+  if (d->H % QRE_GROUP || d->I % QRE_GROUP) return QRE_ERR_SHAPE;
+  if (d->K > d->E) return QRE_ERR_SHAPE;
+  if (d->E > QRE_MAX_EXPERTS) return QRE_ERR_LIMIT;
+  const int64_t S = (int64_t)d->T * d->K;
+  if (S >= (1ll << 31)) return QRE_ERR_LIMIT;
+  if (max_tiles(S, d->E, 1) >= (1ll << 31)) return QRE_ERR_LIMIT;
+  // grid limit of the GEMM launch (row tiles along grid.y)
+  if (max_tiles(S, d->E, gemm_tile_rows(S, d->E, 2 * d->I, d->H)) > 65535) return QRE_ERR_LIMIT;
+  if (max_tiles(S, d->E, gemm_tile_rows(S, d->E, d->H, d->I)) > 65535) return QRE_ERR_LIMIT;
+  return QRE_OK;
+}
+
+int check_weights(const qre_weights* w, bool need_gate_up, bool need_down) {
+  if (!w) return QRE_ERR_NULL;
+  if (need_gate_up && (!w->gate_q || !w->gate_s || !w->up_q || !w->up_s)) return QRE_ERR_NULL;
+  if (need_down && (!w->down_q || !w->down_s)) return QRE_ERR_NULL;
+  if (need_gate_up && !(aligned16(w->gate_q) && aligned16(w->gate_s) && aligned16(w->up_q) && aligned16(w->up_s)))
+    return QRE_ERR_ALIGN;
+  if (need_down && !(aligned16(w->down_q) && aligned16(w->down_s))) return QRE_ERR_ALIGN;
+  return QRE_OK;
+}
+
+GemmProblem gate_up_problem(const qre_desc& d, const void* x, const int8_t* xq, const float* xs,
+                            const int32_t* sorted_slot, const qre_weights& w, const Tile* tiles,
+                            const int32_t* ntiles, int64_t mt, int bm, void* h) {
+  GemmProblem p;
+  p.act_int8 = d.act_int8;
+  p.bits = d.weight_bits;
+  p.gather_k = d.K;
+  p.sorted_slot = sorted_slot;
+  p.a = d.act_int8 ? static_cast<const void*>(xq) : x;
+  p.a_scale = xs;
+  p.w0q = static_cast<const uint8_t*>(w.gate_q);
+  p.w0s = static_cast<const uint16_t*>(w.gate_s);
+  p.w1q = static_cast<const uint8_t*>(w.up_q);
+  p.w1s = static_cast<const uint16_t*>(w.up_s);
+  p.tiles = tiles;
+  p.ntiles = ntiles;
+  p.max_tiles = mt;
+  p.bm = bm;
+  p.out = h;
+  p.n = d.I;
+  p.kdim = d.H;
+  return p;
+}
+
+GemmProblem down_problem(const qre_desc& d, const void* h, const int8_t* hq, const float* hs, const qre_weights& w,
+                         const Tile* tiles, const int32_t* ntiles, int64_t mt, int bm, void* y) {
+  GemmProblem p;
+  p.act_int8 = d.act_int8;
+  p.bits = d.weight_bits;
+  p.gather_k = 0;
+  p.sorted_slot = nullptr;
+  p.a = d.act_int8 ? static_cast<const void*>(hq) : h;
+  p.a_scale = hs;
+  p.w0q = static_cast<const uint8_t*>(w.down_q);
+  p.w0s = static_cast<const uint16_t*>(w.down_s);
+  p.w1q = nullptr;
+  p.w1s = nullptr;
+  p.tiles = tiles;
+  p.ntiles = ntiles;
+  p.max_tiles = mt;
+  p.bm = bm;
+  p.out = y;
+  p.n = d.H;
+  p.kdim = d.I;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qre_status_string(int s) {
+  switch (s) {
+    case QRE_OK: return "ok";
+    case QRE_ERR_NULL: return "null pointer";
+    case QRE_ERR_SHAPE: return "bad shape";
+    case QRE_ERR_BITS: return "weight_bits must be 4 or 8";
+    case QRE_ERR_GROUP: return "group_size must be 128";
+    case QRE_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case QRE_ERR_WORKSPACE: return "workspace too small";
+    case QRE_ERR_HIP: return "HIP error";
+    case QRE_ERR_MODE: return "bad act_int8 mode or missing mode argument";
+    case QRE_ERR_LIMIT: return "size exceeds a library limit";
+    default: return "unknown status";
+  }
+}
+
+int qre_last_hip_error(void) { return g_last_hip_error; }
+
+int qre_workspace_bytes(const qre_desc* desc, size_t* bytes) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!bytes) return QRE_ERR_NULL;
+  *bytes = make_layout(*desc, nullptr).bytes;
+  return QRE_OK;
+}
+
+int qre_stage_workspace_bytes(const qre_desc* desc, size_t* bytes) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!bytes) return QRE_ERR_NULL;
+  *bytes = stage_bytes(*desc);
+  return QRE_OK;
+}
+
+int qre_moe_forward(const qre_desc* desc, const void* x, const int32_t* topk_ids, const float* topk_w,
+                    const qre_weights* weights, void* out, void* workspace, size_t workspace_bytes,
+                    qre_stream_t stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  const qre_desc& d = *desc;
+  if (d.T == 0) return QRE_OK;
+  if (!x || !topk_ids || !topk_w || !out || !workspace) return QRE_ERR_NULL;
+  rc = check_weights(weights, true, true);
+  if (rc) return rc;
+  if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(out) || !aligned16(workspace))
+    return QRE_ERR_ALIGN;
+  const Layout L = make_layout(d, workspace);
+  if (workspace_bytes < L.bytes) return QRE_ERR_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t S = (int64_t)d.T * d.K;
+  const StageLayout& st = L.st;
+
+  hipError_t e = launch_route(topk_ids, d.T, d.K, d.E, L.counts, L.offsets, L.sorted_slot, L.slot_row,
+                              st.route_scratch, st.tiles_gu, st.ntiles, st.bm_gu, st.tiles_dn, st.ntiles + 1,
+                              st.bm_dn, s);
+  if (e != hipSuccess) return hip_status(e);
+  if (d.act_int8) {
+    e = launch_quantize_act(static_cast<const uint16_t*>(x), d.T, d.H, L.xq, L.xs, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  e = launch_gemm(gate_up_problem(d, x, L.xq, L.xs, L.sorted_slot, *weights, st.tiles_gu, st.ntiles, st.mt_gu,
+                                  st.bm_gu, L.h), s);
+  if (e != hipSuccess) return hip_status(e);
+  if (d.act_int8) {
+    e = launch_quantize_act(L.h, (int)S, d.I, L.hq, L.hs, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  e = launch_gemm(down_problem(d, L.h, L.hq, L.hs, *weights, st.tiles_dn, st.ntiles + 1, st.mt_dn, st.bm_dn, L.y),
+                  s);
+  if (e != hipSuccess) return hip_status(e);
+  e = launch_combine(L.y, L.slot_row, topk_w, d.T, d.K, d.H, static_cast<uint16_t*>(out), s);
+  return hip_status(e);
+}
+
+int qre_read_dropped_slots(const qre_desc* desc, const void* workspace, int32_t* n_dropped, qre_stream_t stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!n_dropped) return QRE_ERR_NULL;
+  const qre_desc& d = *desc;
+  const int64_t S = (int64_t)d.T * d.K;
+  if (S == 0) {
+    *n_dropped = 0;
+    return QRE_OK;
+  }
+  if (!workspace) return QRE_ERR_NULL;
+  const Layout L = make_layout(d, const_cast<void*>(workspace));
+  int32_t valid = 0;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(&valid, L.offsets + d.E, sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e);
+  *n_dropped = (int32_t)(S - valid);
+  return QRE_OK;
+}
+
+static int check_stage_ws(const qre_desc& d, const void* workspace, size_t workspace_bytes) {
+  if (!workspace) return QRE_ERR_NULL;
+  if (!aligned16(workspace)) return QRE_ERR_ALIGN;
+  if (workspace_bytes < stage_bytes(d)) return QRE_ERR_WORKSPACE;
+  return QRE_OK;
+}
+
+int qre_route(const qre_desc* desc, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
+              int32_t* sorted_slot, int32_t* slot_row, void* workspace, size_t workspace_bytes,
+              qre_stream_t stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  const qre_desc& d = *desc;
+  if (!counts || !offsets) return QRE_ERR_NULL;
+  if (!aligned16(counts) || !aligned16(offsets)) return QRE_ERR_ALIGN;
+  const int64_t S = (int64_t)d.T * d.K;
+  if (S > 0) {
+    if (!topk_ids || !sorted_slot || !slot_row) return QRE_ERR_NULL;
+    if (!aligned16(topk_ids) || !aligned16(sorted_slot) || !aligned16(slot_row)) return QRE_ERR_ALIGN;
+  }
+  rc = check_stage_ws(d, workspace, workspace_bytes);
+  if (rc) return rc;
+  const StageLayout st = stage_layout(d, workspace);
+  return hip_status(launch_route(topk_ids, d.T, d.K, d.E, counts, offsets, sorted_slot, slot_row, st.route_scratch,
+                                 st.tiles_gu, st.ntiles, st.bm_gu, st.tiles_dn, st.ntiles + 1, st.bm_dn,
+                                 reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qre_build_tiles(const qre_desc* desc, const int32_t* offsets, void* workspace, size_t workspace_bytes,
+                    qre_stream_t stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  const qre_desc& d = *desc;
+  if (!offsets) return QRE_ERR_NULL;
+  if (!aligned16(offsets)) return QRE_ERR_ALIGN;
+  rc = check_stage_ws(d, workspace, workspace_bytes);
+  if (rc) return rc;
+  const StageLayout st = stage_layout(d, workspace);
+  return hip_status(launch_build_tiles(offsets, d.E, st.tiles_gu, st.ntiles, st.bm_gu, st.tiles_dn, st.ntiles + 1,
+                                       st.bm_dn, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qre_quantize_act(const void* v, int32_t rows, int32_t cols, int8_t* q, float* s, qre_stream_t stream) {
+  if (rows < 0 || cols <= 0 || cols % QRE_GROUP) return QRE_ERR_SHAPE;
+  if ((int64_t)rows * cols >= (1ll << 40)) return QRE_ERR_LIMIT;
+  if (rows == 0) return QRE_OK;
+  if (!v || !q || !s) return QRE_ERR_NULL;
+  if (!aligned16(v) || !aligned16(q) || !aligned16(s)) return QRE_ERR_ALIGN;
+  return hip_status(launch_quantize_act(static_cast<const uint16_t*>(v), rows, cols, q, s,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qre_quantize_weights(const float* w, int64_t rows, int64_t cols, int32_t bits, void* q, void* s,
+                         qre_stream_t stream) {
+  if (bits != 4 && bits != 8) return QRE_ERR_BITS;
+  if (rows < 0 || cols <= 0 || cols % QRE_GROUP) return QRE_ERR_SHAPE;
+  if (rows * (cols / QRE_GROUP) >= (1ll << 40)) return QRE_ERR_LIMIT;
+  if (rows == 0) return QRE_OK;
+  if (!w || !q || !s) return QRE_ERR_NULL;
+  if (!aligned16(w) || !aligned16(q) || !aligned16(s)) return QRE_ERR_ALIGN;
+  return hip_status(launch_quantize_weights(w, rows, cols, bits, static_cast<uint8_t*>(q),
+                                            static_cast<uint16_t*>(s), reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qre_gate_up(const qre_desc* desc, const void* x, const int8_t* xq, const float* xs, const int32_t* sorted_slot,
+                const qre_weights* weights, void* h, const void* workspace, size_t workspace_bytes,
+                qre_stream_t stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  const qre_desc& d = *desc;
+  if (d.T == 0) return QRE_OK;
+  rc = check_stage_ws(d, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (d.act_int8 ? (!xq || !xs) : !x) return QRE_ERR_MODE;
+  if (!sorted_slot || !h) return QRE_ERR_NULL;
+  rc = check_weights(weights, true, false);
+  if (rc) return rc;
+  if (!aligned16(d.act_int8 ? (const void*)xq : x) || (d.act_int8 && !aligned16(xs)) || !aligned16(sorted_slot) ||
+      !aligned16(h))
+    return QRE_ERR_ALIGN;
+  const StageLayout st = stage_layout(d, workspace);
+  return hip_status(launch_gemm(gate_up_problem(d, x, xq, xs, sorted_slot, *weights, st.tiles_gu, st.ntiles, st.mt_gu,
+                                                st.bm_gu, h),
+                                reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qre_down(const qre_desc* desc, const void* h, const int8_t* hq, const float* hs, const qre_weights* weights,
+             void* y, const void* workspace, size_t workspace_bytes, qre_stream_t stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  const qre_desc& d = *desc;
+  if (d.T == 0) return QRE_OK;
+  rc = check_stage_ws(d, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (d.act_int8 ? (!hq || !hs) : !h) return QRE_ERR_MODE;
+  if (!y) return QRE_ERR_NULL;
+  rc = check_weights(weights, false, true);
+  if (rc) return rc;
+  if (!aligned16(d.act_int8 ? (const void*)hq : h) || (d.act_int8 && !aligned16(hs)) || !aligned16(y))
+    return QRE_ERR_ALIGN;
+  const StageLayout st = stage_layout(d, workspace);
+  return hip_status(launch_gemm(down_problem(d, h, hq, hs, *weights, st.tiles_dn, st.ntiles + 1, st.mt_dn, st.bm_dn,
+                                             y),
+                                reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qre_combine(const void* y, const int32_t* slot_row, const float* topk_w, int32_t T, int32_t K, int32_t H,
+                void* out, qre_stream_t stream) {
+  if (T < 0 || K <= 0 || H <= 0 || H % QRE_GROUP) return QRE_ERR_SHAPE;
+  if ((int64_t)T * K >= (1ll << 31)) return QRE_ERR_LIMIT;
+  if (T == 0) return QRE_OK;
+  if (!y || !slot_row || !topk_w || !out) return QRE_ERR_NULL;
+  if (!aligned16(y) || !aligned16(slot_row) || !aligned16(topk_w) || !aligned16(out)) return QRE_ERR_ALIGN;
+  return hip_status(launch_combine(static_cast<const uint16_t*>(y), slot_row, topk_w, T, K, H,
+                                   static_cast<uint16_t*>(out), reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

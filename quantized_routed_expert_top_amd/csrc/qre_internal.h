@@ -1,0 +1,89 @@
+// Internal declarations of the gfx950 kernels behind include/qre.h.
+//
+// Device helpers and the launchers each kernel file exports to the host-side
+// entry points (qre_api.hip).  Everything here is HIP C++ for CDNA4: wave64,
+// MFMA, LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qre {
+
+constexpr int kGroup = 128;      // quantization group along the reduction dim
+constexpr int kWave = 64;
+
+// Tile of sorted rows processed by one GEMM workgroup: rows [row0, row0+nrows) of expert e.
+struct Tile {
+  int32_t e, row0, nrows, pad;
+};
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Nearest-even rounding of an FP32 value to BF16 bits (quiet NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// v_perm_b32: byte i of the result is byte sel.byte[i] of the 8-byte value {hi, lo}.
+__device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// Launchers (all enqueue on `stream` and return the launch status)
+// ---------------------------------------------------------------------------
+
+// Routing.  The small variant runs in one workgroup and fuses the tile-list
+// build for up to two GEMM row-tile heights; the large variant is three kernels.
+// `ws` (route scratch) must hold route_scratch_bytes(S, E) bytes.
+size_t route_scratch_bytes(int64_t S, int E);
+hipError_t launch_route(const int32_t* ids, int T, int K, int E, int32_t* counts, int32_t* offsets,
+                        int32_t* sorted_slot, int32_t* slot_row, void* ws, Tile* tiles_a, int32_t* ntiles_a,
+                        int bm_a, Tile* tiles_b, int32_t* ntiles_b, int bm_b, hipStream_t stream);
+// Tile list from offsets alone (used by the stage entry points).
+hipError_t launch_build_tiles(const int32_t* offsets, int E, Tile* tiles_a, int32_t* ntiles_a, int bm_a,
+                              Tile* tiles_b, int32_t* ntiles_b, int bm_b, hipStream_t stream);
+// Upper bound on the number of row tiles of height bm over S sorted rows and E experts.
+int64_t max_tiles(int64_t S, int E, int bm);
+
+// INT8 quantizers.
+hipError_t launch_quantize_act(const uint16_t* v, int rows, int cols, int8_t* q, float* s, hipStream_t stream);
+hipError_t launch_quantize_weights(const float* w, int64_t rows, int64_t cols, int bits, uint8_t* q,
+                                   uint16_t* s, hipStream_t stream);
+
+// Grouped GEMMs.
+struct GemmProblem {
+  int act_int8;           // 0: bf16 activations, 1: int8 activations + fp32 scales
+  int bits;               // 4 or 8
+  int gather_k;           // >0: A row of sorted row r is token sorted_slot[r] / gather_k; 0: A row = r
+  const int32_t* sorted_slot;
+  const void* a;          // bf16 [rows][kdim] or int8 [rows][kdim]
+  const float* a_scale;   // int8 mode: fp32 [rows][kdim/128]
+  const uint8_t* w0q; const uint16_t* w0s;   // [E][n][kdim*bits/8], [E][n][kdim/128]
+  const uint8_t* w1q; const uint16_t* w1s;   // second matrix (gate/up: up), or null
+  const Tile* tiles; const int32_t* ntiles; int64_t max_tiles; int bm;
+  void* out;              // bf16 [S][n]
+  int n, kdim;
+};
+// Fused gate/up + SiLU*mul (w1 = up) or plain projection (w1 = null).
+hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
+// Row-tile height the GEMM wants for a problem with S sorted rows over E experts.
+int gemm_tile_rows(int64_t S, int E, int n, int kdim);
+
+// Combine.
+hipError_t launch_combine(const uint16_t* y, const int32_t* slot_row, const float* topk_w, int T, int K,
+                          int H, uint16_t* out, hipStream_t stream);
+
+}  // namespace qre

@@ -1,0 +1,321 @@
+// Token->expert permutation for the routed-expert feed-forward: a stable
+// counting sort of the slots s = t*K + k by expert id, plus the GEMM row-tile
+// list.  The minnow README (section "Quantization") routes 32-token decode
+// blocks on the GPU by default; this is that step for CDNA4.
+//
+// Method (no atomic decides any order, so the result is bit-exact and
+// deterministic):
+//  * every wave owns a contiguous chunk of slots and walks it 64 slots at a
+//    time; lanes holding the same expert id find each other with one wave
+//    ballot per id bit (a wave-level multi-split); the lowest such lane adds
+//    the group's size to the wave's per-expert count, and a lane's rank inside
+//    its group is the popcount of the group mask below it;
+//  * an exclusive scan over (expert-major, wave-minor) counts gives every wave
+//    its first output position per expert;
+//  * the scatter pass re-walks the chunk in the same order, so equal ids keep
+//    ascending slot order.
+// Small problems (S <= kSmallMax) do all of it in one workgroup with the
+// tables in LDS; larger ones use three kernels with the per-wave table in HBM.
+#include "qre_internal.h"
+
+namespace qre {
+namespace {
+
+constexpr int kSmallMax = 8192;   // slots handled by the one-workgroup kernel
+constexpr int kLargeChunk = 1024; // slots per wave in the three-kernel path
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Mask of the lanes whose key equals this lane's key (keys < 2^nbits).
+// Must be called by all 64 lanes.
+__device__ __forceinline__ uint64_t match_any(uint32_t key, int nbits) {
+  uint64_t m = ~0ull;
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1u;
+    const uint64_t bal = __ballot(bit);
+    m &= bit ? bal : ~bal;
+  }
+  return m;
+}
+
+__device__ __forceinline__ uint32_t slot_key(const int32_t* ids, int64_t s, int64_t c1, int E) {
+  if (s >= c1) return (uint32_t)E;
+  const int32_t id = ids[s];
+  return (id >= 0 && id < E) ? (uint32_t)id : (uint32_t)E;
+}
+
+// Count this wave's chunk [c0, c1) into hist_row[E] (LDS, zeroed by the caller).
+__device__ void wave_count(const int32_t* ids, int64_t c0, int64_t c1, int E, int nbits, int* hist_row) {
+  const int lane = lane_id();
+  for (int64_t base = c0; base < c1; base += kWave) {
+    const uint32_t key = slot_key(ids, base + lane, c1, E);
+    const uint64_t m = match_any(key, nbits);
+    if (key < (uint32_t)E && lane == __builtin_ctzll(m)) hist_row[key] += __popcll(m);
+  }
+}
+
+// Scatter this wave's chunk; base_row[e] (LDS) holds the next output position
+// of expert e for this wave and is advanced as the chunk is walked.
+__device__ void wave_scatter(const int32_t* ids, int64_t c0, int64_t c1, int E, int nbits, int* base_row,
+                             int32_t* sorted_slot, int32_t* slot_row) {
+  const int lane = lane_id();
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int64_t base = c0; base < c1; base += kWave) {
+    const int64_t s = base + lane;
+    const uint32_t key = slot_key(ids, s, c1, E);
+    const uint64_t m = match_any(key, nbits);
+    if (s < c1) {
+      if (key < (uint32_t)E) {
+        const int pos = base_row[key] + __popcll(m & below);
+        sorted_slot[pos] = (int32_t)s;
+        slot_row[s] = pos;
+      } else {
+        slot_row[s] = -1;
+      }
+    }
+    // every lane has read base_row[key] above; LDS ops of one wave stay in order
+    if (key < (uint32_t)E && lane == __builtin_ctzll(m)) base_row[key] += __popcll(m);
+  }
+}
+
+// Exclusive scan of data[0, n) (LDS) by the whole workgroup; returns the total.
+__device__ int block_exclusive_scan(int* data, int n, int* wave_tmp) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int per = ceil_div(n, nt);
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  int local = 0;
+  for (int i = lo; i < hi; ++i) local += data[i];
+  int v = local;
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(v, d);
+    if (lane_id() >= d) v += o;
+  }
+  if (lane_id() == kWave - 1) wave_tmp[tid / kWave] = v;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int w = 0; w < nt / kWave; ++w) {
+    if (w < tid / kWave) before += wave_tmp[w];
+    total += wave_tmp[w];
+  }
+  int run = before + v - local;
+  for (int i = lo; i < hi; ++i) {
+    const int c = data[i];
+    data[i] = run;
+    run += c;
+  }
+  __syncthreads();
+  return total;
+}
+
+// Write the row-tile list of height bm from cnt[e] and offs[e] (LDS).  scratch
+// (LDS, E entries) is clobbered.  All threads must call.
+__device__ void build_tiles(const int* cnt, const int* offs, int E, int bm, int* scratch, int* wave_tmp,
+                            Tile* tiles, int32_t* ntiles) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) scratch[e] = ceil_div(cnt[e], bm);
+  __syncthreads();
+  const int total = block_exclusive_scan(scratch, E, wave_tmp);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int nt = ceil_div(cnt[e], bm);
+    for (int j = 0; j < nt; ++j) {
+      Tile t;
+      t.e = e;
+      t.row0 = offs[e] + j * bm;
+      t.nrows = min(bm, cnt[e] - j * bm);
+      t.pad = 0;
+      tiles[scratch[e] + j] = t;
+    }
+  }
+  if (threadIdx.x == 0) *ntiles = total;
+  __syncthreads();
+}
+
+// One workgroup of NW waves.  LDS: hist[NW][E], cnt[E], offs[E+1], scratch[E], wave_tmp[NW].
+template <int NW>
+__global__ __launch_bounds__(NW * kWave) void k_route_small(const int32_t* __restrict__ ids, int S, int E,
+                                                            int nbits, int32_t* counts, int32_t* offsets,
+                                                            int32_t* sorted_slot, int32_t* slot_row,
+                                                            Tile* tiles_a, int32_t* ntiles_a, int bm_a,
+                                                            Tile* tiles_b, int32_t* ntiles_b, int bm_b) {
+  extern __shared__ int lds[];
+  int* hist = lds;                 // [NW][E]
+  int* cnt = hist + NW * E;        // [E]
+  int* offs = cnt + E;             // [E+1]
+  int* scratch = offs + E + 1;     // [E]
+  int* wave_tmp = scratch + E;     // [NW]
+  const int tid = threadIdx.x, w = tid / kWave;
+  for (int i = tid; i < NW * E; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  const int64_t L = (int64_t)ceil_div(ceil_div(S, NW), kWave) * kWave;
+  const int64_t c0 = min((int64_t)S, w * L), c1 = min((int64_t)S, c0 + L);
+  wave_count(ids, c0, c1, E, nbits, hist + w * E);
+  __syncthreads();
+  // per expert: prefix over waves, total count
+  for (int e = tid; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int v = 0; v < NW; ++v) {
+      const int c = hist[v * E + e];
+      hist[v * E + e] = run;
+      run += c;
+    }
+    cnt[e] = run;
+    offs[e] = run;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(offs, E, wave_tmp);
+  if (tid == 0) offs[E] = total;
+  __syncthreads();
+  for (int e = tid; e <= E; e += blockDim.x) {
+    offsets[e] = offs[e];
+    if (e < E) counts[e] = cnt[e];
+  }
+  for (int i = tid; i < NW * E; i += blockDim.x) hist[i] += offs[i % E];
+  __syncthreads();
+  wave_scatter(ids, c0, c1, E, nbits, hist + w * E, sorted_slot, slot_row);
+  for (int i = total + tid; i < S; i += blockDim.x) sorted_slot[i] = -1;
+  if (tiles_a) build_tiles(cnt, offs, E, bm_a, scratch, wave_tmp, tiles_a, ntiles_a);
+  if (tiles_b) build_tiles(cnt, offs, E, bm_b, scratch, wave_tmp, tiles_b, ntiles_b);
+}
+
+// Three-kernel path.  ghist[gw][E]: per-wave counts, then per-wave bases.
+__global__ __launch_bounds__(256) void k_route_count(const int32_t* __restrict__ ids, int S, int E, int nbits,
+                                                     int32_t* ghist) {
+  extern __shared__ int lds[];
+  const int w = threadIdx.x / kWave;
+  int* row = lds + w * E;
+  for (int i = threadIdx.x; i < 4 * E; i += blockDim.x) lds[i] = 0;
+  __syncthreads();
+  const int64_t gw = (int64_t)blockIdx.x * 4 + w;
+  const int64_t c0 = min((int64_t)S, gw * kLargeChunk), c1 = min((int64_t)S, c0 + kLargeChunk);
+  wave_count(ids, c0, c1, E, nbits, row);
+  // the wave reads back its own LDS row (in-order within the wave)
+  for (int e = lane_id(); e < E; e += kWave) ghist[gw * E + e] = row[e];
+}
+
+__global__ __launch_bounds__(1024) void k_route_scan(int32_t* ghist, int nwaves, int E, int32_t* counts,
+                                                     int32_t* offsets, Tile* tiles_a, int32_t* ntiles_a, int bm_a,
+                                                     Tile* tiles_b, int32_t* ntiles_b, int bm_b) {
+  extern __shared__ int lds[];
+  int* cnt = lds;                  // [E]
+  int* offs = cnt + E;             // [E+1]
+  int* scratch = offs + E + 1;     // [E]
+  int* wave_tmp = scratch + E;     // [16]
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int v = 0; v < nwaves; ++v) {
+      const int c = ghist[(int64_t)v * E + e];
+      ghist[(int64_t)v * E + e] = run;
+      run += c;
+    }
+    cnt[e] = run;
+    offs[e] = run;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(offs, E, wave_tmp);
+  if (tid == 0) offs[E] = total;
+  __syncthreads();
+  for (int e = tid; e <= E; e += blockDim.x) {
+    offsets[e] = offs[e];
+    if (e < E) counts[e] = cnt[e];
+  }
+  if (tiles_a) build_tiles(cnt, offs, E, bm_a, scratch, wave_tmp, tiles_a, ntiles_a);
+  if (tiles_b) build_tiles(cnt, offs, E, bm_b, scratch, wave_tmp, tiles_b, ntiles_b);
+}
+
+__global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict__ ids, int S, int E, int nbits,
+                                                       const int32_t* ghist, const int32_t* offsets,
+                                                       int32_t* sorted_slot, int32_t* slot_row) {
+  extern __shared__ int lds[];
+  const int w = threadIdx.x / kWave;
+  int* row = lds + w * E;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + w;
+  for (int e = lane_id(); e < E; e += kWave) row[e] = ghist[gw * E + e] + offsets[e];
+  const int64_t c0 = min((int64_t)S, gw * kLargeChunk), c1 = min((int64_t)S, c0 + kLargeChunk);
+  wave_scatter(ids, c0, c1, E, nbits, row, sorted_slot, slot_row);
+  const int total = offsets[E];
+  for (int64_t i = total + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < S;
+       i += (int64_t)gridDim.x * blockDim.x)
+    sorted_slot[i] = -1;
+}
+
+__global__ __launch_bounds__(256) void k_build_tiles(const int32_t* offsets, int E, Tile* tiles_a,
+                                                     int32_t* ntiles_a, int bm_a, Tile* tiles_b, int32_t* ntiles_b,
+                                                     int bm_b) {
+  extern __shared__ int lds[];
+  int* cnt = lds;
+  int* offs = cnt + E;
+  int* scratch = offs + E + 1;
+  int* wave_tmp = scratch + E;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    offs[e] = offsets[e];
+    cnt[e] = offsets[e + 1] - offsets[e];
+  }
+  __syncthreads();
+  build_tiles(cnt, offs, E, bm_a, scratch, wave_tmp, tiles_a, ntiles_a);
+  build_tiles(cnt, offs, E, bm_b, scratch, wave_tmp, tiles_b, ntiles_b);
+}
+
+int bits_for(int E) {
+  int b = 0;
+  while ((1 << b) <= E) ++b;   // keys 0..E (E is the drop sentinel)
+  return b;
+}
+
+}  // namespace
+
+size_t route_scratch_bytes(int64_t S, int E) {
+  if (S <= kSmallMax) return 0;
+  const int64_t nwaves = (S + kLargeChunk - 1) / kLargeChunk;
+  const int64_t nwaves4 = (nwaves + 3) / 4 * 4;
+  return (size_t)nwaves4 * E * sizeof(int32_t);
+}
+
+int64_t max_tiles(int64_t S, int E, int bm) {
+  // sum_e ceil(c_e / bm) <= (S + min(E, S) * (bm - 1)) / bm
+  const int64_t touched = S < E ? S : E;
+  return (S + touched * (bm - 1)) / bm;
+}
+
+hipError_t launch_route(const int32_t* ids, int T, int K, int E, int32_t* counts, int32_t* offsets,
+                        int32_t* sorted_slot, int32_t* slot_row, void* ws, Tile* tiles_a, int32_t* ntiles_a,
+                        int bm_a, Tile* tiles_b, int32_t* ntiles_b, int bm_b, hipStream_t stream) {
+  const int64_t S = (int64_t)T * K;
+  const int nbits = bits_for(E);
+  if (S <= 512) {
+    constexpr int NW = 4;
+    const size_t lds = sizeof(int) * (size_t)(NW * E + 3 * E + 1 + NW);
+    hipLaunchKernelGGL(k_route_small<NW>, dim3(1), dim3(NW * kWave), lds, stream, ids, (int)S, E, nbits, counts,
+                       offsets, sorted_slot, slot_row, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b);
+    return hipGetLastError();
+  }
+  if (S <= kSmallMax) {
+    constexpr int NW = 16;
+    const size_t lds = sizeof(int) * (size_t)(NW * E + 3 * E + 1 + NW);
+    hipLaunchKernelGGL(k_route_small<NW>, dim3(1), dim3(NW * kWave), lds, stream, ids, (int)S, E, nbits, counts,
+                       offsets, sorted_slot, slot_row, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b);
+    return hipGetLastError();
+  }
+  int32_t* ghist = static_cast<int32_t*>(ws);
+  const int64_t nwaves = (S + kLargeChunk - 1) / kLargeChunk;
+  const int nblocks = (int)((nwaves + 3) / 4);
+  hipLaunchKernelGGL(k_route_count, dim3(nblocks), dim3(256), sizeof(int) * 4 * E, stream, ids, (int)S, E, nbits,
+                     ghist);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), sizeof(int) * (size_t)(3 * E + 1 + 16), stream, ghist,
+                     nblocks * 4, E, counts, offsets, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_route_scatter, dim3(nblocks), dim3(256), sizeof(int) * 4 * E, stream, ids, (int)S, E,
+                     nbits, ghist, offsets, sorted_slot, slot_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_tiles(const int32_t* offsets, int E, Tile* tiles_a, int32_t* ntiles_a, int bm_a,
+                              Tile* tiles_b, int32_t* ntiles_b, int bm_b, hipStream_t stream) {
+  hipLaunchKernelGGL(k_build_tiles, dim3(1), dim3(256), sizeof(int) * (size_t)(3 * E + 1 + 4), stream, offsets,
+                     E, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b);
+  return hipGetLastError();
+}
+
+}  // namespace qre

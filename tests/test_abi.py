@@ -1,0 +1,93 @@
+"""The C ABI without a GPU: libqre.so loads, exports every function that
+include/qre.h declares, and rejects bad arguments on the host (validation runs
+before any HIP call, so no device is needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import quantized_routed_expert_top_amd as qre
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qre.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qre_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert "qre_moe_forward" in names and len(names) >= 12
+    lib = C.CDLL(qre.library_path())
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    for code in range(0, -10, -1):
+        assert qre.status_string(code) != "unknown status"
+    assert qre.status_string(5) == "unknown status"
+
+
+def _desc(**kw):
+    d = dict(T=32, H=2048, I=512, E=256, K=8, weight_bits=4, group_size=128, act_int8=0)
+    d.update(kw)
+    return qre._Desc(*(d[k] for k, _ in qre._Desc._fields_))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(weight_bits=5), -3), (dict(group_size=64), -4), (dict(act_int8=2), -8),
+    (dict(H=2000), -2), (dict(I=100), -2), (dict(T=-1), -2), (dict(K=0), -2), (dict(K=300), -2),
+    (dict(E=0), -2), (dict(E=1024, K=8), -9), (dict(T=1 << 28, K=8), -9),
+])
+def test_descriptor_validation(kw, code):
+    n = C.c_size_t(0)
+    assert qre._lib().qre_workspace_bytes(C.byref(_desc(**kw)), C.byref(n)) == code
+
+
+def test_workspace_sizes_grow_with_problem():
+    small = qre.workspace_bytes(32, 2048, 512, 256, 8, 4)
+    big = qre.workspace_bytes(512, 2048, 512, 256, 8, 4)
+    a8 = qre.workspace_bytes(512, 2048, 512, 256, 8, 8, act_int8=True)
+    assert 0 < small < big < a8
+    # h (bf16 S x I) and y (bf16 S x H) dominate
+    S = 512 * 8
+    assert big >= S * 512 * 2 + S * 2048 * 2
+
+
+def test_forward_argument_errors_need_no_gpu():
+    L = qre._lib()
+    d = _desc()
+    w = qre._Weights(16, 16, 16, 16, 16, 16)
+    ws = C.c_size_t(0)
+    L.qre_workspace_bytes(C.byref(d), C.byref(ws))
+    P = C.c_void_p
+    # null x
+    assert L.qre_moe_forward(C.byref(d), None, P(16), P(16), C.byref(w), P(16), P(16), ws.value, None) == -1
+    # misaligned out
+    assert L.qre_moe_forward(C.byref(d), P(16), P(16), P(16), C.byref(w), P(24), P(16), ws.value, None) == -5
+    # workspace too small
+    assert L.qre_moe_forward(C.byref(d), P(16), P(16), P(16), C.byref(w), P(32), P(16), ws.value - 1,
+                             None) == -6
+    # missing weight pointer
+    w2 = qre._Weights(16, 16, 16, None, 16, 16)
+    assert L.qre_moe_forward(C.byref(d), P(16), P(16), P(16), C.byref(w2), P(32), P(16), ws.value, None) == -1
+    # zero tokens: valid, nothing enqueued (null pointers allowed)
+    d0 = _desc(T=0)
+    assert L.qre_moe_forward(C.byref(d0), None, None, None, None, None, None, 0, None) == 0
+    # stage calls
+    assert L.qre_quantize_act(P(16), 4, 100, P(16), P(16), None) == -2
+    assert L.qre_quantize_weights(P(16), 4, 256, 3, P(16), P(16), None) == -3
+    assert L.qre_combine(P(16), P(16), P(16), 4, 2, 100, P(16), None) == -2
+    assert L.qre_gate_up(C.byref(_desc(act_int8=1)), P(16), None, None, P(16), C.byref(w), P(16), P(16),
+                         1 << 24, None) == -8
+    d8k = _desc(T=8192)
+    assert L.qre_route(C.byref(d8k), P(16), P(16), P(16), P(16), P(16), None, 0, None) == -1   # needs workspace
+    n = C.c_size_t(0)
+    assert L.qre_stage_workspace_bytes(C.byref(d8k), C.byref(n)) == 0
+    assert L.qre_route(C.byref(d8k), P(16), P(16), P(16), P(16), P(16), P(16), n.value - 1, None) == -6
+    assert L.qre_build_tiles(C.byref(d8k), P(16), P(16), n.value - 1, None) == -6

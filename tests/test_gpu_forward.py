@@ -1,0 +1,130 @@
+"""End-to-end GPU parity of qre_moe_forward against the CPU oracle.
+
+* every weight/activation mode on small problems that span several row tiles
+  and ragged tails (all outputs compared);
+* every workload at its full size, through the same call and launch
+  configuration the benchmark times, compared on a seeded sample of tokens
+  that always includes the first and the last;
+* edge cases: one expert, top-1, duplicate ids, out-of-range ids (dropped and
+  counted), a single token, zero tokens;
+* GPU self-invariants: bit-identical reruns, token permutation, expert
+  relabelling.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_routed_expert_top_amd as qre
+from quantized_routed_expert_top_amd.inputs import (WORKLOADS, Workload, gen_routing, gen_x, sample_tokens,
+                                                    topk_softmax, f32_to_bf16_bits)
+from quantized_routed_expert_top_amd.synthetic import gpu_experts, touched_experts, x_tensor
+from gpu_helpers import assert_parity, bf16_np, oracle_experts, to_gpu_experts
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run_gpu(x_bits, ids, w, W, act_int8):
+    return qre.moe_forward(x_tensor(x_bits, DEV), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), W,
+                           act_int8=act_int8)
+
+
+def _check(wl: Workload, tokens=None, x_bits=None, ids=None, w=None, Wg=None, Wo=None):
+    x_bits = gen_x(wl) if x_bits is None else x_bits
+    if ids is None:
+        ids, w = gen_routing(wl)
+    toks = np.arange(wl.T) if tokens is None else tokens
+    if Wo is None:
+        Wo = oracle_experts(wl, touched_experts(ids[toks], wl.E))
+    if Wg is None:
+        Wg = to_gpu_experts(Wo, wl.weight_bits) if tokens is None else gpu_experts(wl, DEV)
+    out = bf16_np(_run_gpu(x_bits, ids, w, Wg, wl.act_int8))
+    ref32, _, _ = oracle.moe_forward(x_bits, ids, w, Wo, E=wl.E, bits=wl.weight_bits, act_int8=wl.act_int8,
+                                     tokens=None if tokens is None else toks)
+    return assert_parity(out[toks], ref32, what=wl.name)
+
+
+SMALL = [
+    Workload("small_a", T=64, H=512, I=256, E=8, K=2, weight_bits=4, act_int8=False, seed=11),
+    Workload("small_b", T=45, H=384, I=384, E=5, K=3, weight_bits=8, act_int8=False, seed=12),
+    Workload("small_c", T=100, H=256, I=128, E=16, K=4, weight_bits=4, act_int8=True, seed=13),
+    Workload("small_d", T=77, H=640, I=256, E=12, K=6, weight_bits=8, act_int8=True, seed=14,
+             outlier_frac=0.02),
+]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("act_int8", [False, True])
+def test_tiny_workload_all_modes(bits, act_int8):
+    wl = WORKLOADS["tiny_w8a16"].with_(weight_bits=bits, act_int8=act_int8)
+    _check(wl)
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_small_workloads(wl):
+    _check(wl)
+
+
+@pytest.mark.parametrize("name", ["decode_w4a16", "cb_w4a16", "cb_w8a16", "prefill_w8a8", "zipf_w4a16"])
+def test_full_size_workload_sampled(name):
+    wl = WORKLOADS[name]
+    print(f"[full-size parity] {name}", flush=True)
+    tokens = sample_tokens(wl.T, 24 if wl.T > 32 else wl.T, seed=1)
+    st = _check(wl, tokens=tokens)
+    print(f"  {name}: {st}", flush=True)
+
+
+def test_decode_modes_at_full_size():
+    """The decode shape in the three other weight/activation modes."""
+    for bits, a8 in ((8, False), (4, True), (8, True)):
+        wl = WORKLOADS["decode_w4a16"].with_(weight_bits=bits, act_int8=a8)
+        _check(wl, tokens=np.arange(wl.T))
+
+
+def test_edge_cases():
+    rng = np.random.default_rng(3)
+    # one expert, top-1
+    wl = Workload("e1", T=33, H=256, I=128, E=1, K=1, weight_bits=4, act_int8=False, seed=21)
+    _check(wl)
+    # single token, K = E
+    wl = Workload("t1", T=1, H=256, I=256, E=4, K=4, weight_bits=8, act_int8=True, seed=22)
+    _check(wl)
+    # duplicate ids within a token and out-of-range ids (dropped, counted)
+    wl = Workload("dup", T=40, H=256, I=128, E=6, K=3, weight_bits=4, act_int8=False, seed=23)
+    x_bits = gen_x(wl)
+    ids, w = gen_routing(wl)
+    ids[0, 1] = ids[0, 0]
+    ids[1, :] = ids[1, 0]
+    ids[5, 2] = -1
+    ids[9, 0] = wl.E
+    ids[17, 1] = 1 << 30
+    Wo = oracle_experts(wl, range(wl.E))
+    Wg = to_gpu_experts(Wo, wl.weight_bits)
+    _check(wl, x_bits=x_bits, ids=ids, w=w, Wg=Wg, Wo=Wo)
+    ws = torch.empty(qre.workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.K, 4), dtype=torch.uint8, device=DEV)
+    qre.moe_forward(x_tensor(x_bits, DEV), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), Wg,
+                    workspace=ws)
+    assert qre.read_dropped_slots(wl.T, wl.H, wl.I, wl.E, wl.K, 4, False, ws) == 3
+    # zero tokens: nothing to do, output untouched
+    out = torch.full((0, 256), 1.0, dtype=torch.bfloat16, device=DEV)
+    qre.moe_forward(torch.empty((0, 256), dtype=torch.bfloat16, device=DEV),
+                    torch.empty((0, 3), dtype=torch.int32, device=DEV),
+                    torch.empty((0, 3), dtype=torch.float32, device=DEV), Wg, out=out)
+
+
+def test_invariances_decode_shape():
+    wl = WORKLOADS["decode_w4a16"]
+    x_bits = gen_x(wl)
+    ids, w = gen_routing(wl)
+    Wg = gpu_experts(wl, DEV)
+    a = bf16_np(_run_gpu(x_bits, ids, w, Wg, False))
+    for _ in range(2):                                        # bit-identical reruns
+        np.testing.assert_array_equal(bf16_np(_run_gpu(x_bits, ids, w, Wg, False)), a)
+    perm = np.random.default_rng(0).permutation(wl.T)          # token permutation
+    np.testing.assert_array_equal(bf16_np(_run_gpu(x_bits[perm], ids[perm], w[perm], Wg, False)), a[perm])
+    relabel = np.random.default_rng(1).permutation(wl.E)       # expert e -> relabel[e]
+    inv = torch.from_numpy(np.argsort(relabel)).to(DEV)
+    W2 = qre.QuantizedExperts(*(t[inv].contiguous() for t in (Wg.gate_q, Wg.gate_s, Wg.up_q, Wg.up_s,
+                                                              Wg.down_q, Wg.down_s)), Wg.bits)
+    np.testing.assert_array_equal(bf16_np(_run_gpu(x_bits, relabel[ids].astype(np.int32), w, W2, False)), a)

@@ -1,0 +1,239 @@
+"""GPU parity of each step of the routed-expert feed-forward against the CPU
+oracle, through the C ABI: permutation (bit-exact), INT8 quantizers
+(bit-exact), weight converter (bit-exact), combine (bit-exact), and the
+gate/up and down grouped GEMMs (tolerance, plus bit-exact exact-arithmetic
+cases)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_routed_expert_top_amd as qre
+from quantized_routed_expert_top_amd.inputs import Workload, f32_to_bf16_bits, topk_softmax
+from gpu_helpers import assert_parity, bf16_np, bf16_to_f64, oracle_experts, to_gpu_experts
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _ids(T, K, E, seed, bad=0, skew=False):
+    rng = np.random.default_rng(seed)
+    if skew:
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        ids = rng.choice(E, size=(T, K), p=p / p.sum())
+    else:
+        ids = rng.integers(0, E, size=(T, K))
+    ids = ids.astype(np.int32)
+    if bad:
+        flat = ids.reshape(-1)
+        pos = rng.choice(flat.size, size=min(bad, flat.size), replace=False)
+        flat[pos] = rng.choice([-1, E, E + 5, -100], size=pos.size)
+    return ids
+
+
+@pytest.mark.parametrize("T,K,E,bad,skew", [
+    (32, 8, 256, 0, False), (32, 8, 256, 3, False), (512, 8, 256, 0, False), (37, 3, 11, 2, False),
+    (1000, 5, 512, 7, False), (2000, 8, 8, 0, True), (8192, 8, 256, 11, False), (4096, 8, 256, 0, True),
+    (1, 1, 1, 0, False), (0, 4, 16, 0, False), (9000, 1, 300, 5, True),
+])
+def test_route_bit_exact(T, K, E, bad, skew):
+    ids = _ids(T, K, E, seed=T + K + E, bad=bad, skew=skew)
+    c, o, ss, sr, nbad = oracle.route(ids, E)
+    gc, go, gss, gsr, _ = qre.route(torch.from_numpy(ids).to(DEV), E)
+    np.testing.assert_array_equal(gc.cpu().numpy(), c)
+    np.testing.assert_array_equal(go.cpu().numpy(), o)
+    np.testing.assert_array_equal(gss.cpu().numpy(), ss)
+    np.testing.assert_array_equal(gsr.cpu().numpy(), sr)
+    assert T * K - int(go[-1]) == nbad
+
+
+def test_route_is_deterministic():
+    ids = torch.from_numpy(_ids(8192, 8, 256, seed=5)).to(DEV)
+    a = [t.cpu().numpy() for t in qre.route(ids, 256)[:4]]
+    for _ in range(3):
+        b = [t.cpu().numpy() for t in qre.route(ids, 256)[:4]]
+        for u, v in zip(a, b):
+            np.testing.assert_array_equal(u, v)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 128), (37, 256), (512, 2048), (300, 1536)])
+def test_quantize_act_bit_exact(rows, cols):
+    rng = np.random.default_rng(rows + cols)
+    v = rng.standard_normal((rows, cols)).astype(np.float32)
+    v[:, rng.choice(cols, max(1, cols // 100), replace=False)] *= 20.0
+    v[0, :128] = 0.0
+    if rows > 2:
+        v[2, :128] = np.array([127.0, 2.5, 3.5, -0.5, 126.5, -2.5, 1.5] + [0.0] * 121) * 2.0 ** -3
+    vb = f32_to_bf16_bits(v)
+    q, s = oracle.quantize_act(vb)
+    gq, gs = qre.quantize_act(torch.from_numpy(vb.view(np.int16)).to(DEV).view(torch.bfloat16))
+    np.testing.assert_array_equal(gq.cpu().numpy(), q)
+    np.testing.assert_array_equal(gs.cpu().numpy().view(np.uint32), s.view(np.uint32))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("rows,cols", [(3, 128), (257, 512), (1024, 2048)])
+def test_quantize_weights_bit_exact(bits, rows, cols):
+    rng = np.random.default_rng(bits * 1000 + rows)
+    w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    w[0, :128] = 0.0                                       # zero group
+    w[1 % rows, 128 % cols:(128 % cols) + 128] *= 1e-4     # tiny group: subnormal FP16 scale
+    w[-1, -128:] *= 1e3
+    q, s = oracle.quantize_weights(w, bits)
+    gq, gs = qre.quantize_weights(torch.from_numpy(w).to(DEV), bits)
+    np.testing.assert_array_equal(gq.cpu().numpy(), q)
+    np.testing.assert_array_equal(gs.cpu().view(torch.int16).numpy().view(np.uint16), s)
+
+
+@pytest.mark.parametrize("T,K,H", [(32, 8, 2048), (5, 3, 256), (300, 8, 4096), (64, 1, 128)])
+def test_combine_bit_exact(T, K, H):
+    rng = np.random.default_rng(T * K + H)
+    E = 16
+    ids = _ids(T, K, E, seed=T, bad=2 if T * K > 4 else 0)
+    _, _, _, slot_row, _ = oracle.route(ids, E)
+    _, w = topk_softmax(rng.standard_normal((T, E)).astype(np.float32), K)
+    y = f32_to_bf16_bits(rng.standard_normal((T * K, H)).astype(np.float32))
+    _, o16 = oracle.combine(y, slot_row, w, T=T, K=K, H=H)
+    g = qre.combine(torch.from_numpy(y.view(np.int16)).to(DEV).view(torch.bfloat16),
+                    torch.from_numpy(slot_row).to(DEV), torch.from_numpy(w).to(DEV))
+    np.testing.assert_array_equal(bf16_np(g), o16)
+
+
+# ---- grouped GEMMs -------------------------------------------------------------
+
+STAGE_SHAPES = [
+    # T, H, I, E, K: several 16-row tiles per expert, ragged tails, all column blocks
+    (64, 512, 256, 8, 2),
+    (45, 384, 128, 5, 3),
+    (32, 2048, 512, 256, 8),
+]
+
+
+def _stage_problem(T, H, I, E, K, bits, seed):
+    wl = Workload("stage", T=T, H=H, I=I, E=E, K=K, weight_bits=bits, act_int8=False, seed=seed)
+    rng = np.random.default_rng([seed, 77])
+    x = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    ids, w = topk_softmax(rng.standard_normal((T, E)).astype(np.float32), K)
+    touched = np.unique(ids)
+    Wo = oracle_experts(wl, touched)
+    return x, ids, w, Wo
+
+
+@pytest.mark.parametrize("act_int8", [False, True])
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("shape", STAGE_SHAPES)
+def test_gate_up_and_down_stages(shape, bits, act_int8):
+    T, H, I, E, K = shape
+    x, ids, w, Wo = _stage_problem(T, H, I, E, K, bits, seed=sum(shape) + bits)
+    counts, offsets, sorted_slot, slot_row, _ = oracle.route(ids, E)
+    shp = dict(T=T, H=H, I=I, E=E, K=K, bits=bits)
+    Wg = to_gpu_experts(Wo, bits)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    ws = qre.build_tiles(t(offsets), T, H, I, E, K, bits, act_int8)
+    nvalid = int(offsets[-1])
+    if act_int8:
+        xq, xs = oracle.quantize_act(x)
+        h_ref = oracle.gate_up(None, sorted_slot, offsets, Wo, act_int8=True, xq=xq, xs=xs, **shp)
+        h_gpu = qre.gate_up(None, t(sorted_slot), Wg, K, ws, act_int8=True, xq=t(xq), xs=t(xs))
+    else:
+        h_ref = oracle.gate_up(x, sorted_slot, offsets, Wo, **shp)
+        h_gpu = qre.gate_up(t(x.view(np.int16)).view(torch.bfloat16), t(sorted_slot), Wg, K, ws)
+    assert_parity(bf16_np(h_gpu)[:nvalid], bf16_to_f64(h_ref[:nvalid]), what="h")
+    # down, fed the oracle's h
+    if act_int8:
+        hq, hs = oracle.quantize_act(h_ref)
+        y_ref = oracle.down(None, offsets, Wo, act_int8=True, hq=hq, hs=hs, **shp)
+        y_gpu = qre.down(None, Wg, T, K, ws, act_int8=True, hq=t(hq), hs=t(hs))
+    else:
+        y_ref = oracle.down(h_ref, offsets, Wo, **shp)
+        y_gpu = qre.down(t(h_ref.view(np.int16)).view(torch.bfloat16), Wg, T, K, ws)
+    assert_parity(bf16_np(y_gpu)[:nvalid], bf16_to_f64(y_ref[:nvalid]), what="y")
+
+
+@pytest.mark.parametrize("act_int8", [False, True])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gemm_exact_arithmetic_case(bits, act_int8):
+    """Small integers on power-of-two scales: every partial sum is exact in
+    FP32, every gate is >= 17 (so SiLU(g) = g in FP32 and in the oracle's
+    double), and g * u has at most 21 significant bits, so GPU and oracle must
+    agree bit for bit whatever the summation order."""
+    T, H, I, E, K = 40, 512, 128, 3, 2
+    qmax = 7 if bits == 4 else 127
+    rng = np.random.default_rng(bits + 10 * act_int8)
+    # x = xc * 2^-2: 127 at every 8th input (so every group max is 127 and the
+    # INT8 quantization of x is exact), 0 at input 2 of each group, else -3..3
+    xc = rng.integers(-3, 4, size=(T, H))
+    xc[:, ::8] = 127
+    xc[:, 2::128] = 0
+    x = f32_to_bf16_bits((xc * 2.0 ** -2).astype(np.float32))
+    def mats():
+        # codes on scale 2^-6; each group's qmax sits at input 2, where x = 0
+        g = np.zeros((I, H))
+        c = rng.integers(36, 65, size=I)               # g = 127 c / 256 in [17.9, 31.8]
+        for i in range(I):
+            g[i, np.arange(0, H, 8)[:c[i]]] = 1
+        g[:, 2::128] = qmax
+        u = np.zeros((I, H))
+        u[:, 1::8] = rng.integers(-1, 2, size=(I, H // 8))
+        u[:, 2::128] = qmax
+        d = rng.integers(-1, 2, size=(H, I)) * 1.0
+        d[:, ::128] = qmax
+        return [(m * 2.0 ** -6).astype(np.float32) for m in (g, u, d)]
+    ws = [mats() for _ in range(E)]
+    qs = [[oracle.quantize_weights(m, bits) for m in e] for e in ws]
+    st = lambda j, k: np.stack([qs[e][j][k] for e in range(E)])
+    Wo = oracle.QWeights(st(0, 0), st(0, 1), st(1, 0), st(1, 1), st(2, 0), st(2, 1))
+    assert np.all(Wo.gate_s == np.float16(2.0 ** -6).view(np.uint16))
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    counts, offsets, sorted_slot, slot_row, _ = oracle.route(ids, E)
+    shp = dict(T=T, H=H, I=I, E=E, K=K, bits=bits)
+    Wg = to_gpu_experts(Wo, bits)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    ws = qre.build_tiles(t(offsets), T, H, I, E, K, bits, act_int8)
+    if act_int8:
+        xq, xs = oracle.quantize_act(x)
+        assert np.all(xs == 2.0 ** -2)
+        h_ref = oracle.gate_up(None, sorted_slot, offsets, Wo, act_int8=True, xq=xq, xs=xs, **shp)
+        h_gpu = qre.gate_up(None, t(sorted_slot), Wg, K, ws, act_int8=True, xq=t(xq), xs=t(xs))
+    else:
+        h_ref = oracle.gate_up(x, sorted_slot, offsets, Wo, **shp)
+        h_gpu = qre.gate_up(t(x.view(np.int16)).view(torch.bfloat16), t(sorted_slot), Wg, K, ws)
+    assert np.mean(bf16_to_f64(h_ref) != 0) > 0.5
+    np.testing.assert_array_equal(bf16_np(h_gpu), h_ref)
+    # down on an exactly representable h (INT8 grid of scale 2^-3)
+    hc = rng.integers(-4, 5, size=(T * K, I))
+    hc[:, ::128] = 127
+    hb = f32_to_bf16_bits((hc * 2.0 ** -3).astype(np.float32))
+    if act_int8:
+        hq, hs = oracle.quantize_act(hb)
+        y_ref = oracle.down(None, offsets, Wo, act_int8=True, hq=hq, hs=hs, **shp)
+        y_gpu = qre.down(None, Wg, T, K, ws, act_int8=True, hq=t(hq), hs=t(hs))
+    else:
+        y_ref = oracle.down(hb, offsets, Wo, **shp)
+        y_gpu = qre.down(t(hb.view(np.int16)).view(torch.bfloat16), Wg, T, K, ws)
+    np.testing.assert_array_equal(bf16_np(y_gpu), y_ref)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_extreme_codes_decode(bits):
+    """Codes the quantizer never emits (-8 for INT4, -128 for INT8) still decode
+    correctly: hand-packed weights, one expert, top-1."""
+    T, H, I = 16, 128, 128
+    qmin = -8 if bits == 4 else -128
+    codes = np.full((I, H), qmin, np.int64)
+    codes[:, 1::2] = 1
+    if bits == 4:
+        packed = ((codes[:, 0::2] & 0xF) | ((codes[:, 1::2] & 0xF) << 4)).astype(np.uint8)
+    else:
+        packed = (codes & 0xFF).astype(np.uint8)
+    s = np.full((I, 1), np.float16(2.0 ** -4).view(np.uint16), np.uint16)
+    Wo = oracle.QWeights(packed[None], s[None], packed[None], s[None], packed[None], s[None])
+    x = f32_to_bf16_bits(np.random.default_rng(0).standard_normal((T, H)).astype(np.float32))
+    ids = np.zeros((T, 1), np.int32)
+    counts, offsets, sorted_slot, _, _ = oracle.route(ids, 1)
+    shp = dict(T=T, H=H, I=I, E=1, K=1, bits=bits)
+    h_ref = oracle.gate_up(x, sorted_slot, offsets, Wo, **shp)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    ws = qre.build_tiles(t(offsets), T, H, I, 1, 1, bits)
+    h_gpu = qre.gate_up(t(x.view(np.int16)).view(torch.bfloat16), t(sorted_slot), to_gpu_experts(Wo, bits), 1, ws)
+    assert_parity(bf16_np(h_gpu), bf16_to_f64(h_ref), what="h")
