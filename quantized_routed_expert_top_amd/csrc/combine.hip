@@ -13,6 +13,8 @@
 namespace qre {
 namespace {
 
+constexpr int kUnroll = 8;   // slots whose loads are in flight together
+
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y, const int32_t* __restrict__ slot_row,
                                                  const float* __restrict__ topk_w, int K, int H,
                                                  uint16_t* __restrict__ out) {
@@ -22,16 +24,29 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-  for (int k = 0; k < K; ++k) {
-    const int32_t r = slot_row[t * K + k];
-    if (r < 0) continue;
-    const float wk = topk_w[t * K + k];
-    const uint4 v = *reinterpret_cast<const uint4*>(y + (int64_t)r * H + col);
-    const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+  for (int k0 = 0; k0 < K; k0 += kUnroll) {
+    // issue every load of this batch of slots before the first FMA
+    int32_t r[kUnroll];
+    float wk[kUnroll];
+    uint4 v[kUnroll];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[2 * j] = __builtin_fmaf(wk, bf16_bits_to_f32(p[j] & 0xffffu), acc[2 * j]);
-      acc[2 * j + 1] = __builtin_fmaf(wk, bf16_bits_to_f32(p[j] >> 16), acc[2 * j + 1]);
+    for (int u = 0; u < kUnroll; ++u) {
+      r[u] = (k0 + u < K) ? slot_row[t * K + k0 + u] : -1;
+      wk[u] = (k0 + u < K) ? topk_w[t * K + k0 + u] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      v[u] = r[u] >= 0 ? *reinterpret_cast<const uint4*>(y + (int64_t)r[u] * H + col) : make_uint4(0, 0, 0, 0);
+    // k ascending, one FMA per term; a dropped slot is skipped, not added as 0
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (r[u] < 0) continue;
+      const uint32_t p[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] = __builtin_fmaf(wk[u], bf16_bits_to_f32(p[j] & 0xffffu), acc[2 * j]);
+        acc[2 * j + 1] = __builtin_fmaf(wk[u], bf16_bits_to_f32(p[j] >> 16), acc[2 * j + 1]);
+      }
     }
   }
   uint32_t o[4];

@@ -13,10 +13,14 @@
 // INT32 and the scaled groups are combined in FP32; outputs return to BF16.
 //
 // CDNA4 mapping (this is the kernel's own design, not the pages'):
-//  * one wave computes a 16-row x 16*FN-column tile (both gate and up for the
-//    fused kernel) over the whole reduction, so each weight byte is read from
-//    HBM exactly once per 16-row tile, with 16-byte loads per lane (64
-//    contiguous bytes per weight row per 128-group for INT4, 128 for INT8);
+//  * a workgroup computes a 16-row x 16*FN-column tile (both gate and up for
+//    the fused kernel), so each weight byte is read from HBM once per 16-row
+//    tile, with 16-byte loads per lane (64 contiguous bytes per weight row per
+//    128-group for INT4, 128 for INT8).  Its four waves split the reduction:
+//    each takes chunks of GW consecutive 128-groups, issues every load of a
+//    chunk before its first MFMA (straight-line code, so the compiler waits
+//    for exactly the group it needs next), and the four partial sums are
+//    added through LDS in a fixed wave order (deterministic);
 //  * a 128-group is four v_mfma_f32_16x16x32_bf16 steps (BF16 activations) or
 //    two v_mfma_i32_16x16x64_i8 steps (INT8 activations); the group's partial
 //    sums are scaled by the FP16 weight scale (and the FP32 activation scale)
@@ -31,8 +35,9 @@
 //  * nibble extraction pairs codes k and k+4 of each 32-bit word, so A is
 //    permuted the same way with v_perm_b32 (a dot product is invariant under a
 //    common permutation of the reduction index);
-//  * loads of group g+PD are issued while group g is multiplied (a register
-//    ring of PD groups) to keep enough bytes in flight for HBM;
+//  * all loads are raw buffer loads: a masked row or a group past the end of
+//    the reduction uses an out-of-range offset, which returns zeros without
+//    touching memory, so no load sits behind a branch;
 //  * workgroups are (column block, row tile); tiles past the device-side tile
 //    count exit at once, so no host readback is needed.
 #include <hip/hip_fp16.h>
@@ -43,8 +48,22 @@ namespace qre {
 namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-__device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+constexpr uint32_t kOOB = 0x80000000u;   // offset past every descriptor (all are < 2^31 bytes)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t bload16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t bload_u16(rsrc_t r, uint32_t off) {
+  return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ float bload_f32(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
@@ -52,17 +71,83 @@ __device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
   return __half2float(__ushort_as_half((unsigned short)h));
 }
 
+// A constant materialized in a VGPR: lets (x & M) | C select one v_and_or_b32
+// (a GFX9 VOP3 instruction reads at most one SGPR or literal).
+template <uint32_t C>
+__device__ __forceinline__ uint32_t vconst() {
+  uint32_t v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "i"(C));
+  return v;
+}
+
 // Two BF16 values (exact small integers held in FP32) packed into one dword.
 __device__ __forceinline__ uint32_t pack_bf16_hi(float lo, float hi) {
   return byte_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
-template <int WB, bool A8, bool DUAL, int FN, int PD>
+// A operand of one MFMA step (16 bytes: 8 BF16 or 16 INT8 activations),
+// permuted into the reduction order of the INT4 weight operand below.  INT8
+// weights need no permutation.
+template <int WB, bool A8>
+__device__ __forceinline__ u32x4_t a_operand(u32x4_t c) {
+  if constexpr (WB == 8) return c;
+  u32x4_t av;
+  if constexpr (!A8) {        // BF16: pair codes k and k+4 of each 32-bit word
+    av.x = byte_perm(c.z, c.x, 0x05040100u);
+    av.y = byte_perm(c.z, c.x, 0x07060302u);
+    av.z = byte_perm(c.w, c.y, 0x05040100u);
+    av.w = byte_perm(c.w, c.y, 0x07060302u);
+  } else {                    // INT8: even codes then odd codes of each 32-bit word
+    av.x = byte_perm(c.y, c.x, 0x06040200u);
+    av.y = byte_perm(c.y, c.x, 0x07050301u);
+    av.z = byte_perm(c.w, c.z, 0x06040200u);
+    av.w = byte_perm(c.w, c.z, 0x07050301u);
+  }
+  return av;
+}
+
+// B operand for BF16 activations, MFMA step t (of 4), from the lane's slice of
+// a 128-group of one weight row (16 bytes INT4 / 32 bytes INT8).  The values
+// are 136 + q (INT4) or 128 + q (INT8), exact in BF16.
+template <int WB>
+__device__ __forceinline__ u32x4_t b_operand_bf16(const u32x4_t* b, int t, uint32_t mask_nib, uint32_t magic) {
+  u32x4_t bv;
+  if constexpr (WB == 4) {
+    const uint32_t w = b[0][t] ^ 0x88888888u;             // nibble -> q + 8
+    bv.x = (w & mask_nib) | magic;                        // bf16 (136+q_k, 136+q_{k+4})
+    bv.y = ((w >> 4) & mask_nib) | magic;
+    bv.z = ((w >> 8) & mask_nib) | magic;
+    bv.w = ((w >> 12) & mask_nib) | magic;
+  } else {
+    const uint32_t w0 = b[t >> 1][(t & 1) * 2] ^ 0x80808080u;       // byte -> q + 128
+    const uint32_t w1 = b[t >> 1][(t & 1) * 2 + 1] ^ 0x80808080u;
+    bv.x = pack_bf16_hi((float)(w0 & 0xffu), (float)((w0 >> 8) & 0xffu));
+    bv.y = pack_bf16_hi((float)((w0 >> 16) & 0xffu), (float)(w0 >> 24));
+    bv.z = pack_bf16_hi((float)(w1 & 0xffu), (float)((w1 >> 8) & 0xffu));
+    bv.w = pack_bf16_hi((float)((w1 >> 16) & 0xffu), (float)(w1 >> 24));
+  }
+  return bv;
+}
+
+// B operand for INT8 activations, MFMA step t (of 2): INT8 codes as they are,
+// INT4 codes as q + 8 (even codes then odd codes of each word).
+template <int WB>
+__device__ __forceinline__ u32x4_t b_operand_i8(const u32x4_t* b, int t) {
+  if constexpr (WB == 8) return b[t];
+  const uint32_t w0 = b[0][2 * t] ^ 0x88888888u;
+  const uint32_t w1 = b[0][2 * t + 1] ^ 0x88888888u;
+  return u32x4_t{w0 & 0x0f0f0f0fu, (w0 >> 4) & 0x0f0f0f0fu, w1 & 0x0f0f0f0fu, (w1 >> 4) & 0x0f0f0f0fu};
+}
+
+template <int WB, bool A8, bool DUAL, int FN, int GW>
 struct Gemm16 {
   static constexpr int NM = DUAL ? 2 : 1;                // weight matrices
   static constexpr int NA = A8 ? 2 : 4;                  // 16-byte A chunks per lane per group
   static constexpr int NB = (WB == 4) ? 1 : 2;           // 16-byte B chunks per lane per group
-  static constexpr int BN = 4 * 16 * FN;                 // columns per workgroup
+  static constexpr int BN = 16 * FN;                     // columns per workgroup
+  static constexpr int NW = 4;                           // waves per workgroup (split the reduction)
+  static constexpr int A_GROUP_BYTES = A8 ? kGroup : 2 * kGroup;
+  static constexpr int W_GROUP_BYTES = kGroup * WB / 8;
 
   struct Buf {
     u32x4_t a[NA];
@@ -72,14 +157,19 @@ struct Gemm16 {
   };
 
   const GemmProblem& p;
-  int lane, li, kb, G, e, row0, nrows, n_wave;
-  bool arow_ok;
-  const uint8_t* a_row;          // this lane's A row (byte pointer)
-  int64_t erow[4];               // A rows (for activation scales) of accumulator rows 4kb+r
-  const uint8_t* wq[FN][NM];
-  const uint16_t* wsp[FN][NM];
+  int wave, lane, li, kb, G, e, row0, nrows, n_blk;
+  rsrc_t ra, rxs, rw[NM], rs[NM];
+  uint32_t a_off;              // byte offset of this lane's A row (+ k offset), or kOOB
+  uint32_t xs_off[4];          // byte offsets of the activation scales of rows 4kb+r (INT8 mode)
+  uint32_t w_off[FN];          // byte offset of this lane's weight row in the expert's matrix
+  uint32_t s_off[FN];          // byte offset of this lane's scale row
 
-  __device__ Gemm16(const GemmProblem& prob, const Tile& td, int wave) : p(prob) {
+  uint32_t kMaskNib, kMagic;     // 0x000f000f, 0x43004300 in VGPRs
+
+  __device__ Gemm16(const GemmProblem& prob, const Tile& td, int col0) : p(prob) {
+    kMaskNib = vconst<0x000f000fu>();
+    kMagic = vconst<0x43004300u>();
+    wave = threadIdx.x >> 6;
     lane = threadIdx.x & 63;
     li = lane & 15;
     kb = lane >> 4;
@@ -87,55 +177,70 @@ struct Gemm16 {
     e = td.e;
     row0 = td.row0;
     nrows = td.nrows;
-    n_wave = (blockIdx.x * 4 + wave) * 16 * FN;
-    const int a_elem = A8 ? 1 : 2;
-    arow_ok = li < nrows;
-    a_row = nullptr;
-    if (arow_ok) {
+    n_blk = col0;
+    const int64_t a_rows = p.a_rows;
+    ra = make_rsrc(p.a, a_rows * G * A_GROUP_BYTES);
+    a_off = kOOB;
+    if (li < nrows) {
       const int r = row0 + li;
       const int64_t ar = p.gather_k ? (int64_t)(p.sorted_slot[r] / p.gather_k) : (int64_t)r;
-      a_row = static_cast<const uint8_t*>(p.a) + ar * p.kdim * a_elem;
+      a_off = (uint32_t)(ar * G * A_GROUP_BYTES + kb * 32 * (A8 ? 1 : 2));
     }
+    if constexpr (A8) {
+      rxs = make_rsrc(p.a_scale, a_rows * G * 4);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 4 * kb + r;
-      erow[r] = -1;
-      if (A8 && m < nrows) erow[r] = p.gather_k ? (int64_t)(p.sorted_slot[row0 + m] / p.gather_k) : (int64_t)(row0 + m);
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * kb + r;
+        xs_off[r] = kOOB;
+        if (m < nrows) {
+          const int64_t ar = p.gather_k ? (int64_t)(p.sorted_slot[row0 + m] / p.gather_k) : (int64_t)(row0 + m);
+          xs_off[r] = (uint32_t)(ar * G * 4);
+        }
+      }
     }
-    const int64_t row_bytes = (int64_t)p.kdim * WB / 8;
+    const int64_t mat_bytes = (int64_t)p.n * G * W_GROUP_BYTES;
+    const int64_t smat_bytes = (int64_t)p.n * G * 2;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      rw[m] = make_rsrc((m == 0 ? p.w0q : p.w1q) + e * mat_bytes, mat_bytes);
+      rs[m] = make_rsrc((m == 0 ? p.w0s : p.w1s) + e * (int64_t)p.n * G, smat_bytes);
+    }
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
-      const int64_t n = (int64_t)e * p.n + n_wave + f * 16 + li;
-#pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        wq[f][m] = (m == 0 ? p.w0q : p.w1q) + n * row_bytes;
-        wsp[f][m] = (m == 0 ? p.w0s : p.w1s) + n * G;
-      }
+      const int n = n_blk + f * 16 + li;
+      w_off[f] = (uint32_t)((int64_t)n * G * W_GROUP_BYTES + kb * (WB == 4 ? 16 : 32));
+      s_off[f] = (uint32_t)((int64_t)n * G * 2);
     }
   }
 
+  // Issue the loads of group g into bf.  With kCheck, g >= G loads nothing
+  // (out-of-range offsets); without it the caller guarantees g < G, and every
+  // per-group offset is a compile-time immediate on a per-lane base.  A masked
+  // row's base is kOOB, and kOOB plus any in-row offset stays out of range.
+  template <bool kCheck>
   __device__ __forceinline__ void load(Buf& bf, int g) const {
-    if (arow_ok) {
-      const uint8_t* ap = a_row + (int64_t)(g * kGroup + kb * 32) * (A8 ? 1 : 2);
+    const bool in = !kCheck || g < G;
+    // issue order: scales, weights, activations (the MFMAs need the last two,
+    // the scales come last in the group's arithmetic, so one wait covers all)
 #pragma unroll
-      for (int j = 0; j < NA; ++j) bf.a[j] = ld16(ap + 16 * j);
-    } else {
+    for (int f = 0; f < FN; ++f)
 #pragma unroll
-      for (int j = 0; j < NA; ++j) bf.a[j] = u32x4_t{0u, 0u, 0u, 0u};
-    }
+      for (int m = 0; m < NM; ++m) bf.s[f][m] = bload_u16(rs[m], in ? s_off[f] + 2u * g : kOOB);
     if constexpr (A8) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) bf.xs[r] = erow[r] >= 0 ? p.a_scale[erow[r] * G + g] : 0.0f;
+      for (int r = 0; r < 4; ++r) bf.xs[r] = bload_f32(rxs, in ? xs_off[r] + 4u * g : kOOB);
     }
 #pragma unroll
     for (int f = 0; f < FN; ++f)
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        const uint8_t* bp = wq[f][m] + (int64_t)g * (kGroup * WB / 8) + kb * (WB == 4 ? 16 : 32);
+        const uint32_t wo = in ? w_off[f] + (uint32_t)g * W_GROUP_BYTES : kOOB;
 #pragma unroll
-        for (int j = 0; j < NB; ++j) bf.b[f][m][j] = ld16(bp + 16 * j);
-        bf.s[f][m] = wsp[f][m][g];
+        for (int j = 0; j < NB; ++j) bf.b[f][m][j] = bload16(rw[m], wo + 16 * j);
       }
+    const uint32_t ao = in ? a_off + (uint32_t)g * A_GROUP_BYTES : kOOB;
+#pragma unroll
+    for (int j = 0; j < NA; ++j) bf.a[j] = bload16(ra, ao + 16 * j);
   }
 
   // BF16 activations: one 128-group, accumulated into acc[f][m] (FP32).
@@ -149,37 +254,13 @@ struct Gemm16 {
     const u32x4_t ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const u32x4_t c = bf.a[t];
-      u32x4_t av;
-      if constexpr (WB == 4) {   // match the nibble pairing (k, k+4)
-        av.x = byte_perm(c.z, c.x, 0x05040100u);
-        av.y = byte_perm(c.z, c.x, 0x07060302u);
-        av.z = byte_perm(c.w, c.y, 0x05040100u);
-        av.w = byte_perm(c.w, c.y, 0x07060302u);
-      } else {
-        av = c;
-      }
-      const bf16x8_t a8 = __builtin_bit_cast(bf16x8_t, av);
+      const bf16x8_t a8 = __builtin_bit_cast(bf16x8_t, a_operand<WB, false>(bf.a[t]));
       accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, __builtin_bit_cast(bf16x8_t, ones), accx, 0, 0, 0);
 #pragma unroll
       for (int f = 0; f < FN; ++f)
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-          u32x4_t bv;
-          if constexpr (WB == 4) {
-            const uint32_t w = bf.b[f][m][0][t] ^ 0x88888888u;   // nibble -> q + 8
-            bv.x = (w & 0x000f000fu) | 0x43004300u;              // bf16 (136+q_k, 136+q_{k+4})
-            bv.y = ((w >> 4) & 0x000f000fu) | 0x43004300u;
-            bv.z = ((w >> 8) & 0x000f000fu) | 0x43004300u;
-            bv.w = ((w >> 12) & 0x000f000fu) | 0x43004300u;
-          } else {
-            const uint32_t w0 = bf.b[f][m][t >> 1][(t & 1) * 2] ^ 0x80808080u;       // byte -> q + 128
-            const uint32_t w1 = bf.b[f][m][t >> 1][(t & 1) * 2 + 1] ^ 0x80808080u;
-            bv.x = pack_bf16_hi((float)(w0 & 0xffu), (float)((w0 >> 8) & 0xffu));
-            bv.y = pack_bf16_hi((float)((w0 >> 16) & 0xffu), (float)(w0 >> 24));
-            bv.z = pack_bf16_hi((float)(w1 & 0xffu), (float)((w1 >> 8) & 0xffu));
-            bv.w = pack_bf16_hi((float)((w1 >> 16) & 0xffu), (float)(w1 >> 24));
-          }
+          const u32x4_t bv = b_operand_bf16<WB>(bf.b[f][m], t, kMaskNib, kMagic);
           accg[f][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, __builtin_bit_cast(bf16x8_t, bv), accg[f][m],
                                                                0, 0, 0);
         }
@@ -206,33 +287,13 @@ struct Gemm16 {
     const i32x4_t ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const u32x4_t c = bf.a[t];
-      u32x4_t av;
-      if constexpr (WB == 4) {   // match the nibble split (even codes, odd codes) of each word
-        av.x = byte_perm(c.y, c.x, 0x06040200u);
-        av.y = byte_perm(c.y, c.x, 0x07050301u);
-        av.z = byte_perm(c.w, c.z, 0x06040200u);
-        av.w = byte_perm(c.w, c.z, 0x07050301u);
-      } else {
-        av = c;
-      }
-      const i32x4_t ai = __builtin_bit_cast(i32x4_t, av);
+      const i32x4_t ai = __builtin_bit_cast(i32x4_t, a_operand<WB, true>(bf.a[t]));
       if constexpr (WB == 4) accx = __builtin_amdgcn_mfma_i32_16x16x64_i8(ai, ones, accx, 0, 0, 0);
 #pragma unroll
       for (int f = 0; f < FN; ++f)
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-          u32x4_t bv;
-          if constexpr (WB == 4) {
-            const uint32_t w0 = bf.b[f][m][0][2 * t] ^ 0x88888888u;       // nibble -> q + 8
-            const uint32_t w1 = bf.b[f][m][0][2 * t + 1] ^ 0x88888888u;
-            bv.x = w0 & 0x0f0f0f0fu;
-            bv.y = (w0 >> 4) & 0x0f0f0f0fu;
-            bv.z = w1 & 0x0f0f0f0fu;
-            bv.w = (w1 >> 4) & 0x0f0f0f0fu;
-          } else {
-            bv = bf.b[f][m][t];
-          }
+          const u32x4_t bv = b_operand_i8<WB>(bf.b[f][m], t);
           accg[f][m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ai, __builtin_bit_cast(i32x4_t, bv), accg[f][m], 0, 0, 0);
         }
     }
@@ -249,78 +310,429 @@ struct Gemm16 {
       }
   }
 
-  __device__ void run() const {
+  __device__ __forceinline__ void group(const Buf& bf, f32x4_t (&acc)[FN][NM]) const {
+    if constexpr (A8) group_i8(bf, acc);
+    else group_bf16(bf, acc);
+  }
+
+  // Store rows 4kb+r of column li of every fragment (lane layout of the MFMA
+  // accumulator), applying SiLU*mul for the fused gate/up GEMM.
+  __device__ __forceinline__ void store(const f32x4_t (&v)[FN][NM], int f) const {
+    uint16_t* out = static_cast<uint16_t*>(p.out);
+    const int64_t col = n_blk + f * 16 + li;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * kb + r;
+      if (m < nrows) {
+        float o;
+        if constexpr (DUAL) o = silu(v[f][0][r]) * v[f][1][r];
+        else o = v[f][0][r];
+        out[(int64_t)(row0 + m) * p.n + col] = (uint16_t)f32_to_bf16_bits(o);
+      }
+    }
+  }
+
+  // One wave, whole reduction of NG (compile-time) groups, in chunks of GW
+  // groups with two chunks in flight: the loads of chunk c+2 are issued as soon
+  // as chunk c is consumed.  Everything is unrolled, so each wait is exact.
+  template <int NG>
+  __device__ void run_stream() const {
+    constexpr int NC = (NG + GW - 1) / GW;
     f32x4_t acc[FN][NM];
 #pragma unroll
     for (int f = 0; f < FN; ++f)
 #pragma unroll
       for (int m = 0; m < NM; ++m) acc[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    Buf buf[PD];
+    Buf b[2][GW];
 #pragma unroll
-    for (int j = 0; j < PD; ++j)
-      if (j < G) load(buf[j], j);
-    for (int g0 = 0; g0 < G; g0 += PD) {
+    for (int c = 0; c < 2 && c < NC; ++c) {
 #pragma unroll
-      for (int j = 0; j < PD; ++j) {
-        const int g = g0 + j;
-        if (g < G) {
-          if constexpr (A8) group_i8(buf[j], acc);
-          else group_bf16(buf[j], acc);
-          if (g + PD < G) load(buf[j], g + PD);
-        }
+      for (int j = 0; j < GW; ++j) {
+        load<false>(b[c][j], c * GW + j);
+        __builtin_amdgcn_sched_barrier(0);     // keep the groups' loads in order
       }
     }
-    // epilogue: lane holds rows 4kb+r of column li of each 16-column fragment
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int j = 0; j < GW; ++j)
+        if (c * GW + j < NG) group(b[c & 1][j], acc);
+      // finish this chunk's scaling before moving on: without this the FMA
+      // chain is deferred to the end and every group's partials stay live
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) asm volatile("" : "+v"(acc[f][m]));
+      if (c + 2 < NC) {
+#pragma unroll
+        for (int j = 0; j < GW; ++j) {
+          load<false>(b[c & 1][j], (c + 2) * GW + j);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int f = 0; f < FN; ++f) store(acc, f);
+  }
+
+  // red: LDS [NW][FN][NM][64] of f32x4 partial sums.
+  __device__ void run_split(f32x4_t* red) const {
+    f32x4_t acc[FN][NM];
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) acc[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int c = wave; c * GW < G; c += NW) {        // chunks of GW groups, one per wave at a time
+      Buf buf[GW];
+#pragma unroll
+      for (int j = 0; j < GW; ++j) load<true>(buf[j], c * GW + j);
+      // keep every load of the chunk ahead of the first MFMA (the scheduler
+      // would otherwise sink loads next to their uses and expose the latency
+      // once per group)
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < GW; ++j) group(buf[j], acc);
+    }
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) red[((wave * FN + f) * NM + m) * 64 + lane] = acc[f][m];
+    __syncthreads();
+    // epilogue: wave w finishes fragments f = w, w + NW, ...
+    for (int f = wave; f < FN; f += NW) {
+      f32x4_t v[FN][NM];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        v[f][m] = red[((0 * FN + f) * NM + m) * 64 + lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v[f][m] += red[((w * FN + f) * NM + m) * 64 + lane];
+      }
+      store(v, f);
+    }
+  }
+};
+
+// Row-tile kernel for short expert segments (decode blocks, batched blocks):
+// the weights stream once per tile of up to BMR rows, so this path is bound by
+// HBM.  The workgroup first copies its tile's activation rows into LDS
+// (permuted for the INT4 code order; the 16-byte chunk index XOR-ed with the
+// row so the 16 rows of an MFMA operand hit different banks), and every wave
+// loads the FP16 scales of its columns once.  Afterwards the only vector-memory
+// instructions are the weight loads (16 bytes per lane), DEPTH groups ahead.
+// Rows past the tile's last (and, for BMR = 8, MFMA rows 8..15) read arbitrary
+// LDS bytes; they only reach accumulator rows that are never stored.
+template <int WB, bool A8, bool DUAL, int FN, int NG, int DEPTH, int BMR>
+struct Dec16 {
+  static constexpr int NM = DUAL ? 2 : 1;
+  static constexpr int NB = (WB == 4) ? 1 : 2;
+  static constexpr int ELEM = A8 ? 1 : 2;
+  static constexpr int ROWB = NG * kGroup * ELEM;           // LDS bytes of one staged row
+  static constexpr int CPR = ROWB / 16;                     // 16-byte chunks per row
+  static constexpr int STEPS = A8 ? 2 : 4;                  // MFMA steps per 128-group
+  static constexpr int W_GROUP_BYTES = kGroup * WB / 8;
+  static constexpr int NSC = (NG * 2 + 15) / 16;            // 16-byte scale chunks per column
+  static constexpr int BN = 4 * 16 * FN;                    // columns per workgroup
+  static_assert(CPR % 8 == 0, "row swizzle needs 8-chunk rows");
+
+  static constexpr size_t lds_bytes() { return (size_t)BMR * ROWB + (A8 ? (size_t)NG * 16 * 4 : 0); }
+
+  struct WBuf {
+    u32x4_t b[FN][NM][NB];
+  };
+
+  __device__ static uint32_t lds_chunk(int row, int chunk) { return (uint32_t)(row * ROWB + ((chunk ^ (row & 7)) << 4)); }
+
+  __device__ static void run(const GemmProblem& p, const Tile& td, uint8_t* lds) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, kb = lane >> 4;
+    const int e = td.e, row0 = td.row0, nrows = td.nrows;
+    // 1. stage the tile's activation rows (and INT8 scales) into LDS
+    const uint8_t* a = static_cast<const uint8_t*>(p.a);
+    for (int idx = tid; idx < nrows * CPR; idx += blockDim.x) {
+      const int r = idx / CPR, c = idx % CPR;
+      const int64_t src = p.gather_k ? (int64_t)(p.sorted_slot[row0 + r] / p.gather_k) : (int64_t)(row0 + r);
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a + src * ROWB + c * 16);
+      *reinterpret_cast<u32x4_t*>(lds + lds_chunk(r, c)) = a_operand<WB, A8>(v);
+    }
+    float* xs_lds = reinterpret_cast<float*>(lds + (size_t)BMR * ROWB);   // [NG][16]
+    if constexpr (A8) {
+      for (int idx = tid; idx < nrows * NG; idx += blockDim.x) {
+        const int r = idx / NG, g = idx % NG;
+        const int64_t src = p.gather_k ? (int64_t)(p.sorted_slot[row0 + r] / p.gather_k) : (int64_t)(row0 + r);
+        xs_lds[g * 16 + r] = p.a_scale[src * NG + g];
+      }
+    }
+    __syncthreads();
+    const int col0 = (blockIdx.x * 4 + wave) * 16 * FN;
+    if (col0 >= p.n) return;                                 // wave-uniform, after the barrier
+
+    // 2. per-wave descriptors, weight offsets and all scales of its columns
+    const int64_t mat_bytes = (int64_t)p.n * NG * W_GROUP_BYTES;
+    const int64_t smat_bytes = (int64_t)p.n * NG * 2;
+    rsrc_t rw[NM], rs[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      rw[m] = make_rsrc((m == 0 ? p.w0q : p.w1q) + e * mat_bytes, mat_bytes);
+      rs[m] = make_rsrc((m == 0 ? p.w0s : p.w1s) + e * (int64_t)p.n * NG, smat_bytes);
+    }
+    uint32_t w_off[FN];
+    u32x4_t sc[FN][NM][NSC];
+#pragma unroll
+    for (int f = 0; f < FN; ++f) {
+      const int n = col0 + f * 16 + li;
+      w_off[f] = (uint32_t)(n * NG * W_GROUP_BYTES + kb * (WB == 4 ? 16 : 32));
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int q = 0; q < NSC; ++q) sc[f][m][q] = bload16(rs[m], (uint32_t)(n * NG * 2 + 16 * q));
+    }
+    const int arow = (BMR == 16) ? li : (li & (BMR - 1));   // LDS row feeding MFMA row li
+
+    // 3. the weight stream
+    const uint32_t mask_nib = vconst<0x000f000fu>(), magic = vconst<0x43004300u>();
+    f32x4_t acc[FN][NM];
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) acc[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    WBuf buf[DEPTH];
+    auto load_group = [&](WBuf& bf, int g) {
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            bf.b[f][m][j] = bload16(rw[m], w_off[f] + (uint32_t)(g * W_GROUP_BYTES + 16 * j));
+    };
+#pragma unroll
+    for (int j = 0; j < DEPTH && j < NG; ++j) {
+      load_group(buf[j], j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const WBuf& bf = buf[g % DEPTH];
+      if constexpr (!A8) {
+        f32x4_t accg[FN][NM];
+        f32x4_t accx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+          for (int m = 0; m < NM; ++m) accg[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const u32x4_t ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) {
+          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(lds + lds_chunk(arow, g * 16 + kb * 4 + t));
+          const bf16x8_t a8 = __builtin_bit_cast(bf16x8_t, av);
+          accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, __builtin_bit_cast(bf16x8_t, ones), accx, 0, 0, 0);
+#pragma unroll
+          for (int f = 0; f < FN; ++f)
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+              const u32x4_t bv = b_operand_bf16<WB>(bf.b[f][m], t, mask_nib, magic);
+              accg[f][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, __builtin_bit_cast(bf16x8_t, bv),
+                                                                   accg[f][m], 0, 0, 0);
+            }
+        }
+        constexpr float kOff = (WB == 4) ? 136.0f : 128.0f;
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            const uint32_t word = sc[f][m][g >> 3][(g >> 1) & 3];
+            const float s16 = half_bits_to_f32((g & 1) ? (word >> 16) : (word & 0xffffu));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[f][m][r] = __builtin_fmaf(s16, accg[f][m][r] - kOff * accx[r], acc[f][m][r]);
+          }
+      } else {
+        i32x4_t accg[FN][NM];
+        i32x4_t accx = {0, 0, 0, 0};
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+          for (int m = 0; m < NM; ++m) accg[f][m] = i32x4_t{0, 0, 0, 0};
+        const i32x4_t ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) {
+          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(lds + lds_chunk(arow, g * 8 + kb * 2 + t));
+          const i32x4_t ai = __builtin_bit_cast(i32x4_t, av);
+          if constexpr (WB == 4) accx = __builtin_amdgcn_mfma_i32_16x16x64_i8(ai, ones, accx, 0, 0, 0);
+#pragma unroll
+          for (int f = 0; f < FN; ++f)
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+              const u32x4_t bv = b_operand_i8<WB>(bf.b[f][m], t);
+              accg[f][m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ai, __builtin_bit_cast(i32x4_t, bv), accg[f][m],
+                                                                 0, 0, 0);
+            }
+        }
+        const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(xs_lds + g * 16 + 4 * kb);
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            const uint32_t word = sc[f][m][g >> 3][(g >> 1) & 3];
+            const float ws = half_bits_to_f32((g & 1) ? (word >> 16) : (word & 0xffffu));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int isum = (WB == 4) ? accg[f][m][r] - 8 * accx[r] : accg[f][m][r];
+              acc[f][m][r] = __builtin_fmaf((float)isum, xs[r] * ws, acc[f][m][r]);
+            }
+          }
+      }
+      // finish this group's scaling now (otherwise the FMA chain is deferred
+      // to the end and every group's partial sums stay live)
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) asm volatile("" : "+v"(acc[f][m]));
+      if (g + DEPTH < NG) load_group(buf[g % DEPTH], g + DEPTH);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // 4. epilogue: lane holds rows 4kb+r of column li of each fragment
     uint16_t* out = static_cast<uint16_t*>(p.out);
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
-      const int64_t col = n_wave + f * 16 + li;
+      const int64_t col = col0 + f * 16 + li;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 4 * kb + r;
         if (m < nrows) {
-          float v;
-          if constexpr (DUAL) v = silu(acc[f][0][r]) * acc[f][1][r];
-          else v = acc[f][0][r];
-          out[(int64_t)(row0 + m) * p.n + col] = (uint16_t)f32_to_bf16_bits(v);
+          float o;
+          if constexpr (DUAL) o = silu(acc[f][0][r]) * acc[f][1][r];
+          else o = acc[f][0][r];
+          out[(int64_t)(row0 + m) * p.n + col] = (uint16_t)f32_to_bf16_bits(o);
         }
       }
     }
   }
 };
 
-template <int WB, bool A8, bool DUAL, int FN, int PD>
-__global__ __launch_bounds__(256) void k_gemm16(GemmProblem p) {
-  if ((int)blockIdx.y >= *p.ntiles) return;                 // tile past the routed rows
+template <int WB, bool A8, bool DUAL, int FN, int NG, int DEPTH, int BMR>
+__global__ __launch_bounds__(256) void k_gemm_dec(GemmProblem p) {
+  using K = Dec16<WB, A8, DUAL, FN, NG, DEPTH, BMR>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t dec_lds[];
+  if ((int)blockIdx.y >= *p.ntiles) return;
   const Tile td = p.tiles[blockIdx.y];
-  const int wave = threadIdx.x >> 6;
-  if ((blockIdx.x * 4 + wave) * 16 * FN >= p.n) return;     // wave-uniform
-  Gemm16<WB, A8, DUAL, FN, PD> g(p, td, wave);
-  g.run();
+  K::run(p, td, dec_lds);
 }
 
-template <int WB, bool A8, bool DUAL>
-hipError_t launch_variant(const GemmProblem& p, hipStream_t stream) {
-  constexpr int FN = 1, PD = 3;
+template <int WB, bool A8, bool DUAL, int FN, int NG, int DEPTH, int BMR>
+hipError_t launch_dec(const GemmProblem& p, hipStream_t stream) {
+  using K = Dec16<WB, A8, DUAL, FN, NG, DEPTH, BMR>;
+  const dim3 grid((p.n + K::BN - 1) / K::BN, (unsigned)p.max_tiles);
+  hipLaunchKernelGGL((k_gemm_dec<WB, A8, DUAL, FN, NG, DEPTH, BMR>), grid, dim3(256), K::lds_bytes(), stream, p);
+  return hipGetLastError();
+}
+
+// Split-reduction kernel (any reduction length): workgroup = one 16 x 16*FN
+// tile, four waves over the groups, LDS reduction.
+template <int WB, bool A8, bool DUAL, int FN, int GW>
+__global__ __launch_bounds__(256) void k_gemm16(GemmProblem p) {
+  using K = Gemm16<WB, A8, DUAL, FN, GW>;
+  __shared__ f32x4_t red[K::NW * FN * K::NM * 64];
+  if ((int)blockIdx.y >= *p.ntiles) return;                 // tile past the routed rows
+  const Tile td = p.tiles[blockIdx.y];
+  K g(p, td, blockIdx.x * K::BN);
+  g.run_split(red);
+}
+
+// Streaming kernel (reduction of NG groups known at compile time): every wave
+// owns its own 16 x 16*FN tile over the whole reduction; a workgroup is four
+// neighbouring column tiles of one row tile.
+template <int WB, bool A8, bool DUAL, int FN, int GW, int NG>
+__global__ __launch_bounds__(256) void k_gemm16_stream(GemmProblem p) {
+  using K = Gemm16<WB, A8, DUAL, FN, GW>;
+  if ((int)blockIdx.y >= *p.ntiles) return;
+  const int col0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * K::BN;
+  if (col0 >= p.n) return;                                  // wave-uniform
+  const Tile td = p.tiles[blockIdx.y];
+  K g(p, td, col0);
+  g.template run_stream<NG>();
+}
+
+template <int WB, bool A8, bool DUAL, int FN, int GW>
+hipError_t launch_split(const GemmProblem& p, hipStream_t stream) {
+  constexpr int BN = 16 * FN;
+  const dim3 grid((p.n + BN - 1) / BN, (unsigned)p.max_tiles);
+  hipLaunchKernelGGL((k_gemm16<WB, A8, DUAL, FN, GW>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int WB, bool A8, bool DUAL, int FN, int GW, int NG>
+hipError_t launch_stream(const GemmProblem& p, hipStream_t stream) {
   constexpr int BN = 4 * 16 * FN;
   const dim3 grid((p.n + BN - 1) / BN, (unsigned)p.max_tiles);
-  hipLaunchKernelGGL((k_gemm16<WB, A8, DUAL, FN, PD>), grid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((k_gemm16_stream<WB, A8, DUAL, FN, GW, NG>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+// Kernel choice by reduction length (G = kdim / 128): the usual expert shapes
+// get the streaming kernel, anything else the split-reduction kernel.  The
+// fused gate/up GEMM streams two matrices, so one 16-column fragment per wave;
+// the down GEMM streams one, so two.
+// Largest activation tile (rows x kdim x element bytes) the decode kernel stages in LDS.
+constexpr int64_t kDecLdsMax = 64 * 1024;
+
+template <int WB, bool A8, bool DUAL, int NG, int BMR>
+hipError_t launch_dec_ng(const GemmProblem& p, hipStream_t stream) {
+  // the fused gate/up GEMM streams two matrices per column, so one 16-column
+  // fragment per wave; the down GEMM streams one, so two.  DEPTH groups of
+  // weight loads in flight (64 VGPRs of INT4 / 128 of INT8 per wave).
+  constexpr int FN = DUAL ? 1 : 2;
+  constexpr int DEPTH = (NG < 8) ? NG : 8;
+  return launch_dec<WB, A8, DUAL, FN, NG, DEPTH, BMR>(p, stream);
+}
+
+template <int WB, bool A8, bool DUAL, int BMR>
+hipError_t launch_dec_shape(const GemmProblem& p, hipStream_t stream, bool* done) {
+  *done = true;
+  switch (p.kdim / kGroup) {
+    case 4: return launch_dec_ng<WB, A8, DUAL, 4, BMR>(p, stream);
+    case 8: return launch_dec_ng<WB, A8, DUAL, 8, BMR>(p, stream);
+    case 12: return launch_dec_ng<WB, A8, DUAL, 12, BMR>(p, stream);
+    case 16: return launch_dec_ng<WB, A8, DUAL, 16, BMR>(p, stream);
+    case 32: return launch_dec_ng<WB, A8, DUAL, 32, BMR>(p, stream);
+    default: *done = false; return hipSuccess;
+  }
+}
+
+// Kernel choice: the LDS-staged decode kernel when the reduction length is one
+// of the usual expert shapes and the activation tile fits in LDS; otherwise the
+// split-reduction kernel (any reduction length).
+template <int WB, bool A8, bool DUAL>
+hipError_t launch_shape(const GemmProblem& p, hipStream_t stream) {
+  // LDS of the decode kernel: staged rows (8 or 16) x kdim x element bytes,
+  // plus the FP32 activation scales of 16 rows in INT8 mode
+  const int64_t rows = (p.bm <= 8) ? 8 : 16;
+  const int64_t tile_bytes = rows * p.kdim * (A8 ? 1 : 2) + (A8 ? (int64_t)(p.kdim / kGroup) * 16 * 4 : 0);
+  if (tile_bytes <= kDecLdsMax) {
+    bool done = false;
+    hipError_t e = (p.bm <= 8) ? launch_dec_shape<WB, A8, DUAL, 8>(p, stream, &done)
+                               : launch_dec_shape<WB, A8, DUAL, 16>(p, stream, &done);
+    if (done) return e;
+  }
+  if constexpr (DUAL) return launch_split<WB, A8, DUAL, 1, 1>(p, stream);
+  else return launch_split<WB, A8, DUAL, 4, 1>(p, stream);
 }
 
 }  // namespace
 
-int gemm_tile_rows(int64_t, int, int, int) { return 16; }
+// Row-tile height: 8 when experts see only a few rows each (decode blocks: the
+// weights stream once per tile either way, and a smaller activation tile leaves
+// LDS for more workgroups), 16 otherwise.
+int gemm_tile_rows(int64_t S, int E, int, int) { return (S <= 4 * (int64_t)E) ? 8 : 16; }
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream) {
   if (p.max_tiles == 0 || p.n == 0) return hipSuccess;
   const bool dual = p.w1q != nullptr;
   if (p.bits == 4) {
-    if (p.act_int8) return dual ? launch_variant<4, true, true>(p, stream) : launch_variant<4, true, false>(p, stream);
-    return dual ? launch_variant<4, false, true>(p, stream) : launch_variant<4, false, false>(p, stream);
+    if (p.act_int8) return dual ? launch_shape<4, true, true>(p, stream) : launch_shape<4, true, false>(p, stream);
+    return dual ? launch_shape<4, false, true>(p, stream) : launch_shape<4, false, false>(p, stream);
   }
-  if (p.act_int8) return dual ? launch_variant<8, true, true>(p, stream) : launch_variant<8, true, false>(p, stream);
-  return dual ? launch_variant<8, false, true>(p, stream) : launch_variant<8, false, false>(p, stream);
+  if (p.act_int8) return dual ? launch_shape<8, true, true>(p, stream) : launch_shape<8, true, false>(p, stream);
+  return dual ? launch_shape<8, false, true>(p, stream) : launch_shape<8, false, false>(p, stream);
 }
 
 }  // namespace qre

@@ -119,6 +119,9 @@ int check_desc(const qre_desc* d) {
   if (d->E > QRE_MAX_EXPERTS) return QRE_ERR_LIMIT;
   const int64_t S = (int64_t)d->T * d->K;
   if (S >= (1ll << 31)) return QRE_ERR_LIMIT;
+  // the GEMMs address x, h and one expert's weights with 32-bit buffer offsets
+  if ((int64_t)d->T * d->H * 2 >= (1ll << 31) || S * d->I * 2 >= (1ll << 31)) return QRE_ERR_LIMIT;
+  if ((int64_t)d->H * d->I * 2 >= (1ll << 31)) return QRE_ERR_LIMIT;
   if (max_tiles(S, d->E, 1) >= (1ll << 31)) return QRE_ERR_LIMIT;
   // grid limit of the GEMM launch (row tiles along grid.y)
   if (max_tiles(S, d->E, gemm_tile_rows(S, d->E, 2 * d->I, d->H)) > 65535) return QRE_ERR_LIMIT;
@@ -146,6 +149,7 @@ GemmProblem gate_up_problem(const qre_desc& d, const void* x, const int8_t* xq, 
   p.sorted_slot = sorted_slot;
   p.a = d.act_int8 ? static_cast<const void*>(xq) : x;
   p.a_scale = xs;
+  p.a_rows = d.T;
   p.w0q = static_cast<const uint8_t*>(w.gate_q);
   p.w0s = static_cast<const uint16_t*>(w.gate_s);
   p.w1q = static_cast<const uint8_t*>(w.up_q);
@@ -169,6 +173,7 @@ GemmProblem down_problem(const qre_desc& d, const void* h, const int8_t* hq, con
   p.sorted_slot = nullptr;
   p.a = d.act_int8 ? static_cast<const void*>(hq) : h;
   p.a_scale = hs;
+  p.a_rows = (int64_t)d.T * d.K;
   p.w0q = static_cast<const uint8_t*>(w.down_q);
   p.w0s = static_cast<const uint16_t*>(w.down_s);
   p.w1q = nullptr;

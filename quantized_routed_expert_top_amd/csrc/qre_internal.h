@@ -69,8 +69,9 @@ struct GemmProblem {
   int bits;               // 4 or 8
   int gather_k;           // >0: A row of sorted row r is token sorted_slot[r] / gather_k; 0: A row = r
   const int32_t* sorted_slot;
-  const void* a;          // bf16 [rows][kdim] or int8 [rows][kdim]
-  const float* a_scale;   // int8 mode: fp32 [rows][kdim/128]
+  const void* a;          // bf16 [a_rows][kdim] or int8 [a_rows][kdim]
+  const float* a_scale;   // int8 mode: fp32 [a_rows][kdim/128]
+  int64_t a_rows;         // rows of the A source (T for gathered x, S for h)
   const uint8_t* w0q; const uint16_t* w0s;   // [E][n][kdim*bits/8], [E][n][kdim/128]
   const uint8_t* w1q; const uint16_t* w1s;   // second matrix (gate/up: up), or null
   const Tile* tiles; const int32_t* ntiles; int64_t max_tiles; int bm;
