@@ -62,6 +62,37 @@ def read_traffic(workload: str):
         return None
 
 
+class HipEvents:
+    """hipEvent_t handles through ctypes (recorded by the library on its stream)."""
+
+    def __init__(self):
+        import ctypes as C
+        self.C = C
+        self.lib = C.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [C.c_void_p]
+        self.events = []
+
+    def create(self):
+        h = self.C.c_void_p()
+        if self.lib.hipEventCreate(self.C.byref(h)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self.events.append(h.value)
+        return h.value
+
+    def elapsed_ms(self, a, b):
+        ms = self.C.c_float()
+        if self.lib.hipEventElapsedTime(self.C.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy_all(self):
+        for h in self.events:
+            self.lib.hipEventDestroy(h)
+        self.events = []
+
+
 def cpu_baseline(wl, x_bits, ids, w, budget_s=12.0):
     """The oracle as it stands, on this host's cores, over whole blocks of the
     same workload (repeated until ~budget_s of CPU time, at least once)."""
@@ -167,37 +198,18 @@ def main():
         if not torch.equal(out, eager_out):
             raise RuntimeError("timed steps changed the output")
 
-        # ---- per-kernel durations: stage entry points with events around each launch ----
-        sw = qre.stage_workspace(wl.T, wl.H, wl.I, wl.E, wl.K, wl.weight_bits, wl.act_int8, dev)
-        S = wl.T * wl.K
-        h = torch.empty((S, wl.I), dtype=torch.bfloat16, device=dev)
-        y = torch.empty((S, wl.H), dtype=torch.bfloat16, device=dev)
+        # ---- per-kernel durations: the same kernels, with HIP events between steps ----
+        hip = HipEvents()
         nk = max(20, min(args.steps, 200))
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(nk)]
+        evs = [[hip.create() for _ in range(6)] for _ in range(nk)]
         for i in range(nk):
-            Wi = copies[i % R]
-            e = evs[i]
-            e[0].record(stream)
-            _, _, sorted_slot, slot_row, _ = qre.route(ids_t, wl.E, wl.H, wl.I, wl.weight_bits, wl.act_int8,
-                                                       workspace=sw)
-            if wl.act_int8:
-                xq, xs = qre.quantize_act(x)
-            e[1].record(stream)
-            qre.gate_up(x, sorted_slot, Wi, wl.K, sw, act_int8=wl.act_int8,
-                        xq=xq if wl.act_int8 else None, xs=xs if wl.act_int8 else None, h=h)
-            e[2].record(stream)
-            if wl.act_int8:
-                hq, hs = qre.quantize_act(h)
-            e[3].record(stream)
-            qre.down(h, Wi, wl.T, wl.K, sw, act_int8=wl.act_int8, hq=hq if wl.act_int8 else None,
-                     hs=hs if wl.act_int8 else None, y=y)
-            e[4].record(stream)
-            res = qre.combine(y, slot_row, w_t)
-            e[5].record(stream)
+            qre.moe_forward_timed(x, ids_t, w_t, copies[i % R], evs[i], act_int8=wl.act_int8, out=out,
+                                  workspace=ws)
         torch.cuda.synchronize()
-        if not torch.equal(res, eager_out):
-            raise RuntimeError("stage entry points disagree with qre_moe_forward")
-    dur = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(5)] for e in evs[2:]]).mean(axis=0) * 1e3  # us
+        if not torch.equal(out, eager_out):
+            raise RuntimeError("timed forward differs from qre_moe_forward")
+    dur = np.array([[hip.elapsed_ms(e[j], e[j + 1]) for j in range(5)] for e in evs[2:]]).mean(axis=0) * 1e3  # us
+    hip.destroy_all()
 
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = wl.T * args.steps / wall
@@ -206,7 +218,7 @@ def main():
     achieved = gu_bytes / (gu_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(wl.name),
-                "kernel": "k_gemm16 gate/up (fused SiLU*mul)", "avg_us": round(gu_us, 2),
+                "kernel": "fused gate/up + SiLU*mul GEMM", "avg_us": round(gu_us, 2),
                 "alg_bytes_per_launch": int(gu_bytes)}
     step_bytes = alg["total"]
     result = {
@@ -231,7 +243,7 @@ def main():
                  "hbm_frac_whole_step": round(step_bytes / (wall / args.steps) / 1e9 / HBM_PEAK_GBS, 4),
                  "mfma_frac_whole_step": round(alg["flops"] / (wall / args.steps) / 1e12 /
                                                (I8_PEAK_TOPS if wl.act_int8 else BF16_PEAK_TFLOPS), 5)},
-        "kernels_us": {"route": round(float(dur[0]), 2), "gate_up": round(gu_us, 2),
+        "kernels_us": {"route_and_quantize_x": round(float(dur[0]), 2), "gate_up": round(gu_us, 2),
                        "quantize_h": round(float(dur[2]), 2), "down": round(dn_us, 2),
                        "combine": round(float(dur[4]), 2)},
     }

@@ -104,17 +104,36 @@ int qre_workspace_bytes(const qre_desc* desc, size_t* bytes);
 
 /* The whole routed-expert feed-forward: x, topk_ids, topk_w, weights -> out.
  * Runs the permutation, the INT8 activation quantizer (act_int8 only), the
- * fused gate/up/SiLU grouped GEMM, the down grouped GEMM and the combine.
+ * fused gate/up/SiLU grouped GEMM, the down grouped GEMM and the combine.  For
+ * up to 2048 slots with the usual expert shapes the permutation is computed
+ * inside the gate/up kernel (each expert's workgroups find that expert's slots)
+ * instead of by a separate launch; the results are the same.
  * `workspace` (>= qre_workspace_bytes) holds the permutation, h and y; after
  * the call it also holds what qre_read_dropped_slots reads. */
 int qre_moe_forward(const qre_desc* desc, const void* x, const int32_t* topk_ids,
                     const float* topk_w, const qre_weights* weights, void* out,
                     void* workspace, size_t workspace_bytes, qre_stream_t stream);
 
+/* qre_moe_forward that also records events[i] (each a hipEvent_t created by the
+ * caller, or NULL to skip it) on `stream` between its steps: [0] before the
+ * permutation, [1] before the gate/up GEMM, [2] after it, [3] before the down
+ * GEMM, [4] after it, [5] after the combine.  The kernels are the same as
+ * qre_moe_forward's; this is a measurement aid (six event records per call). */
+int qre_moe_forward_timed(const qre_desc* desc, const void* x, const int32_t* topk_ids,
+                          const float* topk_w, const qre_weights* weights, void* out,
+                          void* workspace, size_t workspace_bytes, void* const* events,
+                          qre_stream_t stream);
+
 /* Number of slots whose expert id was outside [0, E) in the last
  * qre_moe_forward that used `workspace` (host out).  Synchronizes `stream`. */
 int qre_read_dropped_slots(const qre_desc* desc, const void* workspace, int32_t* n_dropped,
                            qre_stream_t stream);
+
+/* Device addresses, inside a qre_moe_forward workspace, of the permutation the
+ * last call computed (layouts of qre_route; host out).  Reading them after
+ * the call has finished gives the same arrays qre_route would produce. */
+int qre_workspace_permutation(const qre_desc* desc, void* workspace, int32_t** counts,
+                              int32_t** offsets, int32_t** sorted_slot, int32_t** slot_row);
 
 /* ---- Stage entry points (same conventions).  They compute exactly what the
  * corresponding step of qre_moe_forward computes, with the same kernels. ---- */

@@ -60,7 +60,9 @@ def _lib():
         L.qre_workspace_bytes.argtypes = [P, P]
         L.qre_stage_workspace_bytes.argtypes = [P, P]
         L.qre_moe_forward.argtypes = [P, P, P, P, P, P, P, sz, P]
+        L.qre_moe_forward_timed.argtypes = [P, P, P, P, P, P, P, sz, P, P]
         L.qre_read_dropped_slots.argtypes = [P, P, P, P]
+        L.qre_workspace_permutation.argtypes = [P, P, P, P, P, P]
         L.qre_route.argtypes = [P, P, P, P, P, P, P, sz, P]
         L.qre_build_tiles.argtypes = [P, P, P, sz, P]
         L.qre_quantize_act.argtypes = [P, i32, i32, P, P, P]
@@ -212,6 +214,44 @@ def moe_forward(x, topk_ids, topk_w, W: QuantizedExperts, act_int8=False, out=No
         C.byref(d), _ptr(x), _ptr(topk_ids), _ptr(topk_w), C.byref(ws_struct), _ptr(out), _ptr(workspace),
         workspace.numel(), _stream()))
     return out
+
+
+def moe_forward_timed(x, topk_ids, topk_w, W: QuantizedExperts, events, act_int8=False, out=None, workspace=None):
+    """moe_forward that records six caller-created hipEvent_t handles (ints, or
+    None) between its steps; see qre_moe_forward_timed."""
+    T, H = x.shape
+    K = topk_ids.shape[1]
+    _need(x, "x", torch.bfloat16, (T, H))
+    _need(topk_ids, "topk_ids", torch.int32, (T, K))
+    _need(topk_w, "topk_w", torch.float32, (T, K))
+    if len(events) != 6:
+        raise ValueError("six events")
+    d = _desc(T, H, W.I, W.E, K, W.bits, act_int8)
+    if workspace is None:
+        workspace = _workspace(workspace_bytes(T, H, W.I, W.E, K, W.bits, act_int8), x.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    ev = (C.c_void_p * 6)(*[e if e else None for e in events])
+    ws_struct = W._struct()
+    _check("qre_moe_forward_timed", _lib().qre_moe_forward_timed(
+        C.byref(d), _ptr(x), _ptr(topk_ids), _ptr(topk_w), C.byref(ws_struct), _ptr(out), _ptr(workspace),
+        workspace.numel(), ev, _stream()))
+    return out
+
+
+def workspace_permutation(T, H, I, E, K, bits, act_int8, workspace):
+    """(counts[E], offsets[E+1], sorted_slot[S], slot_row[S]) int32 views into a
+    moe_forward workspace (valid once that call has finished)."""
+    P = [C.c_void_p() for _ in range(4)]
+    _check("qre_workspace_permutation", _lib().qre_workspace_permutation(
+        C.byref(_desc(T, H, I, E, K, bits, act_int8)), _ptr(workspace), *[C.byref(p) for p in P]))
+    base = workspace.data_ptr()
+    S = T * K
+    views = []
+    for ptr, n in zip(P, (E, E + 1, S, S)):
+        off = ptr.value - base
+        views.append(workspace[off:off + 4 * n].view(torch.int32))
+    return tuple(views)
 
 
 def read_dropped_slots(T, H, I, E, K, bits, act_int8, workspace) -> int:

@@ -431,7 +431,7 @@ struct Dec16 {
   static constexpr int CPR = ROWB / 16;                     // 16-byte chunks per row
   static constexpr int STEPS = A8 ? 2 : 4;                  // MFMA steps per 128-group
   static constexpr int W_GROUP_BYTES = kGroup * WB / 8;
-  static constexpr int NSC = (NG * 2 + 15) / 16;            // 16-byte scale chunks per column
+  static constexpr int NSW = (NG + 1) / 2;                  // 32-bit words of one column's FP16 scales
   static constexpr int BN = 4 * 16 * FN;                    // columns per workgroup
   static_assert(CPR % 8 == 0, "row swizzle needs 8-chunk rows");
 
@@ -443,30 +443,15 @@ struct Dec16 {
 
   __device__ static uint32_t lds_chunk(int row, int chunk) { return (uint32_t)(row * ROWB + ((chunk ^ (row & 7)) << 4)); }
 
-  __device__ static void run(const GemmProblem& p, const Tile& td, uint8_t* lds) {
+  // Tile: rows [row0, row0 + nrows) (sorted order) of expert e; src(r) gives
+  // the A-source row of local row r (a token for gate/up, a sorted row for down).
+  template <class RowSrc>
+  __device__ static void run(const GemmProblem& p, int e, int row0, int nrows, RowSrc src_row, uint8_t* lds) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, kb = lane >> 4;
-    const int e = td.e, row0 = td.row0, nrows = td.nrows;
-    // 1. stage the tile's activation rows (and INT8 scales) into LDS
-    const uint8_t* a = static_cast<const uint8_t*>(p.a);
-    for (int idx = tid; idx < nrows * CPR; idx += blockDim.x) {
-      const int r = idx / CPR, c = idx % CPR;
-      const int64_t src = p.gather_k ? (int64_t)(p.sorted_slot[row0 + r] / p.gather_k) : (int64_t)(row0 + r);
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a + src * ROWB + c * 16);
-      *reinterpret_cast<u32x4_t*>(lds + lds_chunk(r, c)) = a_operand<WB, A8>(v);
-    }
-    float* xs_lds = reinterpret_cast<float*>(lds + (size_t)BMR * ROWB);   // [NG][16]
-    if constexpr (A8) {
-      for (int idx = tid; idx < nrows * NG; idx += blockDim.x) {
-        const int r = idx / NG, g = idx % NG;
-        const int64_t src = p.gather_k ? (int64_t)(p.sorted_slot[row0 + r] / p.gather_k) : (int64_t)(row0 + r);
-        xs_lds[g * 16 + r] = p.a_scale[src * NG + g];
-      }
-    }
-    __syncthreads();
-    const int col0 = (blockIdx.x * 4 + wave) * 16 * FN;
-    if (col0 >= p.n) return;                                 // wave-uniform, after the barrier
-
-    // 2. per-wave descriptors, weight offsets and all scales of its columns
+    // 1. per-wave descriptors, weight offsets, all scales of its columns and
+    //    the first DEPTH groups of weights: issued before the activation rows
+    //    are staged, so the weight stream starts at once
+    const int col0 = min((blockIdx.x * 4 + wave) * 16 * FN, p.n - 16 * FN);   // a surplus wave re-reads the last tile and stores nothing
     const int64_t mat_bytes = (int64_t)p.n * NG * W_GROUP_BYTES;
     const int64_t smat_bytes = (int64_t)p.n * NG * 2;
     rsrc_t rw[NM], rs[NM];
@@ -476,19 +461,45 @@ struct Dec16 {
       rs[m] = make_rsrc((m == 0 ? p.w0s : p.w1s) + e * (int64_t)p.n * NG, smat_bytes);
     }
     uint32_t w_off[FN];
-    u32x4_t sc[FN][NM][NSC];
+    uint32_t sc[FN][NM][NSW];   // FP16 scales of the lane's column, two per word
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
       const int n = col0 + f * 16 + li;
       w_off[f] = (uint32_t)(n * NG * W_GROUP_BYTES + kb * (WB == 4 ? 16 : 32));
+      const uint32_t so = (uint32_t)(n * NG * 2);
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
+      for (int m = 0; m < NM; ++m) {
+        // loads never cross the end of the column's scale row (a buffer load
+        // that straddles the end of its descriptor returns zeros)
+        if constexpr (NG % 8 == 0) {
 #pragma unroll
-        for (int q = 0; q < NSC; ++q) sc[f][m][q] = bload16(rs[m], (uint32_t)(n * NG * 2 + 16 * q));
+          for (int q = 0; q < NG / 8; ++q) {
+            const u32x4_t v = bload16(rs[m], so + 16 * q);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sc[f][m][4 * q + j] = v[j];
+          }
+        } else if constexpr (NG % 2 == 0) {
+#pragma unroll
+          for (int q = 0; q < NSW; ++q)
+            sc[f][m][q] = __builtin_amdgcn_raw_buffer_load_b32(rs[m], so + 4 * q, 0, 0);
+        } else {
+#pragma unroll
+          for (int q = 0; q < NSW; ++q) {
+            const uint32_t lo = bload_u16(rs[m], so + 4 * q);
+            const uint32_t hi = (2 * q + 1 < NG) ? bload_u16(rs[m], so + 4 * q + 2) : 0u;
+            sc[f][m][q] = lo | (hi << 16);
+          }
+        }
+      }
     }
     const int arow = (BMR == 16) ? li : (li & (BMR - 1));   // LDS row feeding MFMA row li
+    // the swizzle only touches the low 3 bits of a chunk index and a group
+    // spans a multiple of 8 chunks, so every A read is a per-lane base plus a
+    // compile-time group offset (folded into the LDS instruction)
+    uint32_t a_base[STEPS];
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t) a_base[t] = lds_chunk(arow, (A8 ? kb * 2 : kb * 4) + t);
 
-    // 3. the weight stream
     const uint32_t mask_nib = vconst<0x000f000fu>(), magic = vconst<0x43004300u>();
     f32x4_t acc[FN][NM];
 #pragma unroll
@@ -510,6 +521,27 @@ struct Dec16 {
       load_group(buf[j], j);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // 2. stage the tile's activation rows (and INT8 scales) into LDS
+    const uint8_t* a = static_cast<const uint8_t*>(p.a);
+    for (int idx = tid; idx < nrows * CPR; idx += blockDim.x) {
+      const int r = idx / CPR, c = idx % CPR;
+      const int64_t src = src_row(r);
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a + src * ROWB + c * 16);
+      *reinterpret_cast<u32x4_t*>(lds + lds_chunk(r, c)) = a_operand<WB, A8>(v);
+    }
+    float* xs_lds = reinterpret_cast<float*>(lds + (size_t)BMR * ROWB);   // [NG][16]
+    if constexpr (A8) {
+      for (int idx = tid; idx < nrows * NG; idx += blockDim.x) {
+        const int r = idx / NG, g = idx % NG;
+        const int64_t src = src_row(r);
+        xs_lds[g * 16 + r] = p.a_scale[src * NG + g];
+      }
+    }
+    __syncthreads();
+    if ((blockIdx.x * 4 + wave) * 16 * FN >= p.n) return;   // wave-uniform, after the barrier
+
+    // 3. the weight stream
+
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const WBuf& bf = buf[g % DEPTH];
@@ -523,7 +555,7 @@ struct Dec16 {
         const u32x4_t ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0
 #pragma unroll
         for (int t = 0; t < STEPS; ++t) {
-          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(lds + lds_chunk(arow, g * 16 + kb * 4 + t));
+          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(lds + a_base[t] + g * 256);
           const bf16x8_t a8 = __builtin_bit_cast(bf16x8_t, av);
           accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, __builtin_bit_cast(bf16x8_t, ones), accx, 0, 0, 0);
 #pragma unroll
@@ -540,7 +572,7 @@ struct Dec16 {
         for (int f = 0; f < FN; ++f)
 #pragma unroll
           for (int m = 0; m < NM; ++m) {
-            const uint32_t word = sc[f][m][g >> 3][(g >> 1) & 3];
+            const uint32_t word = sc[f][m][g >> 1];
             const float s16 = half_bits_to_f32((g & 1) ? (word >> 16) : (word & 0xffffu));
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[f][m][r] = __builtin_fmaf(s16, accg[f][m][r] - kOff * accx[r], acc[f][m][r]);
@@ -555,7 +587,7 @@ struct Dec16 {
         const i32x4_t ones = {0x01010101, 0x01010101, 0x01010101, 0x01010101};
 #pragma unroll
         for (int t = 0; t < STEPS; ++t) {
-          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(lds + lds_chunk(arow, g * 8 + kb * 2 + t));
+          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(lds + a_base[t] + g * 128);
           const i32x4_t ai = __builtin_bit_cast(i32x4_t, av);
           if constexpr (WB == 4) accx = __builtin_amdgcn_mfma_i32_16x16x64_i8(ai, ones, accx, 0, 0, 0);
 #pragma unroll
@@ -572,7 +604,7 @@ struct Dec16 {
         for (int f = 0; f < FN; ++f)
 #pragma unroll
           for (int m = 0; m < NM; ++m) {
-            const uint32_t word = sc[f][m][g >> 3][(g >> 1) & 3];
+            const uint32_t word = sc[f][m][g >> 1];
             const float ws = half_bits_to_f32((g & 1) ? (word >> 16) : (word & 0xffffu));
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -615,7 +647,129 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmProblem p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t dec_lds[];
   if ((int)blockIdx.y >= *p.ntiles) return;
   const Tile td = p.tiles[blockIdx.y];
-  K::run(p, td, dec_lds);
+  const int row0 = td.row0;
+  if (p.gather_k) {
+    K::run(p, td.e, row0, td.nrows, [&](int r) { return (int64_t)(p.sorted_slot[row0 + r] / p.gather_k); }, dec_lds);
+  } else {
+    K::run(p, td.e, row0, td.nrows, [&](int r) { return (int64_t)(row0 + r); }, dec_lds);
+  }
+}
+
+// Decode blocks with the permutation folded in.  Workgroup (column block, e):
+// the gate/up kernel finds expert e's slots itself (per 64 slots, one ballot
+// for id == e and one for 0 <= id < e, so its rows are e's slots in ascending
+// order and its first sorted row is the number of valid slots with a smaller
+// id: the stable counting sort), writes expert e's part of counts, offsets,
+// sorted_slot and slot_row (column block 0 only), then runs the row tiles.
+// The down kernel reads counts/offsets back.  Used for small slot counts,
+// where every workgroup re-reading all ids is cheap.
+template <int WB, bool A8, int NG, int DEPTH, int BMR>
+__global__ __launch_bounds__(256) void k_gate_up_routed(GemmProblem p, RouteOut ra) {
+  using K = Dec16<WB, A8, true, 1, NG, DEPTH, BMR>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t dec_lds[];
+  __shared__ int wcnt[2][4];
+  __shared__ int rows[kRoutedMaxSlots];                     // e's slots, ascending
+  const int e = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool writer = blockIdx.x == 0;
+  const uint64_t below = (1ull << lane) - 1ull;
+  constexpr int kSub = kRoutedMaxSlots / 256;              // 64-slot sub-chunks per wave
+  const int L = ((ra.S + 255) / 256) * 64;                  // slots per wave, a multiple of 64
+  const int s0 = min(ra.S, wave * L), s1 = min(ra.S, s0 + L);
+  // one pass over the ids: the ballot mask of e's slots per sub-chunk stays in
+  // registers; count e's slots and the valid slots of smaller experts
+  // all loads first (out-of-range sub-chunks read nothing), then the ballots
+  const rsrc_t rid = make_rsrc(ra.ids, (int64_t)ra.S * 4);
+  int ids[kSub];
+#pragma unroll
+  for (int c = 0; c < kSub; ++c) {
+    const int s = s0 + c * 64 + lane;
+    ids[c] = (int)__builtin_amdgcn_raw_buffer_load_b32(rid, s < s1 ? (uint32_t)s * 4u : kOOB, 0, 0);
+  }
+  uint64_t eq[kSub];
+  int n_eq = 0, n_lt = 0;
+#pragma unroll
+  for (int c = 0; c < kSub; ++c) {
+    const int s = s0 + c * 64 + lane;
+    const int id = s < s1 ? ids[c] : -1;
+    eq[c] = __ballot(id == e);
+    n_eq += __popcll(eq[c]);
+    n_lt += __popcll(__ballot(id >= 0 && id < e));
+  }
+  if (writer && e == 0) {
+#pragma unroll
+    for (int c = 0; c < kSub; ++c) {
+      const int s = s0 + c * 64 + lane;
+      if (s < s1 && (ids[c] < 0 || ids[c] >= ra.E)) ra.slot_row[s] = -1;      // dropped slot
+    }
+  }
+  if (lane == 0) {
+    wcnt[0][wave] = n_eq;
+    wcnt[1][wave] = n_lt;
+  }
+  __syncthreads();
+  int count = 0, off = 0, wbase = 0;
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) wbase += wcnt[0][w];
+    count += wcnt[0][w];
+    off += wcnt[1][w];
+  }
+  // LDS reads land in vector registers: tell the compiler these are uniform,
+  // so the row-tile loop and its bounds stay scalar
+  count = __builtin_amdgcn_readfirstlane(count);
+  off = __builtin_amdgcn_readfirstlane(off);
+  wbase = __builtin_amdgcn_readfirstlane(wbase);
+  if (writer && tid == 0) {
+    ra.counts[e] = count;
+    ra.offsets[e] = off;
+    if (e == ra.E - 1) ra.offsets[ra.E] = off + count;
+  }
+  if (writer && e == ra.E - 1)
+    for (int i = off + count + tid; i < ra.S; i += blockDim.x) ra.sorted_slot[i] = -1;
+  if (count == 0) return;
+  // e's slots in ascending order (issuing the first weight groups before
+  // this step measured slower: the masks then stay live beside them)
+  auto collect = [&]() {
+    int rank = wbase;
+#pragma unroll
+    for (int c = 0; c < kSub; ++c) {
+      if (eq[c] >> lane & 1ull) {
+        const int s = s0 + c * 64 + lane;
+        const int j = rank + __popcll(eq[c] & below);
+        rows[j] = s;
+        if (writer) {
+          ra.sorted_slot[off + j] = s;
+          ra.slot_row[s] = off + j;
+        }
+      }
+      rank += __popcll(eq[c]);
+    }
+    __syncthreads();
+  };
+  collect();
+  for (int t0 = 0; t0 < count; t0 += BMR) {
+    // an opaque copy of e keeps the compiler from hoisting the weight loads
+    // out of this loop (they would all stay live in registers)
+    int ev = e;
+    asm volatile("" : "+s"(ev));
+    K::run(p, ev, off + t0, min(BMR, count - t0), [&](int r) { return (int64_t)(rows[t0 + r] / p.gather_k); },
+           dec_lds);
+    __syncthreads();                                        // the LDS tile is reused by the next row tile
+  }
+}
+
+template <int WB, bool A8, int NG, int DEPTH, int BMR>
+__global__ __launch_bounds__(256) void k_down_routed(GemmProblem p, const int32_t* counts, const int32_t* offsets) {
+  using K = Dec16<WB, A8, false, 2, NG, DEPTH, BMR>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t dec_lds[];
+  const int e = blockIdx.y;
+  const int count = counts[e], off = offsets[e];
+  for (int t0 = 0; t0 < count; t0 += BMR) {
+    const int row0 = off + t0;
+    int ev = e;                                             // opaque: no hoisting of weight loads
+    asm volatile("" : "+s"(ev));
+    K::run(p, ev, row0, min(BMR, count - t0), [&](int r) { return (int64_t)(row0 + r); }, dec_lds);
+    __syncthreads();
+  }
 }
 
 template <int WB, bool A8, bool DUAL, int FN, int NG, int DEPTH, int BMR>
@@ -689,7 +843,11 @@ template <int WB, bool A8, bool DUAL, int BMR>
 hipError_t launch_dec_shape(const GemmProblem& p, hipStream_t stream, bool* done) {
   *done = true;
   switch (p.kdim / kGroup) {
+    case 1: return launch_dec_ng<WB, A8, DUAL, 1, BMR>(p, stream);
+    case 2: return launch_dec_ng<WB, A8, DUAL, 2, BMR>(p, stream);
+    case 3: return launch_dec_ng<WB, A8, DUAL, 3, BMR>(p, stream);
     case 4: return launch_dec_ng<WB, A8, DUAL, 4, BMR>(p, stream);
+    case 5: return launch_dec_ng<WB, A8, DUAL, 5, BMR>(p, stream);
     case 8: return launch_dec_ng<WB, A8, DUAL, 8, BMR>(p, stream);
     case 12: return launch_dec_ng<WB, A8, DUAL, 12, BMR>(p, stream);
     case 16: return launch_dec_ng<WB, A8, DUAL, 16, BMR>(p, stream);
@@ -717,6 +875,48 @@ hipError_t launch_shape(const GemmProblem& p, hipStream_t stream) {
   else return launch_split<WB, A8, DUAL, 4, 1>(p, stream);
 }
 
+template <int WB, bool A8, int NG, int BMR>
+hipError_t launch_routed_ng(const GemmProblem& gu, const GemmProblem& dn, const RouteOut& ro, bool down,
+                            hipStream_t stream) {
+  constexpr int DEPTH = (NG < 8) ? NG : 8;
+  if (!down) {
+    using K = Dec16<WB, A8, true, 1, NG, DEPTH, BMR>;
+    const dim3 grid((gu.n + K::BN - 1) / K::BN, ro.E);
+    hipLaunchKernelGGL((k_gate_up_routed<WB, A8, NG, DEPTH, BMR>), grid, dim3(256), K::lds_bytes(), stream, gu, ro);
+  } else {
+    using K = Dec16<WB, A8, false, 2, NG, DEPTH, BMR>;
+    const dim3 grid((dn.n + K::BN - 1) / K::BN, ro.E);
+    hipLaunchKernelGGL((k_down_routed<WB, A8, NG, DEPTH, BMR>), grid, dim3(256), K::lds_bytes(), stream, dn,
+                       ro.counts, ro.offsets);
+  }
+  return hipGetLastError();
+}
+
+template <int WB, bool A8, int BMR>
+hipError_t launch_routed_g(int G, const GemmProblem& gu, const GemmProblem& dn, const RouteOut& ro, bool down,
+                           hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_routed_ng<WB, A8, 1, BMR>(gu, dn, ro, down, stream);
+    case 2: return launch_routed_ng<WB, A8, 2, BMR>(gu, dn, ro, down, stream);
+    case 3: return launch_routed_ng<WB, A8, 3, BMR>(gu, dn, ro, down, stream);
+    case 4: return launch_routed_ng<WB, A8, 4, BMR>(gu, dn, ro, down, stream);
+    case 5: return launch_routed_ng<WB, A8, 5, BMR>(gu, dn, ro, down, stream);
+    case 8: return launch_routed_ng<WB, A8, 8, BMR>(gu, dn, ro, down, stream);
+    case 12: return launch_routed_ng<WB, A8, 12, BMR>(gu, dn, ro, down, stream);
+    case 16: return launch_routed_ng<WB, A8, 16, BMR>(gu, dn, ro, down, stream);
+    case 32: return launch_routed_ng<WB, A8, 32, BMR>(gu, dn, ro, down, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int WB, bool A8>
+hipError_t launch_routed_mode(const GemmProblem& gu, const GemmProblem& dn, const RouteOut& ro, bool down,
+                              hipStream_t stream) {
+  const int G = (down ? dn.kdim : gu.kdim) / kGroup;
+  return (gu.bm <= 8) ? launch_routed_g<WB, A8, 8>(G, gu, dn, ro, down, stream)
+                      : launch_routed_g<WB, A8, 16>(G, gu, dn, ro, down, stream);
+}
+
 }  // namespace
 
 // Row-tile height: 8 when experts see only a few rows each (decode blocks: the
@@ -733,6 +933,31 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream) {
   }
   if (p.act_int8) return dual ? launch_shape<8, true, true>(p, stream) : launch_shape<8, true, false>(p, stream);
   return dual ? launch_shape<8, false, true>(p, stream) : launch_shape<8, false, false>(p, stream);
+}
+
+bool routed_applicable(int64_t S, int E, int H, int I, int act_int8) {
+  if (S > kRoutedMaxSlots) return false;
+  auto ok_g = [](int G) { return (G >= 1 && G <= 5) || G == 8 || G == 12 || G == 16 || G == 32; };
+  if (!ok_g(H / kGroup) || !ok_g(I / kGroup)) return false;
+  const int64_t rows = gemm_tile_rows(S, E, 0, 0) <= 8 ? 8 : 16;
+  const int64_t elem = act_int8 ? 1 : 2;
+  const int64_t extra_h = act_int8 ? (int64_t)(H / kGroup) * 64 : 0, extra_i = act_int8 ? (int64_t)(I / kGroup) * 64 : 0;
+  return rows * H * elem + extra_h <= kDecLdsMax && rows * I * elem + extra_i <= kDecLdsMax;
+}
+
+hipError_t launch_gate_up_routed(const GemmProblem& p, const RouteOut& ro, hipStream_t stream) {
+  const GemmProblem& dn = p;
+  if (p.bits == 4) return p.act_int8 ? launch_routed_mode<4, true>(p, dn, ro, false, stream)
+                                     : launch_routed_mode<4, false>(p, dn, ro, false, stream);
+  return p.act_int8 ? launch_routed_mode<8, true>(p, dn, ro, false, stream)
+                    : launch_routed_mode<8, false>(p, dn, ro, false, stream);
+}
+
+hipError_t launch_down_routed(const GemmProblem& p, const RouteOut& ro, hipStream_t stream) {
+  if (p.bits == 4) return p.act_int8 ? launch_routed_mode<4, true>(p, p, ro, true, stream)
+                                     : launch_routed_mode<4, false>(p, p, ro, true, stream);
+  return p.act_int8 ? launch_routed_mode<8, true>(p, p, ro, true, stream)
+                    : launch_routed_mode<8, false>(p, p, ro, true, stream);
 }
 
 }  // namespace qre

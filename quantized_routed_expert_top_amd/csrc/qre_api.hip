@@ -226,9 +226,9 @@ int qre_stage_workspace_bytes(const qre_desc* desc, size_t* bytes) {
   return QRE_OK;
 }
 
-int qre_moe_forward(const qre_desc* desc, const void* x, const int32_t* topk_ids, const float* topk_w,
-                    const qre_weights* weights, void* out, void* workspace, size_t workspace_bytes,
-                    qre_stream_t stream) {
+static int moe_forward_impl(const qre_desc* desc, const void* x, const int32_t* topk_ids, const float* topk_w,
+                            const qre_weights* weights, void* out, void* workspace, size_t workspace_bytes,
+                            hipEvent_t const* ev, hipStream_t s) {
   int rc = check_desc(desc);
   if (rc) return rc;
   const qre_desc& d = *desc;
@@ -240,30 +240,59 @@ int qre_moe_forward(const qre_desc* desc, const void* x, const int32_t* topk_ids
     return QRE_ERR_ALIGN;
   const Layout L = make_layout(d, workspace);
   if (workspace_bytes < L.bytes) return QRE_ERR_WORKSPACE;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t S = (int64_t)d.T * d.K;
   const StageLayout& st = L.st;
+  auto mark = [&](int i) -> hipError_t { return (ev && ev[i]) ? hipEventRecord(ev[i], s) : hipSuccess; };
 
-  hipError_t e = launch_route(topk_ids, d.T, d.K, d.E, L.counts, L.offsets, L.sorted_slot, L.slot_row,
-                              st.route_scratch, st.tiles_gu, st.ntiles, st.bm_gu, st.tiles_dn, st.ntiles + 1,
-                              st.bm_dn, s);
-  if (e != hipSuccess) return hip_status(e);
-  if (d.act_int8) {
-    e = launch_quantize_act(static_cast<const uint16_t*>(x), d.T, d.H, L.xq, L.xs, s);
-    if (e != hipSuccess) return hip_status(e);
-  }
-  e = launch_gemm(gate_up_problem(d, x, L.xq, L.xs, L.sorted_slot, *weights, st.tiles_gu, st.ntiles, st.mt_gu,
-                                  st.bm_gu, L.h), s);
-  if (e != hipSuccess) return hip_status(e);
-  if (d.act_int8) {
-    e = launch_quantize_act(L.h, (int)S, d.I, L.hq, L.hs, s);
-    if (e != hipSuccess) return hip_status(e);
-  }
-  e = launch_gemm(down_problem(d, L.h, L.hq, L.hs, *weights, st.tiles_dn, st.ntiles + 1, st.mt_dn, st.bm_dn, L.y),
-                  s);
-  if (e != hipSuccess) return hip_status(e);
-  e = launch_combine(L.y, L.slot_row, topk_w, d.T, d.K, d.H, static_cast<uint16_t*>(out), s);
+  const GemmProblem gu = gate_up_problem(d, x, L.xq, L.xs, L.sorted_slot, *weights, st.tiles_gu, st.ntiles,
+                                         st.mt_gu, st.bm_gu, L.h);
+  const GemmProblem dn = down_problem(d, L.h, L.hq, L.hs, *weights, st.tiles_dn, st.ntiles + 1, st.mt_dn, st.bm_dn,
+                                      L.y);
+  const bool routed = routed_applicable(S, d.E, d.H, d.I, d.act_int8);
+  const RouteOut ro = {topk_ids, (int)S, d.E, L.counts, L.offsets, L.sorted_slot, L.slot_row};
+  hipError_t e = mark(0);
+  if (e == hipSuccess && !routed)
+    e = launch_route(topk_ids, d.T, d.K, d.E, L.counts, L.offsets, L.sorted_slot, L.slot_row, st.route_scratch,
+                     st.tiles_gu, st.ntiles, st.bm_gu, st.tiles_dn, st.ntiles + 1, st.bm_dn, s);
+  if (e == hipSuccess && d.act_int8) e = launch_quantize_act(static_cast<const uint16_t*>(x), d.T, d.H, L.xq, L.xs, s);
+  if (e == hipSuccess) e = mark(1);
+  if (e == hipSuccess) e = routed ? launch_gate_up_routed(gu, ro, s) : launch_gemm(gu, s);
+  if (e == hipSuccess) e = mark(2);
+  if (e == hipSuccess && d.act_int8) e = launch_quantize_act(L.h, (int)S, d.I, L.hq, L.hs, s);
+  if (e == hipSuccess) e = mark(3);
+  if (e == hipSuccess) e = routed ? launch_down_routed(dn, ro, s) : launch_gemm(dn, s);
+  if (e == hipSuccess) e = mark(4);
+  if (e == hipSuccess) e = launch_combine(L.y, L.slot_row, topk_w, d.T, d.K, d.H, static_cast<uint16_t*>(out), s);
+  if (e == hipSuccess) e = mark(5);
   return hip_status(e);
+}
+
+int qre_moe_forward(const qre_desc* desc, const void* x, const int32_t* topk_ids, const float* topk_w,
+                    const qre_weights* weights, void* out, void* workspace, size_t workspace_bytes,
+                    qre_stream_t stream) {
+  return moe_forward_impl(desc, x, topk_ids, topk_w, weights, out, workspace, workspace_bytes, nullptr,
+                          reinterpret_cast<hipStream_t>(stream));
+}
+
+int qre_moe_forward_timed(const qre_desc* desc, const void* x, const int32_t* topk_ids, const float* topk_w,
+                          const qre_weights* weights, void* out, void* workspace, size_t workspace_bytes,
+                          void* const* events, qre_stream_t stream) {
+  if (!events) return QRE_ERR_NULL;
+  return moe_forward_impl(desc, x, topk_ids, topk_w, weights, out, workspace, workspace_bytes,
+                          reinterpret_cast<hipEvent_t const*>(events), reinterpret_cast<hipStream_t>(stream));
+}
+
+int qre_workspace_permutation(const qre_desc* desc, void* workspace, int32_t** counts, int32_t** offsets,
+                              int32_t** sorted_slot, int32_t** slot_row) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!workspace || !counts || !offsets || !sorted_slot || !slot_row) return QRE_ERR_NULL;
+  const Layout L = make_layout(*desc, workspace);
+  *counts = L.counts;
+  *offsets = L.offsets;
+  *sorted_slot = L.sorted_slot;
+  *slot_row = L.slot_row;
+  return QRE_OK;
 }
 
 int qre_read_dropped_slots(const qre_desc* desc, const void* workspace, int32_t* n_dropped, qre_stream_t stream) {

@@ -83,6 +83,19 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 // Row-tile height the GEMM wants for a problem with S sorted rows over E experts.
 int gemm_tile_rows(int64_t S, int E, int n, int kdim);
 
+// Decode-sized problems (up to kRoutedMaxSlots slots): the gate/up kernel
+// computes the permutation itself (writing counts, offsets, sorted_slot and
+// slot_row) and the down kernel reads counts/offsets back; no tile list.
+struct RouteOut {
+  const int32_t* ids;
+  int S, E;
+  int32_t *counts, *offsets, *sorted_slot, *slot_row;
+};
+constexpr int64_t kRoutedMaxSlots = 2048;
+bool routed_applicable(int64_t S, int E, int H, int I, int act_int8);
+hipError_t launch_gate_up_routed(const GemmProblem& p, const RouteOut& ro, hipStream_t stream);
+hipError_t launch_down_routed(const GemmProblem& p, const RouteOut& ro, hipStream_t stream);
+
 // Combine.
 hipError_t launch_combine(const uint16_t* y, const int32_t* slot_row, const float* topk_w, int T, int K,
                           int H, uint16_t* out, hipStream_t stream);

@@ -51,6 +51,9 @@ SMALL = [
     Workload("small_c", T=100, H=256, I=128, E=16, K=4, weight_bits=4, act_int8=True, seed=13),
     Workload("small_d", T=77, H=640, I=256, E=12, K=6, weight_bits=8, act_int8=True, seed=14,
              outlier_frac=0.02),
+    # more than 2048 slots: the separate routing launch and the row-tile GEMMs
+    Workload("small_e", T=300, H=256, I=128, E=16, K=8, weight_bits=4, act_int8=False, seed=15),
+    Workload("small_f", T=260, H=384, I=256, E=20, K=8, weight_bits=8, act_int8=True, seed=16),
 ]
 
 
@@ -128,3 +131,30 @@ def test_invariances_decode_shape():
     W2 = qre.QuantizedExperts(*(t[inv].contiguous() for t in (Wg.gate_q, Wg.gate_s, Wg.up_q, Wg.up_s,
                                                               Wg.down_q, Wg.down_s)), Wg.bits)
     np.testing.assert_array_equal(bf16_np(_run_gpu(x_bits, relabel[ids].astype(np.int32), w, W2, False)), a)
+
+
+@pytest.mark.parametrize("T,H,I,E,K,bits,a8", [
+    (32, 2048, 512, 256, 8, 4, False),     # decode block: permutation computed inside the gate/up kernel
+    (40, 256, 128, 6, 3, 8, True),
+    (300, 256, 128, 16, 8, 4, False),      # > 2048 slots: separate routing launch
+])
+def test_forward_permutation_matches_oracle(T, H, I, E, K, bits, a8):
+    """The permutation a forward call leaves in its workspace equals the
+    oracle's stable counting sort, bit for bit, including dropped and
+    duplicate ids."""
+    wl = Workload("perm", T=T, H=H, I=I, E=E, K=K, weight_bits=bits, act_int8=a8, seed=T + E)
+    x_bits = gen_x(wl)
+    ids, w = gen_routing(wl)
+    ids[0, -1] = ids[0, 0]
+    ids[1, 0] = -1
+    ids[T - 1, K - 1] = E + 3
+    Wg = to_gpu_experts(oracle_experts(wl, [0]), bits)
+    ws = torch.empty(qre.workspace_bytes(T, H, I, E, K, bits, a8), dtype=torch.uint8, device=DEV)
+    qre.moe_forward(x_tensor(x_bits, DEV), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), Wg,
+                    act_int8=a8, workspace=ws)
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy() for t in qre.workspace_permutation(T, H, I, E, K, bits, a8, ws)]
+    ref = oracle.route(ids, E)
+    for g, r in zip(got, ref[:4]):
+        np.testing.assert_array_equal(g, r)
+    assert qre.read_dropped_slots(T, H, I, E, K, bits, a8, ws) == ref[4] == 2
