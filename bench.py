@@ -30,7 +30,7 @@ BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, published
 I8_PEAK_TOPS = 5000.0
 METRIC = "routed-expert FFN tokens/s; % HBM peak (32-tok block) & % MFMA peak (prefill)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_{}.txt")
-GEMM_SRC = os.path.join(ROOT, "quantized_routed_expert_top_amd", "csrc", "gemm.hip")
+GEMM_SRCS = [os.path.join(ROOT, "quantized_routed_expert_top_amd", "csrc", f) for f in ("gemm.hip", "gemm_common.h")]
 
 
 def log(*a):
@@ -38,8 +38,11 @@ def log(*a):
 
 
 def source_digest() -> str:
-    with open(GEMM_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in GEMM_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(workload: str):
@@ -215,11 +218,23 @@ def main():
     tokens_per_s = wl.T * args.steps / wall
     gu_us, dn_us = float(dur[1]), float(dur[3])
     gu_bytes = alg["gate_up_weights"]
-    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(wl.name),
-                "kernel": "fused gate/up + SiLU*mul GEMM", "avg_us": round(gu_us, 2),
-                "alg_bytes_per_launch": int(gu_bytes)}
+    S = wl.T * wl.K
+    if S >= 16 * wl.E * 16:
+        # prefill: on average 256+ rows per expert, the gate/up GEMM is a
+        # dense contraction bound by the matrix cores
+        gu_flops = 2.0 * S * wl.H * 2 * wl.I
+        peak = I8_PEAK_TOPS if wl.act_int8 else BF16_PEAK_TFLOPS
+        achieved = gu_flops / (gu_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4), "traffic": read_traffic(wl.name),
+                    "kernel": "fused gate/up + SiLU*mul GEMM", "avg_us": round(gu_us, 2),
+                    "alg_flops_per_launch": gu_flops}
+    else:
+        achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(wl.name),
+                    "kernel": "fused gate/up + SiLU*mul GEMM", "avg_us": round(gu_us, 2),
+                    "alg_bytes_per_launch": int(gu_bytes)}
     step_bytes = alg["total"]
     result = {
         "metric": METRIC,

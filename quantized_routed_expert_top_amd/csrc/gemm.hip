@@ -40,104 +40,12 @@
 //    touching memory, so no load sits behind a branch;
 //  * workgroups are (column block, row tile); tiles past the device-side tile
 //    count exit at once, so no host readback is needed.
-#include <hip/hip_fp16.h>
-
-#include "qre_internal.h"
+#include "gemm_common.h"
 
 namespace qre {
 namespace {
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-constexpr uint32_t kOOB = 0x80000000u;   // offset past every descriptor (all are < 2^31 bytes)
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4_t bload16(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ uint32_t bload_u16(rsrc_t r, uint32_t off) {
-  return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-}
-__device__ __forceinline__ float bload_f32(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
-
-__device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
-  return __half2float(__ushort_as_half((unsigned short)h));
-}
-
-// A constant materialized in a VGPR: lets (x & M) | C select one v_and_or_b32
-// (a GFX9 VOP3 instruction reads at most one SGPR or literal).
-template <uint32_t C>
-__device__ __forceinline__ uint32_t vconst() {
-  uint32_t v;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "i"(C));
-  return v;
-}
-
-// Two BF16 values (exact small integers held in FP32) packed into one dword.
-__device__ __forceinline__ uint32_t pack_bf16_hi(float lo, float hi) {
-  return byte_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-
-// A operand of one MFMA step (16 bytes: 8 BF16 or 16 INT8 activations),
-// permuted into the reduction order of the INT4 weight operand below.  INT8
-// weights need no permutation.
-template <int WB, bool A8>
-__device__ __forceinline__ u32x4_t a_operand(u32x4_t c) {
-  if constexpr (WB == 8) return c;
-  u32x4_t av;
-  if constexpr (!A8) {        // BF16: pair codes k and k+4 of each 32-bit word
-    av.x = byte_perm(c.z, c.x, 0x05040100u);
-    av.y = byte_perm(c.z, c.x, 0x07060302u);
-    av.z = byte_perm(c.w, c.y, 0x05040100u);
-    av.w = byte_perm(c.w, c.y, 0x07060302u);
-  } else {                    // INT8: even codes then odd codes of each 32-bit word
-    av.x = byte_perm(c.y, c.x, 0x06040200u);
-    av.y = byte_perm(c.y, c.x, 0x07050301u);
-    av.z = byte_perm(c.w, c.z, 0x06040200u);
-    av.w = byte_perm(c.w, c.z, 0x07050301u);
-  }
-  return av;
-}
-
-// B operand for BF16 activations, MFMA step t (of 4), from the lane's slice of
-// a 128-group of one weight row (16 bytes INT4 / 32 bytes INT8).  The values
-// are 136 + q (INT4) or 128 + q (INT8), exact in BF16.
-template <int WB>
-__device__ __forceinline__ u32x4_t b_operand_bf16(const u32x4_t* b, int t, uint32_t mask_nib, uint32_t magic) {
-  u32x4_t bv;
-  if constexpr (WB == 4) {
-    const uint32_t w = b[0][t] ^ 0x88888888u;             // nibble -> q + 8
-    bv.x = (w & mask_nib) | magic;                        // bf16 (136+q_k, 136+q_{k+4})
-    bv.y = ((w >> 4) & mask_nib) | magic;
-    bv.z = ((w >> 8) & mask_nib) | magic;
-    bv.w = ((w >> 12) & mask_nib) | magic;
-  } else {
-    const uint32_t w0 = b[t >> 1][(t & 1) * 2] ^ 0x80808080u;       // byte -> q + 128
-    const uint32_t w1 = b[t >> 1][(t & 1) * 2 + 1] ^ 0x80808080u;
-    bv.x = pack_bf16_hi((float)(w0 & 0xffu), (float)((w0 >> 8) & 0xffu));
-    bv.y = pack_bf16_hi((float)((w0 >> 16) & 0xffu), (float)(w0 >> 24));
-    bv.z = pack_bf16_hi((float)(w1 & 0xffu), (float)((w1 >> 8) & 0xffu));
-    bv.w = pack_bf16_hi((float)((w1 >> 16) & 0xffu), (float)(w1 >> 24));
-  }
-  return bv;
-}
-
-// B operand for INT8 activations, MFMA step t (of 2): INT8 codes as they are,
-// INT4 codes as q + 8 (even codes then odd codes of each word).
-template <int WB>
-__device__ __forceinline__ u32x4_t b_operand_i8(const u32x4_t* b, int t) {
-  if constexpr (WB == 8) return b[t];
-  const uint32_t w0 = b[0][2 * t] ^ 0x88888888u;
-  const uint32_t w1 = b[0][2 * t + 1] ^ 0x88888888u;
-  return u32x4_t{w0 & 0x0f0f0f0fu, (w0 >> 4) & 0x0f0f0f0fu, w1 & 0x0f0f0f0fu, (w1 >> 4) & 0x0f0f0f0fu};
-}
+using namespace gk;
 
 template <int WB, bool A8, bool DUAL, int FN, int GW>
 struct Gemm16 {
@@ -667,85 +575,12 @@ template <int WB, bool A8, int NG, int DEPTH, int BMR>
 __global__ __launch_bounds__(256) void k_gate_up_routed(GemmProblem p, RouteOut ra) {
   using K = Dec16<WB, A8, true, 1, NG, DEPTH, BMR>;
   extern __shared__ __attribute__((aligned(16))) uint8_t dec_lds[];
-  __shared__ int wcnt[2][4];
   __shared__ int rows[kRoutedMaxSlots];                     // e's slots, ascending
-  const int e = blockIdx.y, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const bool writer = blockIdx.x == 0;
-  const uint64_t below = (1ull << lane) - 1ull;
-  constexpr int kSub = kRoutedMaxSlots / 256;              // 64-slot sub-chunks per wave
-  const int L = ((ra.S + 255) / 256) * 64;                  // slots per wave, a multiple of 64
-  const int s0 = min(ra.S, wave * L), s1 = min(ra.S, s0 + L);
-  // one pass over the ids: the ballot mask of e's slots per sub-chunk stays in
-  // registers; count e's slots and the valid slots of smaller experts
-  // all loads first (out-of-range sub-chunks read nothing), then the ballots
-  const rsrc_t rid = make_rsrc(ra.ids, (int64_t)ra.S * 4);
-  int ids[kSub];
-#pragma unroll
-  for (int c = 0; c < kSub; ++c) {
-    const int s = s0 + c * 64 + lane;
-    ids[c] = (int)__builtin_amdgcn_raw_buffer_load_b32(rid, s < s1 ? (uint32_t)s * 4u : kOOB, 0, 0);
-  }
-  uint64_t eq[kSub];
-  int n_eq = 0, n_lt = 0;
-#pragma unroll
-  for (int c = 0; c < kSub; ++c) {
-    const int s = s0 + c * 64 + lane;
-    const int id = s < s1 ? ids[c] : -1;
-    eq[c] = __ballot(id == e);
-    n_eq += __popcll(eq[c]);
-    n_lt += __popcll(__ballot(id >= 0 && id < e));
-  }
-  if (writer && e == 0) {
-#pragma unroll
-    for (int c = 0; c < kSub; ++c) {
-      const int s = s0 + c * 64 + lane;
-      if (s < s1 && (ids[c] < 0 || ids[c] >= ra.E)) ra.slot_row[s] = -1;      // dropped slot
-    }
-  }
-  if (lane == 0) {
-    wcnt[0][wave] = n_eq;
-    wcnt[1][wave] = n_lt;
-  }
-  __syncthreads();
-  int count = 0, off = 0, wbase = 0;
-  for (int w = 0; w < 4; ++w) {
-    if (w < wave) wbase += wcnt[0][w];
-    count += wcnt[0][w];
-    off += wcnt[1][w];
-  }
-  // LDS reads land in vector registers: tell the compiler these are uniform,
-  // so the row-tile loop and its bounds stay scalar
-  count = __builtin_amdgcn_readfirstlane(count);
-  off = __builtin_amdgcn_readfirstlane(off);
-  wbase = __builtin_amdgcn_readfirstlane(wbase);
-  if (writer && tid == 0) {
-    ra.counts[e] = count;
-    ra.offsets[e] = off;
-    if (e == ra.E - 1) ra.offsets[ra.E] = off + count;
-  }
-  if (writer && e == ra.E - 1)
-    for (int i = off + count + tid; i < ra.S; i += blockDim.x) ra.sorted_slot[i] = -1;
-  if (count == 0) return;
-  // e's slots in ascending order (issuing the first weight groups before
-  // this step measured slower: the masks then stay live beside them)
-  auto collect = [&]() {
-    int rank = wbase;
-#pragma unroll
-    for (int c = 0; c < kSub; ++c) {
-      if (eq[c] >> lane & 1ull) {
-        const int s = s0 + c * 64 + lane;
-        const int j = rank + __popcll(eq[c] & below);
-        rows[j] = s;
-        if (writer) {
-          ra.sorted_slot[off + j] = s;
-          ra.slot_row[s] = off + j;
-        }
-      }
-      rank += __popcll(eq[c]);
-    }
-    __syncthreads();
-  };
-  collect();
+  __shared__ int wcnt[2][4];
+  const int e = blockIdx.y;
+  const ExpertRows er = route_expert(ra, e, blockIdx.x == 0, rows, wcnt);
+  const int count = er.count, off = er.off;
+  if (count == 0) return;                                   // uniform over the workgroup
   for (int t0 = 0; t0 < count; t0 += BMR) {
     // an opaque copy of e keeps the compiler from hoisting the weight loads
     // out of this loop (they would all stay live in registers)

@@ -248,6 +248,8 @@ static int moe_forward_impl(const qre_desc* desc, const void* x, const int32_t* 
                                          st.mt_gu, st.bm_gu, L.h);
   const GemmProblem dn = down_problem(d, L.h, L.hq, L.hs, *weights, st.tiles_dn, st.ntiles + 1, st.mt_dn, st.bm_dn,
                                       L.y);
+  // Decode-sized problems: the permutation is folded into the gate/up kernel;
+  // otherwise the routing kernel builds it (and the row-tile lists).
   const bool routed = routed_applicable(S, d.E, d.H, d.I, d.act_int8);
   const RouteOut ro = {topk_ids, (int)S, d.E, L.counts, L.offsets, L.sorted_slot, L.slot_row};
   hipError_t e = mark(0);

@@ -1,0 +1,78 @@
+"""Text summaries of rocprofv3 output (the SQLite database it writes).
+
+    python -m quantized_routed_expert_top_amd.rocprof_summary kernels DIR [--top N]
+    python -m quantized_routed_expert_top_amd.rocprof_summary counters DIR [--kernel SUBSTR]
+
+`kernels` prints, per kernel name, the number of dispatches and the average,
+minimum, maximum and total duration (from a --kernel-trace run); `counters`
+prints, per kernel and counter, the mean value per dispatch (from a --pmc
+run).  DIR is the directory given to rocprofv3 with -d; every *.db below it is
+read.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import glob
+import os
+import sqlite3
+import sys
+
+
+def _dbs(d: str) -> list[str]:
+    paths = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))
+    if not paths:
+        raise SystemExit(f"no rocprofv3 database under {d}")
+    return paths
+
+
+def kernel_stats(d: str) -> list[tuple[str, int, float, float, float, float]]:
+    """(name, calls, avg_us, min_us, max_us, total_us), largest total first."""
+    acc: dict[str, list[float]] = collections.defaultdict(list)
+    for path in _dbs(d):
+        con = sqlite3.connect(path)
+        for name, dur in con.execute("select name, end - start from kernels"):
+            acc[name].append(dur / 1000.0)
+        con.close()
+    rows = [(n, len(v), sum(v) / len(v), min(v), max(v), sum(v)) for n, v in acc.items()]
+    rows.sort(key=lambda r: -r[5])
+    return rows
+
+
+def counter_means(d: str, kernel_substr: str = "") -> dict[str, dict[str, tuple[float, int]]]:
+    """{kernel: {counter: (mean value per dispatch, dispatches)}}."""
+    sums: dict[tuple[str, str], list[float]] = collections.defaultdict(list)
+    for path in _dbs(d):
+        con = sqlite3.connect(path)
+        q = ("select kernel_name, counter_name, dispatch_id, sum(value) from counters_collection "
+             "where kernel_name like ? group by kernel_name, counter_name, dispatch_id")
+        for k, c, _, v in con.execute(q, (f"%{kernel_substr}%",)):
+            sums[(k, c)].append(float(v))
+        con.close()
+    out: dict[str, dict[str, tuple[float, int]]] = collections.defaultdict(dict)
+    for (k, c), v in sums.items():
+        out[k][c] = (sum(v) / len(v), len(v))
+    return out
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("what", choices=["kernels", "counters"])
+    ap.add_argument("dir")
+    ap.add_argument("--top", type=int, default=12)
+    ap.add_argument("--kernel", default="")
+    a = ap.parse_args(argv)
+    if a.what == "kernels":
+        print(f"{'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'total_us':>11}  kernel")
+        for n, c, avg, mn, mx, tot in kernel_stats(a.dir)[: a.top]:
+            print(f"{c:6d} {avg:9.2f} {mn:9.2f} {mx:9.2f} {tot:11.1f}  {n}")
+    else:
+        for k, cs in counter_means(a.dir, a.kernel).items():
+            print(k)
+            for c, (v, n) in sorted(cs.items()):
+                print(f"    {c:24s} {v:18.1f}  (dispatches: {n})")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -54,6 +54,14 @@ SMALL = [
     # more than 2048 slots: the separate routing launch and the row-tile GEMMs
     Workload("small_e", T=300, H=256, I=128, E=16, K=8, weight_bits=4, act_int8=False, seed=15),
     Workload("small_f", T=260, H=384, I=256, E=20, K=8, weight_bits=8, act_int8=True, seed=16),
+    # reductions that are multiples of 512: the split-reduction expert kernels
+    # (permutation folded into gate/up; several 16-row tiles per expert;
+    # more than 2048 slots, after the routing kernel)
+    Workload("ks_a", T=40, H=512, I=512, E=8, K=2, weight_bits=4, act_int8=False, seed=17),
+    Workload("ks_b", T=200, H=1024, I=512, E=8, K=2, weight_bits=8, act_int8=True, seed=18),
+    Workload("ks_c", T=280, H=512, I=1536, E=64, K=8, weight_bits=4, act_int8=True, seed=19),
+    Workload("ks_d", T=64, H=2048, I=512, E=16, K=4, weight_bits=8, act_int8=False, seed=20),
+    Workload("ks_e", T=96, H=1536, I=1024, E=12, K=3, weight_bits=4, act_int8=False, seed=21),
 ]
 
 
@@ -137,6 +145,7 @@ def test_invariances_decode_shape():
     (32, 2048, 512, 256, 8, 4, False),     # decode block: permutation computed inside the gate/up kernel
     (40, 256, 128, 6, 3, 8, True),
     (300, 256, 128, 16, 8, 4, False),      # > 2048 slots: separate routing launch
+    (300, 512, 512, 64, 8, 4, True),       # > 2048 slots, split-reduction expert kernels
 ])
 def test_forward_permutation_matches_oracle(T, H, I, E, K, bits, a8):
     """The permutation a forward call leaves in its workspace equals the
