@@ -757,10 +757,11 @@ hipError_t launch_routed_mode(const GemmProblem& gu, const GemmProblem& dn, cons
 // Row-tile height: 8 when experts see only a few rows each (decode blocks: the
 // weights stream once per tile either way, and a smaller activation tile leaves
 // LDS for more workgroups), 16 otherwise.
-int gemm_tile_rows(int64_t S, int E, int, int) { return (S <= 4 * (int64_t)E) ? 8 : 16; }
+int gemm_tile_rows(int64_t S, int E, int, int) { return big_applicable(S, E) ? 128 : (S <= 4 * (int64_t)E) ? 8 : 16; }
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream) {
   if (p.max_tiles == 0 || p.n == 0) return hipSuccess;
+  if (p.bm == 128) return launch_gemm_big(p, stream);
   const bool dual = p.w1q != nullptr;
   if (p.bits == 4) {
     if (p.act_int8) return dual ? launch_shape<4, true, true>(p, stream) : launch_shape<4, true, false>(p, stream);
@@ -771,10 +772,10 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream) {
 }
 
 bool routed_applicable(int64_t S, int E, int H, int I, int act_int8) {
-  if (S > kRoutedMaxSlots) return false;
+  if (S > kRoutedMaxSlots || big_applicable(S, E)) return false;
   auto ok_g = [](int G) { return (G >= 1 && G <= 5) || G == 8 || G == 12 || G == 16 || G == 32; };
   if (!ok_g(H / kGroup) || !ok_g(I / kGroup)) return false;
-  const int64_t rows = gemm_tile_rows(S, E, 0, 0) <= 8 ? 8 : 16;
+  const int64_t rows = (S <= 4 * (int64_t)E) ? 8 : 16;
   const int64_t elem = act_int8 ? 1 : 2;
   const int64_t extra_h = act_int8 ? (int64_t)(H / kGroup) * 64 : 0, extra_i = act_int8 ? (int64_t)(I / kGroup) * 64 : 0;
   return rows * H * elem + extra_h <= kDecLdsMax && rows * I * elem + extra_i <= kDecLdsMax;

@@ -1,0 +1,572 @@
+// Grouped expert GEMMs for many rows per expert (prefill), CDNA4 (gfx950).
+//
+// Same arithmetic as the decode kernels (gemm.hip, gemm_common.h), which the
+// pages fix (minnow README, section "Quantization"; model card "LLaDA2.2-flash
+// for minnow", paragraphs after the precision table): weights dequantized in
+// registers, BF16 activations on BF16 MFMAs (FP32 sums) or INT8 activations
+// on INT8 MFMAs (exact INT32 sums per 128-group), each group's sum scaled in
+// FP32 and the groups added in FP32.  The tiling is this kernel's own, made
+// for tiles that the matrix cores, not HBM, bound:
+//  * workgroup tile: 128 sorted rows of one expert x 128 weight rows (the
+//    fused gate/up kernel takes 64 gate and the same 64 up rows, so the tile
+//    is 64 output columns of h); four waves in 2 x 2, each 64 x 64
+//    (sixteen 16x16 MFMA tiles);
+//  * the reduction is walked one 128-group at a time: the group's activation
+//    rows are staged into LDS (double-buffered, XOR-swizzled 16-byte chunks,
+//    already permuted into the operand order), together with one FP32 per row
+//    (the activation scale for INT8 activations, the row sum that removes the
+//    136 + q / 128 + q offset for BF16 activations); each wave loads its own
+//    weight columns straight into registers (16-byte buffer loads, next group
+//    in flight while the current one computes);
+//  * per group: MFMAs into a per-group accumulator, then one FP32 update of
+//    the running sums (INT8: acc += float(isum) * (xs * ws); BF16: acc +=
+//    ws * (gsum - offset * rowsum)), one barrier per group;
+//  * epilogue: SiLU(gate) * up (fused kernel) or the plain sum, rounded to
+//    BF16, rows past the tile's end masked.
+#include <type_traits>
+
+#include "gemm_common.h"
+
+namespace qre {
+namespace {
+
+using namespace gk;
+
+// s_waitcnt immediates waiting for vmcnt <= n only (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+constexpr int vmcnt_enc(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kLgkmcnt0 = 15 | (3 << 14) | (7 << 4);   // lgkmcnt(0), vmcnt and expcnt at their maxima
+constexpr int kVmcntEnc[17] = {vmcnt_enc(0),  vmcnt_enc(1),  vmcnt_enc(2),  vmcnt_enc(3),  vmcnt_enc(4),  vmcnt_enc(5),
+                               vmcnt_enc(6),  vmcnt_enc(7),  vmcnt_enc(8),  vmcnt_enc(9),  vmcnt_enc(10), vmcnt_enc(11),
+                               vmcnt_enc(12), vmcnt_enc(13), vmcnt_enc(14), vmcnt_enc(15), vmcnt_enc(16)};
+
+// 16-byte chunk swizzle of a staged row: chunk c of row r sits at position
+// c ^ swz(r).  Any 16 aligned consecutive rows then put a given chunk at 16
+// distinct 16-byte bank groups of a 256-byte window, and any 8 at 8 distinct
+// groups of a 128-byte window, so the MFMA operand reads (16 rows x one chunk
+// per 16 lanes) are conflict-free.  swz depends on r mod 16 only, so row
+// tiles 16 apart share read offsets up to a constant.
+__device__ __forceinline__ int swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
+
+// Workgroup -> (row tile, column block).  Workgroups are dispatched to the
+// eight XCDs round-robin (linear id mod 8), and each XCD has its own L2.  The
+// tile list is cut into eight contiguous ranges, one per XCD, walked tile by
+// tile with all column blocks of a tile adjacent: the column blocks of a tile
+// share its activation rows, and the consecutive tiles of an expert share its
+// weights, in one L2.  Returns false for workgroups past the device-side tile
+// count.
+__device__ __forceinline__ bool xcd_tile(const GemmProblem& p, int& tile, int& cb) {
+  const int ncb = gridDim.x;
+  const int lin = blockIdx.y * ncb + blockIdx.x;
+  const int xcd = lin & 7, k = lin >> 3;
+  const int nt = *p.ntiles;
+  const int per = (nt + 7) >> 3;
+  const int local = k / ncb;
+  cb = k - local * ncb;
+  tile = xcd * per + local;
+  return local < per && tile < nt;
+}
+
+template <int WB, bool A8, bool DUAL>
+struct Big {
+  static constexpr int BM = 128;                   // sorted rows per tile
+  static constexpr int BNO = DUAL ? 64 : 128;      // output columns per workgroup
+  static constexpr int TM = 4, TN = 4;             // 16x16 tiles per wave (64 x 64)
+  static constexpr int ELEM = A8 ? 1 : 2;
+  static constexpr int GB = kGroup * ELEM;         // bytes of one row's 128-group
+  static constexpr int CPG = GB / 16;              // 16-byte chunks per row-group
+  static constexpr int STEPS = A8 ? 2 : 4;         // MFMA steps per group
+  static constexpr int NB = (WB == 4) ? 1 : 2;     // 16-byte weight loads per lane per (tile, group)
+  static constexpr int WGB = kGroup * WB / 8;      // weight bytes per (column, group)
+  static constexpr int A_STAGE = BM * GB;          // LDS bytes of one staged A group
+  static constexpr bool RS8 = A8 && WB == 4;       // INT4 codes with INT8 activations need INT8 row sums
+  static constexpr int STAGE = A_STAGE + BM * 4 * (RS8 ? 2 : 1);   // + one FP32 per row (+ one INT32)
+  static constexpr int CPT = BM * CPG / 256;       // staged chunks per thread
+  static constexpr int RPI = 256 / CPG;            // rows covered per staging round
+  static constexpr int NH = A8 ? 1 : 2;            // staging halves (BF16: half a group in flight at a time)
+  static constexpr int QH = CPT / NH;              // staged chunks per thread per half
+  static constexpr size_t lds_bytes() { return 2 * (size_t)STAGE; }
+
+  __device__ static uint32_t lds_chunk(int row, int chunk) { return (uint32_t)(row * GB + ((chunk ^ swz(row)) << 4)); }
+
+  // tile: rows [row0, row0 + nrows) of expert e; src(r) = A row of local row r
+  template <class RowSrc>
+  __device__ static void run(const GemmProblem& p, int cb, int e, int row0, int nrows, RowSrc src, uint8_t* lds) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, kb = lane >> 4;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int NG = p.kdim / kGroup;
+    const int n0 = cb * BNO;
+
+    // weights: column of each 16-wide tile this lane feeds
+    const int64_t mat_bytes = (int64_t)p.n * NG * WGB;
+    rsrc_t rw[DUAL ? 2 : 1], rs[DUAL ? 2 : 1];
+#pragma unroll
+    for (int m = 0; m < (DUAL ? 2 : 1); ++m) {
+      rw[m] = make_rsrc((m == 0 ? p.w0q : p.w1q) + e * mat_bytes, mat_bytes);
+      rs[m] = make_rsrc((m == 0 ? p.w0s : p.w1s) + e * (int64_t)p.n * NG, (int64_t)p.n * NG * 2);
+    }
+    uint32_t wcol[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      wcol[j] = DUAL ? (uint32_t)(n0 + wn * 32 + (j & 1) * 16 + li) : (uint32_t)(n0 + wn * 64 + j * 16 + li);
+    auto wsrc = [&](int j) -> const rsrc_t& { return rw[DUAL ? (j >> 1) : 0]; };
+    auto ssrc = [&](int j) -> const rsrc_t& { return rs[DUAL ? (j >> 1) : 0]; };
+
+    // activations: the rows this thread stages
+    const rsrc_t ra = make_rsrc(p.a, p.a_rows * (int64_t)NG * GB);
+    const rsrc_t rx = make_rsrc(p.a_scale, A8 ? p.a_rows * (int64_t)NG * 4 : 0);
+    const int sc = tid % CPG;                        // chunk within the row-group
+    uint32_t a_off[CPT];
+    int aux_src[CPT];                                // A row (or -1) for the per-row FP32
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int r = tid / CPG + RPI * q;
+      const int64_t s = r < nrows ? src(r) : -1;
+      a_off[q] = s >= 0 ? (uint32_t)(s * NG * GB) + (uint32_t)(sc * 16) : kOOB;
+      aux_src[q] = (int)s;
+    }
+
+    // staging of half h of a group: chunks q in [h*QH, (h+1)*QH) of this thread
+    auto load_a = [&](u32x4_t* v, float* xs, int g, int h) {
+#pragma unroll
+      for (int k = 0; k < QH; ++k) v[k] = bload16(ra, a_off[h * QH + k] + (uint32_t)(g * GB));
+      if constexpr (A8) {
+#pragma unroll
+        for (int k = 0; k < QH; ++k) {
+          const int q = h * QH + k;
+          xs[k] = (sc == 0) ? bload_f32(rx, aux_src[q] >= 0 ? (uint32_t)((aux_src[q] * NG + g) * 4) : kOOB) : 0.f;
+        }
+      }
+    };
+    // write a staged half to LDS buffer b: permuted chunks, plus the per-row FP32
+    auto store_a = [&](const u32x4_t* v, const float* xs, int b, int h) {
+      uint8_t* base = lds + b * STAGE;
+      float* aux = reinterpret_cast<float*>(base + A_STAGE);
+#pragma unroll
+      for (int k = 0; k < QH; ++k) {
+        const int q = h * QH + k;
+        const int r = tid / CPG + RPI * q;
+        *reinterpret_cast<u32x4_t*>(base + lds_chunk(r, sc)) = a_operand<WB, A8>(v[k]);
+        if constexpr (A8) {
+          if (sc == 0) aux[r] = xs[k];
+          if constexpr (RS8) {
+            // exact row sum of the group's 128 INT8 activations: 16 per lane, 8 lanes per row
+            int t = 0;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) t = __builtin_amdgcn_sdot4((int)v[k][w], 0x01010101, t, false);
+#pragma unroll
+            for (int d = 1; d < CPG; d <<= 1) t += __shfl_xor(t, d);
+            if (sc == 0) reinterpret_cast<int*>(aux + BM)[r] = t;
+          }
+        } else {
+          // row sum of the group's 128 BF16 values: 8 per lane, 16 lanes per row
+          float t = 0.f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            t += bf16_bits_to_f32(v[k][w] & 0xffffu) + bf16_bits_to_f32(v[k][w] >> 16);
+#pragma unroll
+          for (int d = 1; d < CPG; d <<= 1) t += __shfl_xor(t, d);
+          if (sc == 0) aux[r] = t;
+        }
+      }
+    };
+
+    struct WB_ {
+      u32x4_t b[TN][NB];
+      uint32_t s[TN];
+    };
+    auto load_w = [&](WB_& w, int g) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+          w.b[j][q] = bload16(wsrc(j), (wcol[j] * NG + g) * WGB + kb * 16 * NB + 16 * q);
+        w.s[j] = bload_u16(ssrc(j), (wcol[j] * NG + g) * 2);
+      }
+    };
+
+    // LDS read bases of this lane's A operand per step (row tile offsets are constants)
+    uint32_t a_base[STEPS];
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t) a_base[t] = lds_chunk(wm * 64 + li, (A8 ? kb * 2 : kb * 4) + t);
+    const uint32_t mask_nib = vconst<0x000f000fu>(), magic = vconst<0x43004300u>();
+
+    f32x4_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // prologue: group 0 staged, its weights in flight
+    WB_ wcur;
+    load_w(wcur, 0);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      u32x4_t v[QH];
+      float xs[QH];
+      load_a(v, xs, 0, h);
+      store_a(v, xs, 0, h);
+    }
+    __syncthreads();
+
+    for (int g = 0; g < NG; ++g) {
+      const int b = g & 1;
+      const bool more = g + 1 < NG;
+      // the next group's activations are in flight during this whole group
+      u32x4_t vn[QH];
+      float xsn[QH];
+      if (more) load_a(vn, xsn, g + 1, 0);
+      const uint8_t* base = lds + b * STAGE;
+      const float* aux = reinterpret_cast<const float*>(base + A_STAGE);
+      float ws[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) ws[j] = half_bits_to_f32(wcur.s[j]);
+      if constexpr (!A8) {
+        f32x4_t part[TM][TN];
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) {
+          u32x4_t bv[TN];
+#pragma unroll
+          for (int j = 0; j < TN; ++j) bv[j] = b_operand_bf16<WB>(wcur.b[j], t, mask_nib, magic);
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            const bf16x8_t av =
+                __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(base + a_base[t] + i * 16 * GB));
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  av, __builtin_bit_cast(bf16x8_t, bv[j]), t == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : part[i][j], 0, 0, 0);
+          }
+          if (NH == 2 && t == STEPS / 2 - 1 && more) {   // first half staged, second half in flight
+            store_a(vn, xsn, b ^ 1, 0);
+            load_a(vn, xsn, g + 1, NH - 1);
+          }
+        }
+        // the weight registers are free once the last MFMA has read them
+        if (more) load_w(wcur, g + 1);
+        constexpr float kOff = (WB == 4) ? 136.0f : 128.0f;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const f32x4_t rsum = *reinterpret_cast<const f32x4_t*>(aux + wm * 64 + i * 16 + 4 * kb);
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              acc[i][j][v] = __builtin_fmaf(ws[j], __builtin_fmaf(-kOff, rsum[v], part[i][j][v]), acc[i][j][v]);
+        }
+      } else {
+        i32x4_t part[TM][TN];
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) {
+          u32x4_t bv[TN];
+#pragma unroll
+          for (int j = 0; j < TN; ++j) bv[j] = b_operand_i8<WB>(wcur.b[j], t);
+#pragma unroll
+          for (int i = 0; i < TM; ++i) {
+            const i32x4_t av =
+                __builtin_bit_cast(i32x4_t, *reinterpret_cast<const u32x4_t*>(base + a_base[t] + i * 16 * GB));
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              part[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                  av, __builtin_bit_cast(i32x4_t, bv[j]), t == 0 ? i32x4_t{0, 0, 0, 0} : part[i][j], 0, 0, 0);
+          }
+        }
+        if (more) load_w(wcur, g + 1);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(aux + wm * 64 + i * 16 + 4 * kb);
+          // INT4 codes entered as q + 8: remove 8 * (row sum of the INT8 activations)
+          i32x4_t rs8 = {0, 0, 0, 0};
+          if constexpr (RS8) rs8 = *reinterpret_cast<const i32x4_t*>(aux + BM + wm * 64 + i * 16 + 4 * kb);
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int isum = RS8 ? part[i][j][v] - 8 * rs8[v] : part[i][j][v];
+              acc[i][j][v] = __builtin_fmaf((float)isum, xs[v] * ws[j], acc[i][j][v]);
+            }
+        }
+      }
+      if (more) store_a(vn, xsn, b ^ 1, NH - 1);
+      __syncthreads();
+    }
+
+    // epilogue: lane holds rows 16i + 4kb + v of column 16j + li of its wave tile
+    uint16_t* out = static_cast<uint16_t*>(p.out);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = wm * 64 + i * 16 + 4 * kb + v;
+        if (r < nrows) {
+          uint16_t* orow = out + (int64_t)(row0 + r) * p.n;
+          if constexpr (DUAL) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              orow[n0 + wn * 32 + j * 16 + li] = (uint16_t)f32_to_bf16_bits(silu(acc[i][j][v]) * acc[i][j + 2][v]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) orow[n0 + wn * 64 + j * 16 + li] = (uint16_t)f32_to_bf16_bits(acc[i][j][v]);
+          }
+        }
+      }
+  }
+};
+
+// INT8 weights with INT8 activations.  Both operands reach LDS through direct
+// buffer->LDS loads (no staging registers), in stages of half a 128-group
+// (64 reduction bytes of 128 rows and of 128 weight rows), four stages, loads
+// issued three half-groups ahead.  A direct load writes lane L's 16 bytes at
+// base + 16 L, so each lane fetches the chunk that belongs at its position:
+// row r keeps its four chunks at positions c ^ ((r >> 2) & 3), which makes
+// the operand reads (16 rows x one chunk per 16 lanes) conflict-free.  Each
+// stage also holds the activation scales (each wave loads 64 into its own
+// 256-byte window; windows 2 and 3 repeat 0 and 1) and the weight scales (one
+// aligned 32-bit word per weight row holding its FP16 scale), loaded with the
+// first half of a group; the second half's scale loads are out-of-range
+// no-ops.  Every stage issues the same six direct loads and nothing else, so
+// one static vmcnt fits all and no register waits on a load in flight.
+template <bool DUAL>
+struct BigW8A8 {
+  static constexpr int BM = 128, BNW = 128;
+  static constexpr int BNO = DUAL ? 64 : 128;      // output columns per workgroup
+  static constexpr int TM = 4, TN = 4;             // 16x16 tiles per wave (64 x 64)
+  static constexpr int HB = kGroup / 2;            // reduction bytes per stage (half a group)
+  static constexpr int QA = BM * HB / 16 / 256;    // direct A loads per thread per stage (2)
+  static constexpr int QB = BNW * HB / 16 / 256;   // direct B loads per thread per stage (2)
+  static constexpr int B_OFF = BM * HB, X_OFF = B_OFF + BNW * HB, S_OFF = X_OFF + 1024;
+  static constexpr int STAGE = S_OFF + 1024;
+  static constexpr int NS = 4;                     // stages; loads run NS - 1 stages ahead
+  static constexpr int VM = QA + QB + 2;           // direct loads per thread per stage
+  static constexpr size_t lds_bytes() { return NS * (size_t)STAGE; }
+
+  __device__ static uint32_t chunk_pos(int row, int chunk) {
+    return (uint32_t)(row * HB + ((chunk ^ ((row >> 2) & 3)) << 4));
+  }
+
+  template <class RowSrc>
+  __device__ static void run(const GemmProblem& p, int cb, int e, int row0, int nrows, RowSrc src, uint8_t* lds) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, kb = lane >> 4;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int NG = p.kdim / kGroup;
+    const int NH = 2 * NG;                          // stages of this tile
+    const int n0 = cb * BNO;
+    const int64_t mat_bytes = (int64_t)p.n * NG * kGroup;
+    const rsrc_t rw0 = make_rsrc(p.w0q + e * mat_bytes, mat_bytes);
+    const rsrc_t rw1 = DUAL ? make_rsrc(p.w1q + e * mat_bytes, mat_bytes) : rw0;
+    const rsrc_t rs0 = make_rsrc(p.w0s + e * (int64_t)p.n * NG, (int64_t)p.n * NG * 2);
+    const rsrc_t rs1 = DUAL ? make_rsrc(p.w1s + e * (int64_t)p.n * NG, (int64_t)p.n * NG * 2) : rs0;
+    const rsrc_t ra = make_rsrc(p.a, p.a_rows * (int64_t)NG * kGroup);
+    const rsrc_t rx = make_rsrc(p.a_scale, p.a_rows * (int64_t)NG * 4);
+
+    // per-lane source offsets of the direct loads: stage h = 2g + t holds the
+    // chunks 2c + t (c = 0..3) of group g, at offset g * 128 + t * 16 from these
+    uint32_t a_off[QA], b_off[QB];
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+      const int P = (q * 4 + wave) * 64 + lane, row = P >> 2, c = (P & 3) ^ ((row >> 2) & 3);
+      a_off[q] = row < nrows ? (uint32_t)(src(row) * NG * kGroup) + (uint32_t)(c * 32) : kOOB;
+    }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const int P = (q * 4 + wave) * 64 + lane, n = P >> 2, c = (P & 3) ^ ((n >> 2) & 3);
+      const int wrow = DUAL ? n0 + (n & 63) : n0 + n;  // DUAL: n < 64 gate (q = 0), else up (q = 1)
+      b_off[q] = (uint32_t)(wrow * NG * kGroup) + (uint32_t)(c * 32);
+    }
+    const int xrow = (wave & 1) * 64 + lane;
+    const uint32_t x_off = xrow < nrows ? (uint32_t)(src(xrow) * NG * 4) : kOOB;
+    // scale of weight row srow (local), group g: the aligned word at
+    // ((wrow * NG + g) * 2) & ~3 (the FP16 value is its high half when the
+    // element index is odd); a row of scales is 4-byte aligned (n * NG even)
+    const int srow = (wave & 1) * 64 + lane;
+    const int swrow = DUAL ? n0 + (srow & 63) : n0 + srow;
+    const uint32_t s_el = (uint32_t)(swrow * NG);
+    const bool s_up = DUAL && srow >= 64;
+
+    auto lds3 = [&](int off) { return (__attribute__((address_space(3))) void*)(lds + off); };
+    // stage loads of half-group h into stage st (h past the end: out-of-range no-ops)
+    auto issue = [&](int h, auto stc) {
+      constexpr int st = decltype(stc)::value;
+      const uint32_t soff = h < NH ? 0u : kOOB;
+      const uint32_t ssoff = (h < NH && (h & 1) == 0) ? 0u : kOOB;   // scales once per group
+      const int g = h >> 1, t = h & 1;
+      const uint32_t koff = (uint32_t)(g * kGroup + t * 16);
+      const int base = st * STAGE;
+#pragma unroll
+      for (int q = 0; q < QA; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds3(base + (q * 4 + wave) * 1024), 16, a_off[q] + koff, soff, 0,
+                                                 0);
+#pragma unroll
+      for (int q = 0; q < QB; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(DUAL && q == 1 ? rw1 : rw0, lds3(base + B_OFF + (q * 4 + wave) * 1024),
+                                                 16, b_off[q] + koff, soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lds3(base + X_OFF + wave * 256), 4, x_off + g * 4, ssoff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_up ? rs1 : rs0, lds3(base + S_OFF + wave * 256), 4,
+                                               ((s_el + g) * 2) & ~3u, ssoff, 0, 0);
+    };
+
+    // LDS read bases (row tile and column tile offsets are compile-time constants)
+    const uint32_t a_rd = chunk_pos(wm * 64 + li, kb);
+    const uint32_t b_rd = chunk_pos((DUAL ? wn * 32 : wn * 64) + li, kb);
+
+    f32x4_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    i32x4_t part[TM][TN];
+    f32x4_t xsr[TM];
+    float ws[TN];
+
+    // one stage: wait for it, refill the stage read last time, compute
+    auto body = [&](int h, auto stc) {
+      constexpr int st = decltype(stc)::value;
+      constexpr int t = st & 1;                      // stage index and half agree (NS even)
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc((NS - 2) * VM));   // this thread's loads of stage h landed
+      __builtin_amdgcn_s_waitcnt(kLgkmcnt0);                   // and its LDS reads of stage h - 1 completed
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();                  // every thread's; stage h - 1 may be refilled
+      asm volatile("" ::: "memory");
+      issue(h + NS - 1, std::integral_constant<int, (st + NS - 1) % NS>{});
+      const uint8_t* base = lds + st * STAGE;
+      if constexpr (t == 0) {
+        const float* xsl = reinterpret_cast<const float*>(base + X_OFF);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) xsr[i] = *reinterpret_cast<const f32x4_t*>(xsl + wm * 64 + i * 16 + 4 * kb);
+        const uint32_t* sl = reinterpret_cast<const uint32_t*>(base + S_OFF);
+        const int g = h >> 1;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int nl = (DUAL ? (j >> 1) * 64 + wn * 32 + (j & 1) * 16 : wn * 64 + j * 16) + li;
+          const uint32_t w = sl[nl];
+          const uint32_t el = (uint32_t)((DUAL ? n0 + (nl & 63) : n0 + nl) * NG + g);
+          ws[j] = half_bits_to_f32((el & 1u) ? (w >> 16) : (w & 0xffffu));
+        }
+      }
+      u32x4_t bv[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int nj = DUAL ? ((j >> 1) * 64 + (j & 1) * 16) : j * 16;   // DUAL: up rows start at 64
+        bv[j] = *reinterpret_cast<const u32x4_t*>(base + B_OFF + b_rd + nj * HB);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const i32x4_t av = __builtin_bit_cast(i32x4_t, *reinterpret_cast<const u32x4_t*>(base + a_rd + i * 16 * HB));
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          part[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, __builtin_bit_cast(i32x4_t, bv[j]),
+                                                             t == 0 ? i32x4_t{0, 0, 0, 0} : part[i][j], 0, 0, 0);
+      }
+      if constexpr (t == 1) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              acc[i][j][v] = __builtin_fmaf((float)part[i][j][v], xsr[i][v] * ws[j], acc[i][j][v]);
+      }
+    };
+
+    issue(0, std::integral_constant<int, 0>{});
+    issue(1, std::integral_constant<int, 1>{});
+    issue(2, std::integral_constant<int, 2>{});
+    // whole rounds of four stages: with an odd group count the last group is
+    // a no-op one (zero operands, zero scales), which keeps every round the
+    // same straight-line code and every wait count static
+    for (int h = 0; h < NH; h += 4) {
+      body(h, std::integral_constant<int, 0>{});
+      body(h + 1, std::integral_constant<int, 1>{});
+      body(h + 2, std::integral_constant<int, 2>{});
+      body(h + 3, std::integral_constant<int, 3>{});
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));        // no load into LDS outlives the workgroup
+
+    uint16_t* out = static_cast<uint16_t*>(p.out);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = wm * 64 + i * 16 + 4 * kb + v;
+        if (r < nrows) {
+          uint16_t* orow = out + (int64_t)(row0 + r) * p.n;
+          if constexpr (DUAL) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              orow[n0 + wn * 32 + j * 16 + li] = (uint16_t)f32_to_bf16_bits(silu(acc[i][j][v]) * acc[i][j + 2][v]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) orow[n0 + wn * 64 + j * 16 + li] = (uint16_t)f32_to_bf16_bits(acc[i][j][v]);
+          }
+        }
+      }
+  }
+};
+
+template <bool DUAL>
+__global__ __launch_bounds__(256, 2) void k_gemm_w8a8(GemmProblem p) {
+  using K = BigW8A8<DUAL>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t big_lds[];
+  int tile, cb;
+  if (!xcd_tile(p, tile, cb)) return;
+  const Tile td = p.tiles[tile];
+  const int row0 = td.row0;
+  if (p.gather_k)
+    K::run(p, cb, td.e, row0, td.nrows, [&](int r) { return (int64_t)(p.sorted_slot[row0 + r] / p.gather_k); },
+           big_lds);
+  else
+    K::run(p, cb, td.e, row0, td.nrows, [&](int r) { return (int64_t)(row0 + r); }, big_lds);
+}
+
+template <int WB, bool A8, bool DUAL>
+__global__ __launch_bounds__(256, 2) void k_gemm_big(GemmProblem p) {
+  using K = Big<WB, A8, DUAL>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t big_lds[];
+  int tile, cb;
+  if (!xcd_tile(p, tile, cb)) return;
+  const Tile td = p.tiles[tile];
+  const int row0 = td.row0;
+  if (p.gather_k)
+    K::run(p, cb, td.e, row0, td.nrows, [&](int r) { return (int64_t)(p.sorted_slot[row0 + r] / p.gather_k); },
+           big_lds);
+  else
+    K::run(p, cb, td.e, row0, td.nrows, [&](int r) { return (int64_t)(row0 + r); }, big_lds);
+}
+
+template <bool DUAL>
+hipError_t launch_w8a8_cfg(const GemmProblem& p, hipStream_t stream) {
+  using K = BigW8A8<DUAL>;
+  if (p.n % K::BNO != 0) return hipErrorInvalidValue;
+  const dim3 grid(p.n / K::BNO, (unsigned)((p.max_tiles + 7) / 8 * 8));
+  hipLaunchKernelGGL((k_gemm_w8a8<DUAL>), grid, dim3(256), K::lds_bytes(), stream, p);
+  return hipGetLastError();
+}
+
+template <int WB, bool A8, bool DUAL>
+hipError_t launch_big_cfg(const GemmProblem& p, hipStream_t stream) {
+  using K = Big<WB, A8, DUAL>;
+  if (p.n % K::BNO != 0) return hipErrorInvalidValue;
+  const dim3 grid(p.n / K::BNO, (unsigned)((p.max_tiles + 7) / 8 * 8));
+  hipLaunchKernelGGL((k_gemm_big<WB, A8, DUAL>), grid, dim3(256), K::lds_bytes(), stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool big_applicable(int64_t S, int E) {
+  // many rows per expert: at least 64 on average
+  return S >= 64 * (int64_t)E;
+}
+
+hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t stream) {
+  const bool dual = p.w1q != nullptr;
+  if (p.bm != 128) return hipErrorInvalidValue;
+  if (p.bits == 4) {
+    if (p.act_int8) return dual ? launch_big_cfg<4, true, true>(p, stream) : launch_big_cfg<4, true, false>(p, stream);
+    return dual ? launch_big_cfg<4, false, true>(p, stream) : launch_big_cfg<4, false, false>(p, stream);
+  }
+  if (p.act_int8) return dual ? launch_w8a8_cfg<true>(p, stream) : launch_w8a8_cfg<false>(p, stream);
+  return dual ? launch_big_cfg<8, false, true>(p, stream) : launch_big_cfg<8, false, false>(p, stream);
+}
+
+}  // namespace qre

@@ -123,9 +123,9 @@ int check_desc(const qre_desc* d) {
   if ((int64_t)d->T * d->H * 2 >= (1ll << 31) || S * d->I * 2 >= (1ll << 31)) return QRE_ERR_LIMIT;
   if ((int64_t)d->H * d->I * 2 >= (1ll << 31)) return QRE_ERR_LIMIT;
   if (max_tiles(S, d->E, 1) >= (1ll << 31)) return QRE_ERR_LIMIT;
-  // grid limit of the GEMM launch (row tiles along grid.y)
-  if (max_tiles(S, d->E, gemm_tile_rows(S, d->E, 2 * d->I, d->H)) > 65535) return QRE_ERR_LIMIT;
-  if (max_tiles(S, d->E, gemm_tile_rows(S, d->E, d->H, d->I)) > 65535) return QRE_ERR_LIMIT;
+  // grid limit of the GEMM launch (row tiles along grid.y, rounded up to a multiple of 8)
+  if (max_tiles(S, d->E, gemm_tile_rows(S, d->E, 2 * d->I, d->H)) > 65528) return QRE_ERR_LIMIT;
+  if (max_tiles(S, d->E, gemm_tile_rows(S, d->E, d->H, d->I)) > 65528) return QRE_ERR_LIMIT;
   return QRE_OK;
 }
 

@@ -62,6 +62,12 @@ SMALL = [
     Workload("ks_c", T=280, H=512, I=1536, E=64, K=8, weight_bits=4, act_int8=True, seed=19),
     Workload("ks_d", T=64, H=2048, I=512, E=16, K=4, weight_bits=8, act_int8=False, seed=20),
     Workload("ks_e", T=96, H=1536, I=1024, E=12, K=3, weight_bits=4, act_int8=False, seed=21),
+    # at least 64 rows per expert on average: the 128-row MFMA tiles (several
+    # tiles per expert with ragged tails; a reduction of one group)
+    Workload("big_a", T=600, H=256, I=128, E=4, K=2, weight_bits=4, act_int8=False, seed=22),
+    Workload("big_b", T=700, H=384, I=256, E=6, K=3, weight_bits=8, act_int8=True, seed=23),
+    Workload("big_c", T=500, H=512, I=384, E=5, K=2, weight_bits=4, act_int8=True, seed=24),
+    Workload("big_d", T=400, H=640, I=256, E=3, K=2, weight_bits=8, act_int8=False, seed=25),
 ]
 
 
