@@ -22,9 +22,13 @@ namespace qre {
 namespace {
 
 constexpr int kSmallMax = 8192;   // slots handled by the one-workgroup kernel
-constexpr int kLargeChunk = 1024; // slots per wave in the three-kernel path
+constexpr int kLargeChunk = 256;  // slots per wave in the three-kernel path
+constexpr int kBatch = 4;         // 64-slot rows whose id loads are issued together
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Partitions of the wave range per expert in the scan kernel (1024 threads).
+__host__ __device__ constexpr int scan_parts(int E) { return E >= 1024 ? 1 : (1024 / E > 16 ? 16 : 1024 / E); }
 
 // Mask of the lanes whose key equals this lane's key (keys < 2^nbits).
 // Must be called by all 64 lanes.
@@ -45,36 +49,48 @@ __device__ __forceinline__ uint32_t slot_key(const int32_t* ids, int64_t s, int6
 }
 
 // Count this wave's chunk [c0, c1) into hist_row[E] (LDS, zeroed by the caller).
+// The ids of kBatch rows of 64 slots are loaded before the first is counted.
 __device__ void wave_count(const int32_t* ids, int64_t c0, int64_t c1, int E, int nbits, int* hist_row) {
   const int lane = lane_id();
-  for (int64_t base = c0; base < c1; base += kWave) {
-    const uint32_t key = slot_key(ids, base + lane, c1, E);
-    const uint64_t m = match_any(key, nbits);
-    if (key < (uint32_t)E && lane == __builtin_ctzll(m)) hist_row[key] += __popcll(m);
+  for (int64_t base = c0; base < c1; base += kWave * kBatch) {
+    uint32_t key[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) key[b] = slot_key(ids, base + b * kWave + lane, c1, E);
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const uint64_t m = match_any(key[b], nbits);
+      if (key[b] < (uint32_t)E && lane == __builtin_ctzll(m)) hist_row[key[b]] += __popcll(m);
+    }
   }
 }
 
 // Scatter this wave's chunk; base_row[e] (LDS) holds the next output position
-// of expert e for this wave and is advanced as the chunk is walked.
+// of expert e for this wave and is advanced as the chunk is walked (in slot
+// order, so equal ids keep ascending slot order).
 __device__ void wave_scatter(const int32_t* ids, int64_t c0, int64_t c1, int E, int nbits, int* base_row,
                              int32_t* sorted_slot, int32_t* slot_row) {
   const int lane = lane_id();
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int64_t base = c0; base < c1; base += kWave) {
-    const int64_t s = base + lane;
-    const uint32_t key = slot_key(ids, s, c1, E);
-    const uint64_t m = match_any(key, nbits);
-    if (s < c1) {
-      if (key < (uint32_t)E) {
-        const int pos = base_row[key] + __popcll(m & below);
-        sorted_slot[pos] = (int32_t)s;
-        slot_row[s] = pos;
-      } else {
-        slot_row[s] = -1;
+  for (int64_t base0 = c0; base0 < c1; base0 += kWave * kBatch) {
+    uint32_t key[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) key[b] = slot_key(ids, base0 + b * kWave + lane, c1, E);
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int64_t s = base0 + b * kWave + lane;
+      const uint64_t m = match_any(key[b], nbits);
+      if (s < c1) {
+        if (key[b] < (uint32_t)E) {
+          const int pos = base_row[key[b]] + __popcll(m & below);
+          sorted_slot[pos] = (int32_t)s;
+          slot_row[s] = pos;
+        } else {
+          slot_row[s] = -1;
+        }
       }
+      // every lane has read base_row[key] above; LDS ops of one wave stay in order
+      if (key[b] < (uint32_t)E && lane == __builtin_ctzll(m)) base_row[key[b]] += __popcll(m);
     }
-    // every lane has read base_row[key] above; LDS ops of one wave stay in order
-    if (key < (uint32_t)E && lane == __builtin_ctzll(m)) base_row[key] += __popcll(m);
   }
 }
 
@@ -191,6 +207,11 @@ __global__ __launch_bounds__(256) void k_route_count(const int32_t* __restrict__
   for (int e = lane_id(); e < E; e += kWave) ghist[gw * E + e] = row[e];
 }
 
+// Per-expert prefix over the waves' counts.  The wave range is cut into NP
+// partitions per expert (NP * E threads' worth of independent loads): pass 1
+// sums each partition, the partition sums are scanned per expert, pass 2
+// writes every wave's base.  LDS: cnt[E], offs[E+1], scratch[E], wave_tmp[16],
+// part[NP][E].
 __global__ __launch_bounds__(1024) void k_route_scan(int32_t* ghist, int nwaves, int E, int32_t* counts,
                                                      int32_t* offsets, Tile* tiles_a, int32_t* ntiles_a, int bm_a,
                                                      Tile* tiles_b, int32_t* ntiles_b, int bm_b) {
@@ -199,19 +220,59 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* ghist, int nwaves,
   int* offs = cnt + E;             // [E+1]
   int* scratch = offs + E + 1;     // [E]
   int* wave_tmp = scratch + E;     // [16]
+  int* part = wave_tmp + 16;       // [NP][E]
+  const int NP = scan_parts(E);
   const int tid = threadIdx.x;
+  constexpr int U = 32;            // loads in flight per thread
+  for (int i = tid; i < NP * E; i += blockDim.x) {
+    const int e = i % E, q = i / E;
+    const int v0 = (int)((int64_t)q * nwaves / NP), v1 = (int)((int64_t)(q + 1) * nwaves / NP);
+    int sum = 0;
+    int v = v0;
+    for (; v + U <= v1; v += U) {
+      int c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) c[u] = ghist[(int64_t)(v + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < U; ++u) sum += c[u];
+    }
+    for (; v < v1; ++v) sum += ghist[(int64_t)v * E + e];
+    part[q * E + e] = sum;
+  }
+  __syncthreads();
   for (int e = tid; e < E; e += blockDim.x) {
     int run = 0;
-    for (int v = 0; v < nwaves; ++v) {
-      const int c = ghist[(int64_t)v * E + e];
-      ghist[(int64_t)v * E + e] = run;
+    for (int q = 0; q < NP; ++q) {
+      const int c = part[q * E + e];
+      part[q * E + e] = run;
       run += c;
     }
     cnt[e] = run;
     offs[e] = run;
   }
   __syncthreads();
-  const int total = block_exclusive_scan(offs, E, wave_tmp);
+  for (int i = tid; i < NP * E; i += blockDim.x) {
+    const int e = i % E, q = i / E;
+    const int v0 = (int)((int64_t)q * nwaves / NP), v1 = (int)((int64_t)(q + 1) * nwaves / NP);
+    int run = part[q * E + e];
+    int v = v0;
+    for (; v + U <= v1; v += U) {
+      int c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) c[u] = ghist[(int64_t)(v + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        ghist[(int64_t)(v + u) * E + e] = run;
+        run += c[u];
+      }
+    }
+    for (; v < v1; ++v) {
+      const int c = ghist[(int64_t)v * E + e];
+      ghist[(int64_t)v * E + e] = run;
+      run += c;
+    }
+  }
+  const int total = block_exclusive_scan(offs, E, wave_tmp);   // offs is complete since the barrier above
   if (tid == 0) offs[E] = total;
   __syncthreads();
   for (int e = tid; e <= E; e += blockDim.x) {
@@ -302,8 +363,8 @@ hipError_t launch_route(const int32_t* ids, int T, int K, int E, int32_t* counts
                      ghist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), sizeof(int) * (size_t)(3 * E + 1 + 16), stream, ghist,
-                     nblocks * 4, E, counts, offsets, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b);
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), sizeof(int) * (size_t)(3 * E + 1 + 16 + scan_parts(E) * E),
+                     stream, ghist, nblocks * 4, E, counts, offsets, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_route_scatter, dim3(nblocks), dim3(256), sizeof(int) * 4 * E, stream, ids, (int)S, E,

@@ -62,6 +62,15 @@ SMALL = [
     Workload("ks_c", T=280, H=512, I=1536, E=64, K=8, weight_bits=4, act_int8=True, seed=19),
     Workload("ks_d", T=64, H=2048, I=512, E=16, K=4, weight_bits=8, act_int8=False, seed=20),
     Workload("ks_e", T=96, H=1536, I=1024, E=12, K=3, weight_bits=4, act_int8=False, seed=21),
+    # decode blocks with reductions of 512..2048 (at most 4 rows per expert on
+    # average): the split-reduction decode kernels, in all four modes; a
+    # Zipf-skewed top-1 routing puts more than 8 rows on one expert (several
+    # row tiles)
+    Workload("ksd_a", T=12, H=512, I=512, E=16, K=4, weight_bits=4, act_int8=False, seed=26),
+    Workload("ksd_b", T=20, H=1024, I=1024, E=32, K=4, weight_bits=8, act_int8=True, seed=27),
+    Workload("ksd_c", T=16, H=1536, I=512, E=24, K=6, weight_bits=4, act_int8=True, seed=28),
+    Workload("ksd_d", T=10, H=2048, I=1536, E=12, K=4, weight_bits=8, act_int8=False, seed=29),
+    Workload("ksd_e", T=48, H=512, I=512, E=12, K=1, weight_bits=4, act_int8=False, seed=30, router="zipf"),
     # at least 64 rows per expert on average: the 128-row MFMA tiles (several
     # tiles per expert with ragged tails; a reduction of one group)
     Workload("big_a", T=600, H=256, I=128, E=4, K=2, weight_bits=4, act_int8=False, seed=22),
