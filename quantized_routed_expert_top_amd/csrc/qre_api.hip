@@ -248,11 +248,9 @@ static int moe_forward_impl(const qre_desc* desc, const void* x, const int32_t* 
                                          st.mt_gu, st.bm_gu, L.h);
   const GemmProblem dn = down_problem(d, L.h, L.hq, L.hs, *weights, st.tiles_dn, st.ntiles + 1, st.mt_dn, st.bm_dn,
                                       L.y);
-  // Decode-sized problems: the permutation is folded into the gate/up kernel
-  // (split-reduction kernels where the reductions allow, else row-streaming
-  // ones); otherwise the routing kernel builds it (and the row-tile lists).
-  const bool ks = false && ks_applicable(S, d.E, d.H, d.I);
-  const bool routed = ks || routed_applicable(S, d.E, d.H, d.I, d.act_int8);
+  // Decode-sized problems: the permutation is folded into the gate/up kernel;
+  // otherwise the routing kernel builds it (and the row-tile lists).
+  const bool routed = routed_applicable(S, d.E, d.H, d.I, d.act_int8);
   const RouteOut ro = {topk_ids, (int)S, d.E, L.counts, L.offsets, L.sorted_slot, L.slot_row};
   hipError_t e = mark(0);
   if (e == hipSuccess && !routed)
@@ -260,13 +258,11 @@ static int moe_forward_impl(const qre_desc* desc, const void* x, const int32_t* 
                      st.tiles_gu, st.ntiles, st.bm_gu, st.tiles_dn, st.ntiles + 1, st.bm_dn, s);
   if (e == hipSuccess && d.act_int8) e = launch_quantize_act(static_cast<const uint16_t*>(x), d.T, d.H, L.xq, L.xs, s);
   if (e == hipSuccess) e = mark(1);
-  if (e == hipSuccess)
-    e = ks ? launch_gate_up_ks(gu, ro, s) : routed ? launch_gate_up_routed(gu, ro, s) : launch_gemm(gu, s);
+  if (e == hipSuccess) e = routed ? launch_gate_up_routed(gu, ro, s) : launch_gemm(gu, s);
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess && d.act_int8) e = launch_quantize_act(L.h, (int)S, d.I, L.hq, L.hs, s);
   if (e == hipSuccess) e = mark(3);
-  if (e == hipSuccess)
-    e = ks ? launch_down_ks(dn, ro, s) : routed ? launch_down_routed(dn, ro, s) : launch_gemm(dn, s);
+  if (e == hipSuccess) e = routed ? launch_down_routed(dn, ro, s) : launch_gemm(dn, s);
   if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess) e = launch_combine(L.y, L.slot_row, topk_w, d.T, d.K, d.H, static_cast<uint16_t*>(out), s);
   if (e == hipSuccess) e = mark(5);

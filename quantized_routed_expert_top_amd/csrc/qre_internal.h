@@ -100,15 +100,6 @@ bool routed_applicable(int64_t S, int E, int H, int I, int act_int8);
 hipError_t launch_gate_up_routed(const GemmProblem& p, const RouteOut& ro, hipStream_t stream);
 hipError_t launch_down_routed(const GemmProblem& p, const RouteOut& ro, hipStream_t stream);
 
-// Decode blocks (at most 4 slots per expert on average, within
-// kRoutedMaxSlots) whose reductions are 512..2048 long: one workgroup per
-// (expert, column range), the four waves splitting each block's reduction so
-// the block's weight slice is fetched at once (gemm_dec.hip).  Same outputs
-// as the routed kernels above (gate/up folds in the permutation).
-bool ks_applicable(int64_t S, int E, int H, int I);
-hipError_t launch_gate_up_ks(const GemmProblem& p, const RouteOut& ro, hipStream_t stream);
-hipError_t launch_down_ks(const GemmProblem& p, const RouteOut& ro, hipStream_t stream);
-
 // Combine.
 hipError_t launch_combine(const uint16_t* y, const int32_t* slot_row, const float* topk_w, int T, int K,
                           int H, uint16_t* out, hipStream_t stream);

@@ -54,17 +54,16 @@ SMALL = [
     # more than 2048 slots: the separate routing launch and the row-tile GEMMs
     Workload("small_e", T=300, H=256, I=128, E=16, K=8, weight_bits=4, act_int8=False, seed=15),
     Workload("small_f", T=260, H=384, I=256, E=20, K=8, weight_bits=8, act_int8=True, seed=16),
-    # reductions that are multiples of 512: the split-reduction expert kernels
-    # (permutation folded into gate/up; several 16-row tiles per expert;
-    # more than 2048 slots, after the routing kernel)
+    # reductions that are multiples of 512 (permutation folded into gate/up;
+    # several row tiles per expert; more than 2048 slots, after the routing
+    # kernel)
     Workload("ks_a", T=40, H=512, I=512, E=8, K=2, weight_bits=4, act_int8=False, seed=17),
     Workload("ks_b", T=200, H=1024, I=512, E=8, K=2, weight_bits=8, act_int8=True, seed=18),
     Workload("ks_c", T=280, H=512, I=1536, E=64, K=8, weight_bits=4, act_int8=True, seed=19),
     Workload("ks_d", T=64, H=2048, I=512, E=16, K=4, weight_bits=8, act_int8=False, seed=20),
     Workload("ks_e", T=96, H=1536, I=1024, E=12, K=3, weight_bits=4, act_int8=False, seed=21),
-    # decode blocks with reductions of 512..2048 (at most 4 rows per expert on
-    # average): the split-reduction decode kernels, in all four modes; a
-    # Zipf-skewed top-1 routing puts more than 8 rows on one expert (several
+    # decode blocks (at most 4 rows per expert on average) in all four modes;
+    # a Zipf-skewed top-1 routing puts more than 8 rows on one expert (several
     # row tiles)
     Workload("ksd_a", T=12, H=512, I=512, E=16, K=4, weight_bits=4, act_int8=False, seed=26),
     Workload("ksd_b", T=20, H=1024, I=1024, E=32, K=4, weight_bits=8, act_int8=True, seed=27),
