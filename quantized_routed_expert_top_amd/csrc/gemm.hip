@@ -72,11 +72,8 @@ struct Gemm16 {
   uint32_t w_off[FN];          // byte offset of this lane's weight row in the expert's matrix
   uint32_t s_off[FN];          // byte offset of this lane's scale row
 
-  uint32_t kMaskNib, kMagic;     // 0x000f000f, 0x43004300 in VGPRs
 
   __device__ Gemm16(const GemmProblem& prob, const Tile& td, int col0) : p(prob) {
-    kMaskNib = vconst<0x000f000fu>();
-    kMagic = vconst<0x43004300u>();
     wave = threadIdx.x >> 6;
     lane = threadIdx.x & 63;
     li = lane & 15;
@@ -168,7 +165,7 @@ struct Gemm16 {
       for (int f = 0; f < FN; ++f)
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-          const u32x4_t bv = b_operand_bf16<WB>(bf.b[f][m], t, kMaskNib, kMagic);
+          const u32x4_t bv = b_operand_bf16<WB>(bf.b[f][m], t);
           accg[f][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, __builtin_bit_cast(bf16x8_t, bv), accg[f][m],
                                                                0, 0, 0);
         }
@@ -343,13 +340,19 @@ struct Dec16 {
   static constexpr int BN = 4 * 16 * FN;                    // columns per workgroup
   static_assert(CPR % 8 == 0, "row swizzle needs 8-chunk rows");
 
-  static constexpr size_t lds_bytes() { return (size_t)BMR * ROWB + (A8 ? (size_t)NG * 16 * 4 : 0); }
+  static constexpr int NC = (NG + 3) / 4;                   // 4-group steps of the offset correction
+  // LDS: rows [BMR][ROWB], then [NG][16] FP32: activation scales (INT8) or
+  // row sums of each 128-group (BF16, for the 136 + q / 128 + q offset)
+  static constexpr size_t lds_bytes() { return (size_t)BMR * ROWB + (size_t)NG * 16 * 4; }
 
   struct WBuf {
     u32x4_t b[FN][NM][NB];
   };
 
-  __device__ static uint32_t lds_chunk(int row, int chunk) { return (uint32_t)(row * ROWB + ((chunk ^ (row & 7)) << 4)); }
+  // chunk c of staged row r sits at c ^ swz(r): any 16 aligned consecutive
+  // rows put a chunk in 16 distinct 16-byte bank groups of a 256-byte window
+  __device__ static int swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
+  __device__ static uint32_t lds_chunk(int row, int chunk) { return (uint32_t)(row * ROWB + ((chunk ^ swz(row)) << 4)); }
 
   // Tile: rows [row0, row0 + nrows) (sorted order) of expert e; src(r) gives
   // the A-source row of local row r (a token for gate/up, a sorted row for down).
@@ -400,6 +403,21 @@ struct Dec16 {
         }
       }
     }
+    // BF16: FP32 scales of the lane's column for groups 4i + kb, the B operand
+    // of the offset correction (an FP32 MFMA over groups after the stream)
+    float csc[FN][NM][NC];
+    if constexpr (!A8) {
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int i = 0; i < NC; ++i) {
+            const int g = 4 * i + kb;
+            const uint32_t n = (uint32_t)(col0 + f * 16 + li);
+            csc[f][m][i] = half_bits_to_f32(bload_u16(rs[m], g < NG ? (n * NG + g) * 2 : kOOB));
+          }
+    }
     const int arow = (BMR == 16) ? li : (li & (BMR - 1));   // LDS row feeding MFMA row li
     // the swizzle only touches the low 3 bits of a chunk index and a group
     // spans a multiple of 8 chunks, so every A read is a per-lane base plus a
@@ -408,7 +426,6 @@ struct Dec16 {
 #pragma unroll
     for (int t = 0; t < STEPS; ++t) a_base[t] = lds_chunk(arow, (A8 ? kb * 2 : kb * 4) + t);
 
-    const uint32_t mask_nib = vconst<0x000f000fu>(), magic = vconst<0x43004300u>();
     f32x4_t acc[FN][NM];
 #pragma unroll
     for (int f = 0; f < FN; ++f)
@@ -431,13 +448,25 @@ struct Dec16 {
     }
     // 2. stage the tile's activation rows (and INT8 scales) into LDS
     const uint8_t* a = static_cast<const uint8_t*>(p.a);
+    float* xs_lds = reinterpret_cast<float*>(lds + (size_t)BMR * ROWB);   // [NG][16]
     for (int idx = tid; idx < nrows * CPR; idx += blockDim.x) {
       const int r = idx / CPR, c = idx % CPR;
       const int64_t src = src_row(r);
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a + src * ROWB + c * 16);
       *reinterpret_cast<u32x4_t*>(lds + lds_chunk(r, c)) = a_operand<WB, A8>(v);
+      if constexpr (!A8) {
+        // row sum of the 128-group: 8 values per lane, 16 consecutive lanes
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) t += bf16_bits_to_f32(v[w] & 0xffffu) + bf16_bits_to_f32(v[w] >> 16);
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) t += __shfl_xor(t, d);
+        if ((c & 15) == 0) {
+          xs_lds[(c >> 4) * 16 + r] = t;
+          if (BMR == 8) xs_lds[(c >> 4) * 16 + r + 8] = t;   // MFMA rows 8..15 repeat rows 0..7
+        }
+      }
     }
-    float* xs_lds = reinterpret_cast<float*>(lds + (size_t)BMR * ROWB);   // [NG][16]
     if constexpr (A8) {
       for (int idx = tid; idx < nrows * NG; idx += blockDim.x) {
         const int r = idx / NG, g = idx % NG;
@@ -455,27 +484,20 @@ struct Dec16 {
       const WBuf& bf = buf[g % DEPTH];
       if constexpr (!A8) {
         f32x4_t accg[FN][NM];
-        f32x4_t accx = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int f = 0; f < FN; ++f)
-#pragma unroll
-          for (int m = 0; m < NM; ++m) accg[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const u32x4_t ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0
 #pragma unroll
         for (int t = 0; t < STEPS; ++t) {
           const u32x4_t av = *reinterpret_cast<const u32x4_t*>(lds + a_base[t] + g * 256);
           const bf16x8_t a8 = __builtin_bit_cast(bf16x8_t, av);
-          accx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, __builtin_bit_cast(bf16x8_t, ones), accx, 0, 0, 0);
 #pragma unroll
           for (int f = 0; f < FN; ++f)
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-              const u32x4_t bv = b_operand_bf16<WB>(bf.b[f][m], t, mask_nib, magic);
-              accg[f][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, __builtin_bit_cast(bf16x8_t, bv),
-                                                                   accg[f][m], 0, 0, 0);
+              const u32x4_t bv = b_operand_bf16<WB>(bf.b[f][m], t);
+              accg[f][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  a8, __builtin_bit_cast(bf16x8_t, bv), t == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : accg[f][m], 0, 0, 0);
             }
         }
-        constexpr float kOff = (WB == 4) ? 136.0f : 128.0f;
+        // the offset (136 + q / 128 + q) is removed once, after the stream
 #pragma unroll
         for (int f = 0; f < FN; ++f)
 #pragma unroll
@@ -483,7 +505,7 @@ struct Dec16 {
             const uint32_t word = sc[f][m][g >> 1];
             const float s16 = half_bits_to_f32((g & 1) ? (word >> 16) : (word & 0xffffu));
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[f][m][r] = __builtin_fmaf(s16, accg[f][m][r] - kOff * accx[r], acc[f][m][r]);
+            for (int r = 0; r < 4; ++r) acc[f][m][r] = __builtin_fmaf(s16, accg[f][m][r], acc[f][m][r]);
           }
       } else {
         i32x4_t accg[FN][NM];
@@ -530,7 +552,26 @@ struct Dec16 {
       if (g + DEPTH < NG) load_group(buf[g % DEPTH], g + DEPTH);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // 4. epilogue: lane holds rows 4kb+r of column li of each fragment
+    // 4. BF16: subtract offset * sum_g s[col][g] * rowsum[row][g], an FP32
+    //    MFMA over groups (lane (li, kb) feeds row li / column li, group 4i + kb)
+    if constexpr (!A8) {
+      constexpr float kOff = (WB == 4) ? 136.0f : 128.0f;
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          f32x4_t corr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < NC; ++i) {
+            const int g = 4 * i + kb;
+            const float ra = g < NG ? xs_lds[g * 16 + li] : 0.f;
+            corr = __builtin_amdgcn_mfma_f32_16x16x4f32(ra, csc[f][m][i], corr, 0, 0, 0);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[f][m][r] = __builtin_fmaf(-kOff, corr[r], acc[f][m][r]);
+        }
+    }
+    // 5. epilogue: lane holds rows 4kb+r of column li of each fragment
     uint16_t* out = static_cast<uint16_t*>(p.out);
 #pragma unroll
     for (int f = 0; f < FN; ++f) {

@@ -189,7 +189,6 @@ struct Big {
     uint32_t a_base[STEPS];
 #pragma unroll
     for (int t = 0; t < STEPS; ++t) a_base[t] = lds_chunk(wm * 64 + li, (A8 ? kb * 2 : kb * 4) + t);
-    const uint32_t mask_nib = vconst<0x000f000fu>(), magic = vconst<0x43004300u>();
 
     f32x4_t acc[TM][TN];
 #pragma unroll
@@ -227,7 +226,7 @@ struct Big {
         for (int t = 0; t < STEPS; ++t) {
           u32x4_t bv[TN];
 #pragma unroll
-          for (int j = 0; j < TN; ++j) bv[j] = b_operand_bf16<WB>(wcur.b[j], t, mask_nib, magic);
+          for (int j = 0; j < TN; ++j) bv[j] = b_operand_bf16<WB>(wcur.b[j], t);
 #pragma unroll
           for (int i = 0; i < TM; ++i) {
             const bf16x8_t av =

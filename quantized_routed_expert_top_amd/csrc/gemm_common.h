@@ -48,15 +48,6 @@ __device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
   return __half2float(__ushort_as_half((unsigned short)h));
 }
 
-// A constant materialized in a VGPR: lets (x & M) | C select one v_and_or_b32
-// (a GFX9 VOP3 instruction reads at most one SGPR or literal).
-template <uint32_t C>
-__device__ __forceinline__ uint32_t vconst() {
-  uint32_t v;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "i"(C));
-  return v;
-}
-
 // Two BF16 values (exact small integers held in FP32) packed into one dword.
 __device__ __forceinline__ uint32_t pack_bf16_hi(float lo, float hi) {
   return byte_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
@@ -85,16 +76,21 @@ __device__ __forceinline__ u32x4_t a_operand(u32x4_t c) {
 
 // B operand for BF16 activations, MFMA step t (of 4), from the lane's slice of
 // a 128-group of one weight row (16 bytes INT4 / 32 bytes INT8).  The values
-// are 136 + q (INT4) or 128 + q (INT8), exact in BF16.
+// are 136 + q (INT4) or 128 + q (INT8), exact in BF16.  For INT4 each output
+// word is one three-input logic op (v_bitop3) of the shifted codes: keep the
+// two nibbles, flip their sign bits (q -> q + 8) and set BF16 128.0 around
+// them.
 template <int WB>
-__device__ __forceinline__ u32x4_t b_operand_bf16(const u32x4_t* b, int t, uint32_t mask_nib, uint32_t magic) {
+__device__ __forceinline__ u32x4_t b_operand_bf16(const u32x4_t* b, int t) {
   u32x4_t bv;
   if constexpr (WB == 4) {
-    const uint32_t w = b[0][t] ^ 0x88888888u;             // nibble -> q + 8
-    bv.x = (w & mask_nib) | magic;                        // bf16 (136+q_k, 136+q_{k+4})
-    bv.y = ((w >> 4) & mask_nib) | magic;
-    bv.z = ((w >> 8) & mask_nib) | magic;
-    bv.w = ((w >> 12) & mask_nib) | magic;
+    constexpr uint32_t kKeep = 0x000f000fu, kSet = 0x43084308u;   // 128.0 pair | nibble sign bits
+    auto cvt = [](uint32_t v) { return ((v ^ kSet) & kKeep) | (kSet & ~kKeep); };
+    const uint32_t w = b[0][t];
+    bv.x = cvt(w);                                        // bf16 (136+q_k, 136+q_{k+4})
+    bv.y = cvt(w >> 4);
+    bv.z = cvt(w >> 8);
+    bv.w = cvt(w >> 12);
   } else {
     const uint32_t w0 = b[t >> 1][(t & 1) * 2] ^ 0x80808080u;       // byte -> q + 128
     const uint32_t w1 = b[t >> 1][(t & 1) * 2 + 1] ^ 0x80808080u;
@@ -134,32 +130,37 @@ __device__ __forceinline__ ExpertRows route_expert(const RouteOut& ra, int e, bo
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint64_t below = (1ull << lane) - 1ull;
   constexpr int kSub = kRoutedMaxSlots / 256;              // 64-slot sub-chunks per wave
-  const int L = ((ra.S + 255) / 256) * 64;                  // slots per wave, a multiple of 64
+  const int nsub = (ra.S + 255) / 256;                      // 64-slot sub-chunks per wave (uniform)
+  const int L = nsub * 64;                                  // slots per wave
   const int s0 = min(ra.S, wave * L), s1 = min(ra.S, s0 + L);
-  // all loads first (out-of-range sub-chunks read nothing), then the ballots;
-  // the ballot masks of e's slots stay in registers
+  // all loads first (out-of-range slots read nothing), then the ballots; the
+  // ballot masks of e's slots stay in registers; the ballots of sub-chunks
+  // past nsub are skipped by uniform branches
   const rsrc_t rid = make_rsrc(ra.ids, (int64_t)ra.S * 4);
   int ids[kSub];
+  uint64_t eq[kSub];
 #pragma unroll
   for (int c = 0; c < kSub; ++c) {
     const int s = s0 + c * 64 + lane;
     ids[c] = (int)__builtin_amdgcn_raw_buffer_load_b32(rid, s < s1 ? (uint32_t)s * 4u : kOOB, 0, 0);
+    eq[c] = 0;
   }
-  uint64_t eq[kSub];
   int n_eq = 0, n_lt = 0;
 #pragma unroll
   for (int c = 0; c < kSub; ++c) {
-    const int s = s0 + c * 64 + lane;
-    const int id = s < s1 ? ids[c] : -1;
-    eq[c] = __ballot(id == e);
-    n_eq += __popcll(eq[c]);
-    n_lt += __popcll(__ballot(id >= 0 && id < e));
+    if (c < nsub) {
+      const int s = s0 + c * 64 + lane;
+      const int id = s < s1 ? ids[c] : -1;
+      eq[c] = __ballot(id == e);
+      n_eq += __popcll(eq[c]);
+      n_lt += __popcll(__ballot(id >= 0 && id < e));
+    }
   }
   if (writer && e == 0) {
 #pragma unroll
     for (int c = 0; c < kSub; ++c) {
       const int s = s0 + c * 64 + lane;
-      if (s < s1 && (ids[c] < 0 || ids[c] >= ra.E)) ra.slot_row[s] = -1;      // dropped slot
+      if (c < nsub && s < s1 && (ids[c] < 0 || ids[c] >= ra.E)) ra.slot_row[s] = -1;   // dropped slot
     }
   }
   if (lane == 0) {
@@ -189,6 +190,7 @@ __device__ __forceinline__ ExpertRows route_expert(const RouteOut& ra, int e, bo
     int rank = wbase;
 #pragma unroll
     for (int c = 0; c < kSub; ++c) {
+      if (c >= nsub) break;
       if (eq[c] >> lane & 1ull) {
         const int s = s0 + c * 64 + lane;
         const int j = rank + __popcll(eq[c] & below);
