@@ -30,7 +30,8 @@ BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, published
 I8_PEAK_TOPS = 5000.0
 METRIC = "routed-expert FFN tokens/s; % HBM peak (32-tok block) & % MFMA peak (prefill)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_{}.txt")
-GEMM_SRCS = [os.path.join(ROOT, "quantized_routed_expert_top_amd", "csrc", f) for f in ("gemm.hip", "gemm_common.h")]
+GEMM_SRCS = [os.path.join(ROOT, "quantized_routed_expert_top_amd", "csrc", f)
+             for f in ("gemm.hip", "gemm_big.hip", "gemm_common.h")]
 
 
 def log(*a):
@@ -219,9 +220,9 @@ def main():
     gu_us, dn_us = float(dur[1]), float(dur[3])
     gu_bytes = alg["gate_up_weights"]
     S = wl.T * wl.K
-    if S >= 16 * wl.E * 16:
-        # prefill: on average 256+ rows per expert, the gate/up GEMM is a
-        # dense contraction bound by the matrix cores
+    if S >= 64 * wl.E:
+        # prefill-sized: 64+ rows per expert on average (the 128-row MFMA
+        # tiles); the gate/up GEMM is a dense contraction for the matrix cores
         gu_flops = 2.0 * S * wl.H * 2 * wl.I
         peak = I8_PEAK_TOPS if wl.act_int8 else BF16_PEAK_TFLOPS
         achieved = gu_flops / (gu_us * 1e-6) / 1e12
