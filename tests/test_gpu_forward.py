@@ -70,6 +70,13 @@ SMALL = [
     Workload("ksd_c", T=16, H=1536, I=512, E=24, K=6, weight_bits=4, act_int8=True, seed=28),
     Workload("ksd_d", T=10, H=2048, I=1536, E=12, K=4, weight_bits=8, act_int8=False, seed=29),
     Workload("ksd_e", T=48, H=512, I=512, E=12, K=1, weight_bits=4, act_int8=False, seed=30, router="zipf"),
+    # decode-sized blocks (permutation inside the gate/up kernel) with
+    # reductions of 8/16 groups (gate/up) and 1/2/4 groups (down); one
+    # expert holding all 33 rows (several row tiles); Zipf routing
+    Workload("st_a", T=24, H=1024, I=128, E=8, K=2, weight_bits=4, act_int8=False, seed=31),
+    Workload("st_b", T=30, H=1024, I=256, E=40, K=6, weight_bits=8, act_int8=False, seed=32),
+    Workload("st_c", T=33, H=512, I=128, E=1, K=1, weight_bits=8, act_int8=False, seed=33),
+    Workload("st_d", T=7, H=2048, I=512, E=64, K=8, weight_bits=4, act_int8=False, seed=34, router="zipf"),
     # at least 64 rows per expert on average: the 128-row MFMA tiles (several
     # tiles per expert with ragged tails; a reduction of one group)
     Workload("big_a", T=600, H=256, I=128, E=4, K=2, weight_bits=4, act_int8=False, seed=22),
@@ -131,6 +138,15 @@ def test_edge_cases():
     qre.moe_forward(x_tensor(x_bits, DEV), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), Wg,
                     workspace=ws)
     assert qre.read_dropped_slots(wl.T, wl.H, wl.I, wl.E, wl.K, 4, False, ws) == 3
+    # the same at a reduction of 4 groups, INT8 weights
+    wl_st = Workload("dup_st", T=40, H=512, I=256, E=6, K=3, weight_bits=8, act_int8=False, seed=24)
+    ids_st, w_st = gen_routing(wl_st)
+    ids_st[0, 1] = ids_st[0, 0]
+    ids_st[1, :] = ids_st[1, 0]
+    ids_st[5, 2] = -1
+    ids_st[9, 0] = wl_st.E
+    Wo_st = oracle_experts(wl_st, range(wl_st.E))
+    _check(wl_st, ids=ids_st, w=w_st, Wg=to_gpu_experts(Wo_st, wl_st.weight_bits), Wo=Wo_st)
     # zero tokens: nothing to do, output untouched
     out = torch.full((0, 256), 1.0, dtype=torch.bfloat16, device=DEV)
     qre.moe_forward(torch.empty((0, 256), dtype=torch.bfloat16, device=DEV),
@@ -157,6 +173,7 @@ def test_invariances_decode_shape():
 
 @pytest.mark.parametrize("T,H,I,E,K,bits,a8", [
     (32, 2048, 512, 256, 8, 4, False),     # decode block: permutation computed inside the gate/up kernel
+    (32, 2048, 512, 256, 8, 4, True),      # the same with INT8 activations
     (40, 256, 128, 6, 3, 8, True),
     (300, 256, 128, 16, 8, 4, False),      # > 2048 slots: separate routing launch
     (300, 512, 512, 64, 8, 4, True),       # > 2048 slots, split-reduction expert kernels
