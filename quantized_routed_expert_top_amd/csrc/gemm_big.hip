@@ -333,11 +333,22 @@ struct BigW8A8 {
   static constexpr int HB = kGroup / 2;            // reduction bytes per stage (half a group)
   static constexpr int QA = BM * HB / 16 / 256;    // direct A loads per thread per stage (2)
   static constexpr int QB = BNW * HB / 16 / 256;   // direct B loads per thread per stage (2)
-  static constexpr int B_OFF = BM * HB, X_OFF = B_OFF + BNW * HB, S_OFF = X_OFF + 1024;
-  static constexpr int STAGE = S_OFF + 1024;
+  static constexpr int B_OFF = BM * HB;
+  static constexpr int STAGE = B_OFF + BNW * HB;
   static constexpr int NS = 4;                     // stages; loads run NS - 1 stages ahead
-  static constexpr int VM = QA + QB + 2;           // direct loads per thread per stage
-  static constexpr size_t lds_bytes() { return NS * (size_t)STAGE; }
+  static constexpr int VM = QA + QB;               // direct loads per thread per stage
+  // After the stages, the tile's scales of every group, loaded once: the
+  // activation scales as [group][row] FP32, the weight scales as stored
+  // ([row][group] FP16) in halves of 64 rows (gate, up) or one of 128 rows,
+  // each padded to whole KB; then a 1 KB sink for the loads of waves with
+  // nothing to load.
+  static constexpr int NHALF = DUAL ? 2 : 1;
+  __host__ __device__ static int xs_bytes(int ng) { return ng * BM * 4; }
+  __host__ __device__ static int ws_half(int ng) { return (BNW / NHALF) * ng * 2; }
+  __host__ __device__ static int ws_half_pad(int ng) { return (ws_half(ng) + 1023) / 1024 * 1024; }
+  __host__ __device__ static size_t lds_bytes(int ng) {
+    return NS * (size_t)STAGE + xs_bytes(ng) + NHALF * ws_half_pad(ng) + 1024;
+  }
 
   __device__ static uint32_t chunk_pos(int row, int chunk) {
     return (uint32_t)(row * HB + ((chunk ^ ((row >> 2) & 3)) << 4));
@@ -372,22 +383,40 @@ struct BigW8A8 {
       const int wrow = DUAL ? n0 + (n & 63) : n0 + n;  // DUAL: n < 64 gate (q = 0), else up (q = 1)
       b_off[q] = (uint32_t)(wrow * NG * kGroup) + (uint32_t)(c * 32);
     }
-    const int xrow = (wave & 1) * 64 + lane;
-    const uint32_t x_off = xrow < nrows ? (uint32_t)(src(xrow) * NG * 4) : kOOB;
-    // scale of weight row srow (local), group g: the aligned word at
-    // ((wrow * NG + g) * 2) & ~3 (the FP16 value is its high half when the
-    // element index is odd); a row of scales is 4-byte aligned (n * NG even)
-    const int srow = (wave & 1) * 64 + lane;
-    const int swrow = DUAL ? n0 + (srow & 63) : n0 + srow;
-    const uint32_t s_el = (uint32_t)(swrow * NG);
-    const bool s_up = DUAL && srow >= 64;
-
     auto lds3 = [&](int off) { return (__attribute__((address_space(3))) void*)(lds + off); };
+
+    // the tile's scales of every group (before the first stage's loads, so
+    // the first stage's wait covers them).  Activation scales: load q (of
+    // 2 NG, four bytes a lane) is group q / 2, rows 64 (q % 2) + lane.  Weight
+    // scales: load q of a half copies its bytes [1 KB q, 1 KB q + 1 KB), lanes
+    // past the half's bytes reading zeros into the padding.  Every wave issues
+    // the same number of loads; the spare ones land in the sink.
+    const int XS_OFF = NS * STAGE, WS_OFF = XS_OFF + xs_bytes(NG);
+    const int SINK = WS_OFF + NHALF * ws_half_pad(NG);
+    {
+      const int nx = 2 * NG, nxw = (nx + 3) / 4;
+      for (int k = 0; k < nxw; ++k) {             // uniform
+        const int q = wave + 4 * k;
+        const int r = (q & 1) * 64 + lane;
+        const uint32_t off = q < nx && r < nrows ? (uint32_t)((src(r) * NG + (q >> 1)) * 4) : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lds3(q < nx ? XS_OFF + ((q >> 1) * BM + (q & 1) * 64) * 4 : SINK),
+                                                 4, off, 0, 0, 0);
+      }
+      const int hsz = ws_half(NG), nph = ws_half_pad(NG) / 1024, nw = NHALF * nph, nww = (nw + 3) / 4;
+      for (int k = 0; k < nww; ++k) {             // uniform
+        const int q = wave + 4 * k;
+        const int half = q / nph, b = (q - half * nph) * 1024 + 16 * lane;
+        const uint32_t off = q < nw && b < hsz ? (uint32_t)(n0 * NG * 2 + b) : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(DUAL && half == 1 ? rs1 : rs0,
+                                                 lds3(q < nw ? WS_OFF + half * ws_half_pad(NG) + (q - half * nph) * 1024
+                                                             : SINK),
+                                                 16, off, 0, 0, 0);
+      }
+    }
     // stage loads of half-group h into stage st (h past the end: out-of-range no-ops)
     auto issue = [&](int h, auto stc) {
       constexpr int st = decltype(stc)::value;
       const uint32_t soff = h < NH ? 0u : kOOB;
-      const uint32_t ssoff = (h < NH && (h & 1) == 0) ? 0u : kOOB;   // scales once per group
       const int g = h >> 1, t = h & 1;
       const uint32_t koff = (uint32_t)(g * kGroup + t * 16);
       const int base = st * STAGE;
@@ -399,9 +428,6 @@ struct BigW8A8 {
       for (int q = 0; q < QB; ++q)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(DUAL && q == 1 ? rw1 : rw0, lds3(base + B_OFF + (q * 4 + wave) * 1024),
                                                  16, b_off[q] + koff, soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lds3(base + X_OFF + wave * 256), 4, x_off + g * 4, ssoff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_up ? rs1 : rs0, lds3(base + S_OFF + wave * 256), 4,
-                                               ((s_el + g) * 2) & ~3u, ssoff, 0, 0);
     };
 
     // LDS read bases (row tile and column tile offsets are compile-time constants)
@@ -429,17 +455,20 @@ struct BigW8A8 {
       issue(h + NS - 1, std::integral_constant<int, (st + NS - 1) % NS>{});
       const uint8_t* base = lds + st * STAGE;
       if constexpr (t == 0) {
-        const float* xsl = reinterpret_cast<const float*>(base + X_OFF);
+        // a group past the reduction (the last round's): zero operands, zero scales
+        const bool gin = (h >> 1) < NG;
+        const int g = gin ? h >> 1 : NG - 1;
+        const float* xsl = reinterpret_cast<const float*>(lds + XS_OFF) + g * BM;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) xsr[i] = *reinterpret_cast<const f32x4_t*>(xsl + wm * 64 + i * 16 + 4 * kb);
-        const uint32_t* sl = reinterpret_cast<const uint32_t*>(base + S_OFF);
-        const int g = h >> 1;
+        for (int i = 0; i < TM; ++i)
+          xsr[i] = gin ? *reinterpret_cast<const f32x4_t*>(xsl + wm * 64 + i * 16 + 4 * kb) : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const int nl = (DUAL ? (j >> 1) * 64 + wn * 32 + (j & 1) * 16 : wn * 64 + j * 16) + li;
-          const uint32_t w = sl[nl];
-          const uint32_t el = (uint32_t)((DUAL ? n0 + (nl & 63) : n0 + nl) * NG + g);
-          ws[j] = half_bits_to_f32((el & 1u) ? (w >> 16) : (w & 0xffffu));
+          const int half = DUAL ? (j >> 1) : 0;
+          const int rowh = (DUAL ? wn * 32 + (j & 1) * 16 : wn * 64 + j * 16) + li;
+          const uint16_t w =
+              *reinterpret_cast<const uint16_t*>(lds + WS_OFF + half * ws_half_pad(NG) + (rowh * NG + g) * 2);
+          ws[j] = half_bits_to_f32(w);
         }
       }
       u32x4_t bv[TN];
@@ -537,7 +566,7 @@ hipError_t launch_w8a8_cfg(const GemmProblem& p, hipStream_t stream) {
   using K = BigW8A8<DUAL>;
   if (p.n % K::BNO != 0) return hipErrorInvalidValue;
   const dim3 grid(p.n / K::BNO, (unsigned)((p.max_tiles + 7) / 8 * 8));
-  hipLaunchKernelGGL((k_gemm_w8a8<DUAL>), grid, dim3(256), K::lds_bytes(), stream, p);
+  hipLaunchKernelGGL((k_gemm_w8a8<DUAL>), grid, dim3(256), K::lds_bytes(p.kdim / kGroup), stream, p);
   return hipGetLastError();
 }
 
