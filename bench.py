@@ -30,25 +30,32 @@ BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, published
 I8_PEAK_TOPS = 5000.0
 METRIC = "routed-expert FFN tokens/s; % HBM peak (32-tok block) & % MFMA peak (prefill)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_{}.txt")
-GEMM_SRCS = [os.path.join(ROOT, "quantized_routed_expert_top_amd", "csrc", f)
-             for f in ("gemm.hip", "gemm_big.hip", "gemm_common.h")]
+CSRC = os.path.join(ROOT, "quantized_routed_expert_top_amd", "csrc")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_digest() -> str:
+def gemm_sources(wl) -> list:
+    """Source files of the gate/up kernel a workload runs: the 128-row tile
+    kernels at 64 or more slots per expert, else the per-expert kernels."""
+    big = wl.T * wl.K >= 64 * wl.E
+    return [os.path.join(CSRC, f) for f in (("gemm_big.hip" if big else "gemm.hip"), "gemm_common.h")]
+
+
+def source_digest(wl) -> str:
     h = hashlib.sha256()
-    for path in GEMM_SRCS:
+    for path in gemm_sources(wl):
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
+def read_traffic(wl):
     """HBM bytes per gate/up launch from the committed rocprofv3 counter
     summary, or None if absent or taken on a different kernel source."""
+    workload = wl.name
     path = TRAFFIC_FILE.format(workload)
     if not os.path.exists(path):
         return None
@@ -58,7 +65,7 @@ def read_traffic(workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("gemm_source_sha256") != source_digest():
+    if kv.get("gemm_source_sha256") != source_digest(wl):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -227,13 +234,13 @@ def main():
         peak = I8_PEAK_TOPS if wl.act_int8 else BF16_PEAK_TFLOPS
         achieved = gu_flops / (gu_us * 1e-6) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(achieved / peak, 4), "traffic": read_traffic(wl.name),
+                    "frac": round(achieved / peak, 4), "traffic": read_traffic(wl),
                     "kernel": "fused gate/up + SiLU*mul GEMM", "avg_us": round(gu_us, 2),
                     "alg_flops_per_launch": gu_flops}
     else:
         achieved = gu_bytes / (gu_us * 1e-6) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(wl.name),
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(wl),
                     "kernel": "fused gate/up + SiLU*mul GEMM", "avg_us": round(gu_us, 2),
                     "alg_bytes_per_launch": int(gu_bytes)}
     step_bytes = alg["total"]
