@@ -56,6 +56,8 @@ def lib():
         L.orc_quantize_weights.argtypes = [P, i64, i64, C.c_int, P, P]
         L.orc_unpack_codes.argtypes = [P, i64, i64, C.c_int, P]
         L.orc_dequantize.argtypes = [P, P, i64, i64, C.c_int, P]
+        L.orc_topk_softmax.restype = C.c_int
+        L.orc_topk_softmax.argtypes = [P, i32, i32, i32, P, P]
         L.orc_quantize_act.restype = C.c_int
         L.orc_quantize_act.argtypes = [P, i64, i64, P, P]
         L.orc_route.restype = C.c_int
@@ -181,6 +183,20 @@ def route(topk_ids: np.ndarray, E: int):
     slot_row = np.zeros(S, dtype=np.int32)
     nbad = lib().orc_route(_p(ids), T, K, E, _p(counts), _p(offsets), _p(sorted_slot), _p(slot_row))
     return counts, offsets, sorted_slot, slot_row, nbad
+
+
+def topk_softmax(logits: np.ndarray, K: int):
+    """logits float32 [T, E] -> (ids int32 [T, K], w float32 [T, K]): the K
+    largest logits per token in descending order, ties to the lower id, and a
+    softmax over them (double inside, one rounding to float32)."""
+    lg = _c(logits, np.float32)
+    T, E = lg.shape
+    ids = np.zeros((T, K), dtype=np.int32)
+    w = np.zeros((T, K), dtype=np.float32)
+    rc = lib().orc_topk_softmax(_p(lg), T, E, K, _p(ids), _p(w))
+    if rc != 0:
+        raise ValueError(f"orc_topk_softmax: {rc}")
+    return ids, w
 
 
 # ---- expert feed-forward -------------------------------------------------------

@@ -510,6 +510,46 @@ int orc_moe_forward(const orc_shape* d, const uint16_t* x, const int32_t* ids, c
     return rc == 0 ? nbad : rc;
 }
 
+/* Router ahead of the permutation: per token, the K experts with the largest
+ * logits, in descending order of logit, ties going to the lower expert id,
+ * and their combine weights, a softmax over the K selected logits with the
+ * largest one subtracted.  The README's "Quantization" section puts the
+ * routing of decode blocks on the GPU and the model card ("Checkpoints and
+ * precision", paragraph under the heading about routed experts) keeps the
+ * router in floating point; the selection and weighting rule itself is not
+ * on the pages: this is the plain top-K softmax reading.  Selection is K
+ * passes of a linear scan (strict comparison, so the first, lowest, id wins a
+ * tie); exponentials and the normalising sum are taken in double and each
+ * weight is rounded once to FP32.  Requires 1 <= K <= E; returns -1 otherwise.
+ * Non-finite logits give unspecified results. */
+int orc_topk_softmax(const float* logits, int32_t T, int32_t E, int32_t K, int32_t* ids, float* w)
+{
+    if (K < 1 || K > E) return -1;
+    uint8_t* taken = (uint8_t*)malloc((size_t)E);
+    double* z = (double*)malloc(sizeof(double) * (size_t)K);
+    for (int64_t t = 0; t < T; ++t) {
+        const float* l = logits + t * E;
+        memset(taken, 0, (size_t)E);
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t best = -1;
+            for (int32_t e = 0; e < E; ++e)
+                if (!taken[e] && (best < 0 || l[e] > l[best])) best = e;
+            taken[best] = 1;
+            ids[t * K + k] = best;
+        }
+        const double m = (double)l[ids[t * K]];
+        double sum = 0.0;
+        for (int32_t k = 0; k < K; ++k) {
+            z[k] = exp((double)l[ids[t * K + k]] - m);
+            sum += z[k];
+        }
+        for (int32_t k = 0; k < K; ++k) w[t * K + k] = (float)(z[k] / sum);
+    }
+    free(taken);
+    free(z);
+    return 0;
+}
+
 int orc_num_threads(void)
 {
 #ifdef _OPENMP
