@@ -130,6 +130,78 @@ def cpu_baseline(wl, x_bits, ids, w, budget_s=12.0):
             "kind": "oracle", "sample": f"{sample}, {runs} run(s), {t_total:.1f} s"}
 
 
+def router_bench(args, wl):
+    """--stage router: the router kernel alone (top-K + softmax over the
+    workload's synthetic logits), replayed from a HIP graph; one JSON line."""
+    import numpy as np
+    import torch
+    import quantized_routed_expert_top_amd as qre
+    from quantized_routed_expert_top_amd.inputs import gen_router_logits
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    logits_np = gen_router_logits(wl)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        lg = torch.from_numpy(logits_np).to(dev)
+        ids, w = qre.topk_softmax(lg, wl.K)
+        for _ in range(args.warmup):
+            qre.topk_softmax(lg, wl.K)
+        torch.cuda.synchronize()
+        ids_eager, w_eager = ids.clone(), w.clone()
+        g = torch.cuda.CUDAGraph()
+        outs = {}
+        with torch.cuda.graph(g, stream=stream):
+            outs["ids"], outs["w"] = qre.topk_softmax(lg, wl.K)
+        g.replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(outs["ids"], ids_eager) and torch.equal(outs["w"], w_eager)):
+            raise RuntimeError("graph replay differs from eager router output")
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        # kernel duration: events around single eager launches on the same stream
+        nk = max(20, min(args.steps, 200))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nk)]
+        for a, b in evs:
+            a.record(stream)
+            qre.topk_softmax(lg, wl.K)
+            b.record(stream)
+        torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs[2:]])) * 1e3
+    nbytes = wl.T * wl.E * 4 + wl.T * wl.K * 8
+    achieved = nbytes / (us * 1e-6) / 1e9
+    result = {
+        "metric": "router tokens/s (top-K selection + softmax weights)",
+        "value": round(wl.T * args.steps / wall, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"router_{wl.name}", "T": wl.T, "E": wl.E, "K": wl.K, "launch": "hipGraph replay"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None, "kernel": "k_topk_softmax",
+                     "avg_us": round(us, 2), "alg_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        log("[bench] timing the CPU oracle router")
+        runs, t_total = 0, 0.0
+        while runs == 0 or t_total < 5.0:
+            t1 = time.perf_counter()
+            oracle.topk_softmax(logits_np, wl.K)
+            t_total += time.perf_counter() - t1
+            runs += 1
+        result["cpu_baseline"] = {"value": round(runs * wl.T / t_total, 1), "unit": "tokens/s", "cores": 1,
+                                  "kind": "oracle", "sample": f"whole batch of {wl.T} tokens, {runs} run(s), "
+                                                              f"{t_total:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,6 +211,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough for >= 1 GiB)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage", choices=["ffn", "router"], default="ffn",
+                    help="ffn: the whole feed-forward (default); router: the top-K + softmax router alone")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration under rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -155,6 +229,8 @@ def main():
     from quantized_routed_expert_top_amd.synthetic import algorithmic_bytes, gpu_problem
 
     wl = WORKLOADS[args.workload]
+    if args.stage == "router":
+        return router_bench(args, wl)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"[bench] workload {wl.name}: generating and quantizing weights on the GPU")

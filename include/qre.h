@@ -195,6 +195,24 @@ int qre_stage_workspace_bytes(const qre_desc* desc, size_t* bytes);
 int qre_combine(const void* y, const int32_t* slot_row, const float* topk_w, int32_t T, int32_t K,
                 int32_t H, void* out, qre_stream_t stream);
 
+/* Router ahead of the permutation (minnow README, "Quantization": routing of
+ * decode blocks runs on the GPU; LLaDA2.2-flash model card, "Checkpoints and
+ * precision": routers keep floating-point weights).  The rule is the plain
+ * top-K softmax: for each token t, topk_ids[t][0..K) are the K experts with
+ * the largest logits[t][e], in descending order of logit, equal logits going
+ * to the lower id; topk_w[t][k] = exp(l_k - l_0) / sum_j exp(l_j - l_0) over
+ * the K selected logits, in FP32 (expf, a fixed-order sum, IEEE division).
+ * logits fp32 [T][E], topk_ids int32 [T][K], topk_w fp32 [T][K], all device
+ * memory owned by the caller; the outputs are exactly what qre_moe_forward
+ * takes.  1 <= K <= E (QRE_ERR_SHAPE), E <= QRE_ROUTER_MAX_EXPERTS and
+ * K <= QRE_ROUTER_MAX_K (QRE_ERR_LIMIT); T == 0 is a no-op.  -0 and +0 count
+ * as equal; NaN or infinite logits give unspecified results (ids stay in
+ * [0, E) and distinct). */
+#define QRE_ROUTER_MAX_EXPERTS 1024
+#define QRE_ROUTER_MAX_K 64
+int qre_topk_softmax(const float* logits, int32_t T, int32_t E, int32_t K, int32_t* topk_ids, float* topk_w,
+                     qre_stream_t stream);
+
 /* Weight conversion (minnow README, "Quantization": convert --experts
  * int4|int8): w fp32 [rows][cols] -> q [rows][cols*bits/8] bytes in the packed
  * layout above and s fp16 [rows][cols/128] with s = fp16(max|w| / qmax),

@@ -69,6 +69,7 @@ def _lib():
         L.qre_gate_up.argtypes = [P, P, P, P, P, P, P, P, sz, P]
         L.qre_down.argtypes = [P, P, P, P, P, P, P, sz, P]
         L.qre_combine.argtypes = [P, P, P, i32, i32, i32, P, P]
+        L.qre_topk_softmax.argtypes = [P, i32, i32, i32, P, P, P]
         L.qre_quantize_weights.argtypes = [P, i64, i64, i32, P, P, P]
         _L = L
     return _L
@@ -371,6 +372,18 @@ def down(h, W: QuantizedExperts, T, K, workspace, act_int8=False, hq=None, hs=No
     _check("qre_down", _lib().qre_down(C.byref(d), _ptr(h), _ptr(hq), _ptr(hs), C.byref(ws_struct), _ptr(y),
                                        _ptr(workspace), workspace.numel(), _stream()))
     return y
+
+
+def topk_softmax(logits, K):
+    """logits[T, E] fp32 -> (topk_ids int32 [T, K], topk_w fp32 [T, K]): the K
+    largest logits per token (descending, ties to the lower id) and a softmax
+    over them, computed by the library's router kernel."""
+    T, E = logits.shape
+    _need(logits, "logits", torch.float32, (T, E))
+    ids = torch.empty((T, K), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, K), dtype=torch.float32, device=logits.device)
+    _check("qre_topk_softmax", _lib().qre_topk_softmax(_ptr(logits), T, E, K, _ptr(ids), _ptr(w), _stream()))
+    return ids, w
 
 
 def combine(y, slot_row, topk_w, out=None):

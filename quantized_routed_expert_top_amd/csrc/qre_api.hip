@@ -435,4 +435,14 @@ int qre_combine(const void* y, const int32_t* slot_row, const float* topk_w, int
                                    static_cast<uint16_t*>(out), reinterpret_cast<hipStream_t>(stream)));
 }
 
+int qre_topk_softmax(const float* logits, int32_t T, int32_t E, int32_t K, int32_t* topk_ids, float* topk_w,
+                     qre_stream_t stream) {
+  if (T < 0 || E < 1 || K < 1 || K > E) return QRE_ERR_SHAPE;
+  if (E > QRE_ROUTER_MAX_EXPERTS || K > QRE_ROUTER_MAX_K || (int64_t)T * E >= (1ll << 31)) return QRE_ERR_LIMIT;
+  if (T == 0) return QRE_OK;
+  if (!logits || !topk_ids || !topk_w) return QRE_ERR_NULL;
+  if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w)) return QRE_ERR_ALIGN;
+  return hip_status(launch_topk_softmax(logits, T, E, K, topk_ids, topk_w, reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -104,4 +104,8 @@ hipError_t launch_down_routed(const GemmProblem& p, const RouteOut& ro, hipStrea
 hipError_t launch_combine(const uint16_t* y, const int32_t* slot_row, const float* topk_w, int T, int K,
                           int H, uint16_t* out, hipStream_t stream);
 
+// Router: top-K of E logits per token (one wave per token), softmax weights.
+hipError_t launch_topk_softmax(const float* logits, int T, int E, int K, int32_t* ids, float* w,
+                               hipStream_t stream);
+
 }  // namespace qre

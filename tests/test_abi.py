@@ -85,6 +85,14 @@ def test_forward_argument_errors_need_no_gpu():
     assert L.qre_combine(P(16), P(16), P(16), 4, 2, 100, P(16), None) == -2
     assert L.qre_gate_up(C.byref(_desc(act_int8=1)), P(16), None, None, P(16), C.byref(w), P(16), P(16),
                          1 << 24, None) == -8
+    # router: K > E, limits, null, misaligned, empty
+    assert L.qre_topk_softmax(P(16), 4, 8, 9, P(16), P(16), None) == -2
+    assert L.qre_topk_softmax(P(16), 4, 8, 0, P(16), P(16), None) == -2
+    assert L.qre_topk_softmax(P(16), 4, 2048, 8, P(16), P(16), None) == -9
+    assert L.qre_topk_softmax(P(16), 4, 128, 65, P(16), P(16), None) == -9
+    assert L.qre_topk_softmax(None, 4, 256, 8, P(16), P(16), None) == -1
+    assert L.qre_topk_softmax(P(16), 4, 256, 8, P(20), P(16), None) == -5
+    assert L.qre_topk_softmax(None, 0, 256, 8, None, None, None) == 0
     d8k = _desc(T=8192)
     assert L.qre_route(C.byref(d8k), P(16), P(16), P(16), P(16), P(16), None, 0, None) == -1   # needs workspace
     n = C.c_size_t(0)
