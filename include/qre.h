@@ -24,8 +24,9 @@
  * Conventions shared by every entry point
  *  - Every pointer argument is a DEVICE pointer owned by the caller unless the
  *    comment says "host".  The library never allocates, frees or retains
- *    memory, keeps no mutable global state, and may be called from several
- *    threads on different streams.
+ *    memory, keeps no mutable global state (only a per-thread copy of the
+ *    last HIP error code, see qre_last_hip_error), and may be called from
+ *    several threads on different streams.
  *  - Work is enqueued on `stream` and the call returns without synchronizing,
  *    except qre_read_dropped_slots, which synchronizes `stream`.
  *  - Arguments are validated on the host before anything is enqueued.  On any

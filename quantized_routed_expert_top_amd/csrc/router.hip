@@ -65,10 +65,12 @@ __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ 
   const float* row = logits + (int64_t)t * E;
   const float kNaN = __int_as_float(0x7fc00000);
   float v[NV];
+  uint32_t taken = 0;                                     // bit j: slot j taken or past E
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int e = lane + 64 * j;
     v[j] = e < E ? row[e] : kNaN;
+    taken |= e < E ? 0u : 1u << j;
   }
   float mv = 0.0f;                                        // lane k: round k's value and id
   int mid = 0;
@@ -86,9 +88,24 @@ __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ 
         L = __builtin_ctzll(hit);
       }
     }
+    if (J < 0) {
+      // every remaining value is NaN (unspecified input): take the lowest
+      // id not yet taken, so the ids stay distinct and inside [0, E)
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const uint64_t free_ = __ballot(!((taken >> j) & 1u));
+        if (J < 0 && free_) {
+          J = j;
+          L = __builtin_ctzll(free_);
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < NV; ++j)
-      if (j == J && lane == L) v[j] = kNaN;
+      if (j == J && lane == L) {
+        v[j] = kNaN;
+        taken |= 1u << j;
+      }
     if (lane == k) {
       mv = m;
       mid = 64 * J + L;

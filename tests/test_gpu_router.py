@@ -90,3 +90,23 @@ def test_router_feeds_forward():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
     assert_parity(bf16_np(out), ref32, what="router_ffn")
+
+
+def test_router_non_finite_logits_keep_ids_valid():
+    """NaN and infinite logits are unspecified input for the weights, but the
+    ids must stay distinct and inside [0, E) (the header's guarantee)."""
+    rng = np.random.default_rng(13)
+    T, E, K = 16, 100, 8
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    l[0, :] = np.nan                                    # every logit NaN
+    l[1, : E - 3] = np.nan                              # fewer finite logits than K
+    l[2, 5] = np.inf
+    l[3, :] = -np.inf
+    ids, _ = qre.topk_softmax(torch.from_numpy(l).to(DEV), K)
+    ids = ids.cpu().numpy()
+    assert ids.min() >= 0 and ids.max() < E
+    for t in range(T):
+        assert len(set(ids[t].tolist())) == K
+    assert set(ids[1, :3].tolist()) == {E - 3, E - 2, E - 1}   # the finite ones first
+    assert ids[2, 0] == 5
+    assert list(ids[3]) == list(range(K))                # all equal (-inf): lowest ids
