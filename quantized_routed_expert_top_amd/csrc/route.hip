@@ -11,7 +11,9 @@
 //    the group's size to the wave's per-expert count, and a lane's rank inside
 //    its group is the popcount of the group mask below it;
 //  * an exclusive scan over (expert-major, wave-minor) counts gives every wave
-//    its first output position per expert;
+//    its first output position per expert (in the three-kernel path: a prefix
+//    over the waves per expert, parallel over experts, then each scatter
+//    workgroup scans the E totals itself);
 //  * the scatter pass re-walks the chunk in the same order, so equal ids keep
 //    ascending slot order.
 // Small problems (S <= kSmallMax) do all of it in one workgroup with the
@@ -27,8 +29,6 @@ constexpr int kBatch = 4;         // 64-slot rows whose id loads are issued toge
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-// Partitions of the wave range per expert in the scan kernel (1024 threads).
-__host__ __device__ constexpr int scan_parts(int E) { return E >= 1024 ? 1 : (1024 / E > 16 ? 16 : 1024 / E); }
 
 // Mask of the lanes whose key equals this lane's key (keys < 2^nbits).
 // Must be called by all 64 lanes.
@@ -207,27 +207,21 @@ __global__ __launch_bounds__(256) void k_route_count(const int32_t* __restrict__
   for (int e = lane_id(); e < E; e += kWave) ghist[gw * E + e] = row[e];
 }
 
-// Per-expert prefix over the waves' counts.  The wave range is cut into NP
-// partitions per expert (NP * E threads' worth of independent loads): pass 1
-// sums each partition, the partition sums are scanned per expert, pass 2
-// writes every wave's base.  LDS: cnt[E], offs[E+1], scratch[E], wave_tmp[16],
-// part[NP][E].
-__global__ __launch_bounds__(1024) void k_route_scan(int32_t* ghist, int nwaves, int E, int32_t* counts,
-                                                     int32_t* offsets, Tile* tiles_a, int32_t* ntiles_a, int bm_a,
-                                                     Tile* tiles_b, int32_t* ntiles_b, int bm_b) {
-  extern __shared__ int lds[];
-  int* cnt = lds;                  // [E]
-  int* offs = cnt + E;             // [E+1]
-  int* scratch = offs + E + 1;     // [E]
-  int* wave_tmp = scratch + E;     // [16]
-  int* part = wave_tmp + 16;       // [NP][E]
-  const int NP = scan_parts(E);
-  const int tid = threadIdx.x;
-  constexpr int U = 32;            // loads in flight per thread
-  for (int i = tid; i < NP * E; i += blockDim.x) {
-    const int e = i % E, q = i / E;
-    const int v0 = (int)((int64_t)q * nwaves / NP), v1 = (int)((int64_t)(q + 1) * nwaves / NP);
-    int sum = 0;
+// Per-expert prefix over the waves' counts, relative to the expert's first
+// sorted row, and the per-expert totals.  Experts are independent, so a
+// workgroup takes kPxE of them: thread (el, q) walks partition q of the wave
+// range for expert el (consecutive el read consecutive ints), pass 1 sums the
+// partition, the partition sums are scanned in LDS, pass 2 rewrites the counts
+// as bases.
+constexpr int kPxE = 32, kPxP = 8;   // experts x partitions = 256 threads
+__global__ __launch_bounds__(256) void k_route_prefix(int32_t* ghist, int nwaves, int E, int32_t* counts) {
+  __shared__ int part[kPxP][kPxE];
+  const int el = threadIdx.x % kPxE, q = threadIdx.x / kPxE;
+  const int e = blockIdx.x * kPxE + el;
+  const int v0 = (int)((int64_t)q * nwaves / kPxP), v1 = (int)((int64_t)(q + 1) * nwaves / kPxP);
+  constexpr int U = 16;            // loads in flight per thread
+  int sum = 0;
+  if (e < E) {
     int v = v0;
     for (; v + U <= v1; v += U) {
       int c[U];
@@ -237,24 +231,12 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* ghist, int nwaves,
       for (int u = 0; u < U; ++u) sum += c[u];
     }
     for (; v < v1; ++v) sum += ghist[(int64_t)v * E + e];
-    part[q * E + e] = sum;
   }
+  part[q][el] = sum;
   __syncthreads();
-  for (int e = tid; e < E; e += blockDim.x) {
-    int run = 0;
-    for (int q = 0; q < NP; ++q) {
-      const int c = part[q * E + e];
-      part[q * E + e] = run;
-      run += c;
-    }
-    cnt[e] = run;
-    offs[e] = run;
-  }
-  __syncthreads();
-  for (int i = tid; i < NP * E; i += blockDim.x) {
-    const int e = i % E, q = i / E;
-    const int v0 = (int)((int64_t)q * nwaves / NP), v1 = (int)((int64_t)(q + 1) * nwaves / NP);
-    int run = part[q * E + e];
+  int run = 0;
+  for (int j = 0; j < q; ++j) run += part[j][el];
+  if (e < E) {
     int v = v0;
     for (; v + U <= v1; v += U) {
       int c[U];
@@ -271,29 +253,45 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* ghist, int nwaves,
       ghist[(int64_t)v * E + e] = run;
       run += c;
     }
+    if (q == kPxP - 1) counts[e] = run;
   }
-  const int total = block_exclusive_scan(offs, E, wave_tmp);   // offs is complete since the barrier above
-  if (tid == 0) offs[E] = total;
-  __syncthreads();
-  for (int e = tid; e <= E; e += blockDim.x) {
-    offsets[e] = offs[e];
-    if (e < E) counts[e] = cnt[e];
-  }
-  if (tiles_a) build_tiles(cnt, offs, E, bm_a, scratch, wave_tmp, tiles_a, ntiles_a);
-  if (tiles_b) build_tiles(cnt, offs, E, bm_b, scratch, wave_tmp, tiles_b, ntiles_b);
 }
 
+// Each workgroup scans the per-expert counts itself (E values); workgroup 0
+// also writes offsets and the row-tile lists.  Then every wave scatters its
+// chunk from its bases.  LDS: rows[4][E], cnt[E], offs[E+1], scratch[E],
+// wave_tmp[4].
 __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict__ ids, int S, int E, int nbits,
-                                                       const int32_t* ghist, const int32_t* offsets,
-                                                       int32_t* sorted_slot, int32_t* slot_row) {
+                                                       const int32_t* ghist, const int32_t* counts, int32_t* offsets,
+                                                       Tile* tiles_a, int32_t* ntiles_a, int bm_a, Tile* tiles_b,
+                                                       int32_t* ntiles_b, int bm_b, int32_t* sorted_slot,
+                                                       int32_t* slot_row) {
   extern __shared__ int lds[];
-  const int w = threadIdx.x / kWave;
-  int* row = lds + w * E;
+  int* rows = lds;                 // [4][E]
+  int* cnt = rows + 4 * E;         // [E]
+  int* offs = cnt + E;             // [E+1]
+  int* scratch = offs + E + 1;     // [E]
+  int* wave_tmp = scratch + E;     // [4]
+  const int tid = threadIdx.x, w = tid / kWave;
+  for (int e = tid; e < E; e += blockDim.x) {
+    const int c = counts[e];
+    cnt[e] = c;
+    offs[e] = c;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(offs, E, wave_tmp);
+  if (tid == 0) offs[E] = total;
+  __syncthreads();
+  if (blockIdx.x == 0) {           // uniform over the workgroup
+    for (int e = tid; e <= E; e += blockDim.x) offsets[e] = offs[e];
+    if (tiles_a) build_tiles(cnt, offs, E, bm_a, scratch, wave_tmp, tiles_a, ntiles_a);
+    if (tiles_b) build_tiles(cnt, offs, E, bm_b, scratch, wave_tmp, tiles_b, ntiles_b);
+  }
+  int* row = rows + w * E;
   const int64_t gw = (int64_t)blockIdx.x * 4 + w;
-  for (int e = lane_id(); e < E; e += kWave) row[e] = ghist[gw * E + e] + offsets[e];
+  for (int e = lane_id(); e < E; e += kWave) row[e] = ghist[gw * E + e] + offs[e];
   const int64_t c0 = min((int64_t)S, gw * kLargeChunk), c1 = min((int64_t)S, c0 + kLargeChunk);
   wave_scatter(ids, c0, c1, E, nbits, row, sorted_slot, slot_row);
-  const int total = offsets[E];
   for (int64_t i = total + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < S;
        i += (int64_t)gridDim.x * blockDim.x)
     sorted_slot[i] = -1;
@@ -363,12 +361,13 @@ hipError_t launch_route(const int32_t* ids, int T, int K, int E, int32_t* counts
                      ghist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), sizeof(int) * (size_t)(3 * E + 1 + 16 + scan_parts(E) * E),
-                     stream, ghist, nblocks * 4, E, counts, offsets, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b);
+  hipLaunchKernelGGL(k_route_prefix, dim3((unsigned)((E + kPxE - 1) / kPxE)), dim3(256), 0, stream, ghist, nblocks * 4, E,
+                     counts);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_route_scatter, dim3(nblocks), dim3(256), sizeof(int) * 4 * E, stream, ids, (int)S, E,
-                     nbits, ghist, offsets, sorted_slot, slot_row);
+  hipLaunchKernelGGL(k_route_scatter, dim3(nblocks), dim3(256), sizeof(int) * (size_t)(7 * E + 5), stream, ids,
+                     (int)S, E, nbits, ghist, counts, offsets, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b,
+                     sorted_slot, slot_row);
   return hipGetLastError();
 }
 
