@@ -218,7 +218,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): this build has no "
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): the library has no "
               f"multi-GPU path; the per-GPU kernel is what it measures.", file=sys.stderr)
         sys.exit(2)
 

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void k_topk_softmax(const float* __restrict__ 
       mid = 64 * J + L;
     }
   }
-  // softmax over the selected: round 0 holds the largest logit
+  // softmax over the selected: the first selection holds the largest logit
   const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mv), 0));
   const bool live = lane < K;
   const float z = live ? expf(mv - m0) : 0.0f;
