@@ -48,11 +48,32 @@ __global__ __launch_bounds__(256) void k_quantize_act(const uint16_t* __restrict
   for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
   m = seg16_max(m);
   const float sc = m / 127.0f;
+  // q = rint(x / sc) with x / sc rounded to FP32 first, as defined.  Fast
+  // form: y = x * r with r = 1 / sc, both rounded to FP32, so
+  // |y - x / sc| <= 3 * 2^-24 * |x / sc| <= 2.3e-5 for |x / sc| <= 127, and
+  // the FP32 quotient is as close; when y is more than kMargin from every
+  // half-integer, rint(y) is the rint of the quotient.  Otherwise (rare), and
+  // for non-finite y, the quotient itself is taken.
+  constexpr float kMargin = 0x1p-14f;
+  const bool zero = !(sc != 0.0f);
+  const float r = 1.0f / (zero ? 1.0f : sc);
+  float qf[8];
+  uint32_t need = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float y = x[j] * r;
+    qf[j] = rintf(y);
+    need |= (fabsf(y - qf[j]) <= 0.5f - kMargin) ? 0u : 1u << j;
+  }
+  if (need != 0u && !zero) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if ((need >> j) & 1u) qf[j] = rintf(x[j] / sc);
+  }
   uint32_t packed[2] = {0u, 0u};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    int qv = 0;
-    if (sc != 0.0f) qv = (int)fminf(127.0f, fmaxf(-127.0f, rintf(x[j] / sc)));
+    const int qv = zero ? 0 : (int)fminf(127.0f, fmaxf(-127.0f, qf[j]));
     packed[j / 4] |= (uint32_t)(qv & 0xff) << (8 * (j % 4));
   }
   *reinterpret_cast<uint2*>(q + off) = make_uint2(packed[0], packed[1]);

@@ -64,6 +64,11 @@ def test_quantize_act_bit_exact(rows, cols):
     v[0, :128] = 0.0
     if rows > 2:
         v[2, :128] = np.array([127.0, 2.5, 3.5, -0.5, 126.5, -2.5, 1.5] + [0.0] * 121) * 2.0 ** -3
+    if rows > 4:
+        # subnormal BF16 inputs (1 / scale overflows: every element takes the
+        # exact quotient) and very large ones
+        v[3, :128] = rng.standard_normal(128) * 1e-39
+        v[4, 128:256] = rng.standard_normal(128) * 1e37
     vb = f32_to_bf16_bits(v)
     q, s = oracle.quantize_act(vb)
     gq, gs = qre.quantize_act(torch.from_numpy(vb.view(np.int16)).to(DEV).view(torch.bfloat16))
