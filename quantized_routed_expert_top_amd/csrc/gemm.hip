@@ -709,9 +709,14 @@ template <int WB, bool A8, bool DUAL, int NG, int BMR>
 hipError_t launch_dec_ng(const GemmProblem& p, hipStream_t stream) {
   // the fused gate/up GEMM streams two matrices per column, so one 16-column
   // fragment per wave; the down GEMM streams one, so two.  DEPTH groups of
-  // weight loads in flight (64 VGPRs of INT4 / 128 of INT8 per wave).
-  constexpr int FN = DUAL ? 1 : 2;
-  constexpr int DEPTH = (NG < 8) ? NG : 8;
+  // weight loads in flight (64 VGPRs of INT4 / 128 of INT8 per wave).  With
+  // 16-row tiles the staged rows already limit LDS to two workgroups per CU,
+  // so the gate/up waves take two fragments each (twice the columns per
+  // staged tile, more weight bytes in flight), with a shallower look-ahead
+  // that keeps two waves per SIMD.
+  constexpr int FN = DUAL ? (BMR == 16 ? 2 : 1) : 2;
+  constexpr int DMAX = (DUAL && BMR == 16) ? (WB == 8 ? 3 : 6) : 8;
+  constexpr int DEPTH = (NG < DMAX) ? NG : DMAX;
   return launch_dec<WB, A8, DUAL, FN, NG, DEPTH, BMR>(p, stream);
 }
 
