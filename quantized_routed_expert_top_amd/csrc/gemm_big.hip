@@ -317,14 +317,14 @@ struct Big {
 // (64 reduction bytes of 128 rows and of 128 weight rows), four stages, loads
 // issued three half-groups ahead.  A direct load writes lane L's 16 bytes at
 // base + 16 L, so each lane fetches the chunk that belongs at its position:
-// row r keeps its four chunks at positions c ^ ((r >> 2) & 3), which makes
-// the operand reads (16 rows x one chunk per 16 lanes) conflict-free.  Each
-// stage also holds the activation scales (each wave loads 64 into its own
-// 256-byte window; windows 2 and 3 repeat 0 and 1) and the weight scales (one
-// aligned 32-bit word per weight row holding its FP16 scale), loaded with the
-// first half of a group; the second half's scale loads are out-of-range
-// no-ops.  Every stage issues the same six direct loads and nothing else, so
-// one static vmcnt fits all and no register waits on a load in flight.
+// row r keeps its four chunks at positions c ^ ((r >> 1) & 3).  Rows are 64
+// bytes apart, so any 8 consecutive rows then put a given chunk in 8 distinct
+// 16-byte slots of a 128-byte window and the operand reads (16 rows x one
+// chunk per 16 lanes) are free of bank conflicts.  The tile's activation and
+// weight scales of every group are loaded once, before the first stage, into
+// their own LDS region.  Every stage issues the same four direct loads per
+// thread and nothing else, so one static vmcnt fits all and no register waits
+// on a load in flight.
 template <bool DUAL>
 struct BigW8A8 {
   static constexpr int BM = 128, BNW = 128;
@@ -351,7 +351,7 @@ struct BigW8A8 {
   }
 
   __device__ static uint32_t chunk_pos(int row, int chunk) {
-    return (uint32_t)(row * HB + ((chunk ^ ((row >> 2) & 3)) << 4));
+    return (uint32_t)(row * HB + ((chunk ^ ((row >> 1) & 3)) << 4));
   }
 
   template <class RowSrc>
@@ -374,12 +374,12 @@ struct BigW8A8 {
     uint32_t a_off[QA], b_off[QB];
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
-      const int P = (q * 4 + wave) * 64 + lane, row = P >> 2, c = (P & 3) ^ ((row >> 2) & 3);
+      const int P = (q * 4 + wave) * 64 + lane, row = P >> 2, c = (P & 3) ^ ((row >> 1) & 3);
       a_off[q] = row < nrows ? (uint32_t)(src(row) * NG * kGroup) + (uint32_t)(c * 32) : kOOB;
     }
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
-      const int P = (q * 4 + wave) * 64 + lane, n = P >> 2, c = (P & 3) ^ ((n >> 2) & 3);
+      const int P = (q * 4 + wave) * 64 + lane, n = P >> 2, c = (P & 3) ^ ((n >> 1) & 3);
       const int wrow = DUAL ? n0 + (n & 63) : n0 + n;  // DUAL: n < 64 gate (q = 0), else up (q = 1)
       b_off[q] = (uint32_t)(wrow * NG * kGroup) + (uint32_t)(c * 32);
     }
