@@ -62,6 +62,11 @@ SMALL = [
     Workload("ks_c", T=280, H=512, I=1536, E=64, K=8, weight_bits=4, act_int8=True, seed=19),
     Workload("ks_d", T=64, H=2048, I=512, E=16, K=4, weight_bits=8, act_int8=False, seed=20),
     Workload("ks_e", T=96, H=1536, I=1024, E=12, K=3, weight_bits=4, act_int8=False, seed=21),
+    # more than 2048 slots and fewer than 64 per expert: 16-row tiles with two
+    # column fragments per gate/up wave, INT8 weights with INT8 and with BF16
+    # activations
+    Workload("rt_a", T=300, H=512, I=256, E=48, K=8, weight_bits=8, act_int8=True, seed=29),
+    Workload("rt_b", T=300, H=1024, I=256, E=48, K=8, weight_bits=8, act_int8=False, seed=30),
     # decode blocks (at most 4 rows per expert on average) in all four modes;
     # a Zipf-skewed top-1 routing puts more than 8 rows on one expert (several
     # row tiles)
