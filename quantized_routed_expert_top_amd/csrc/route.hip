@@ -94,6 +94,55 @@ __device__ void wave_scatter(const int32_t* ids, int64_t c0, int64_t c1, int E, 
   }
 }
 
+// The one-workgroup kernel keeps its wave's chunk (at most kSmallRows rows of
+// 64 slots) in registers between the count and the scatter: the keys and, per
+// row, each lane's mask of equal keys.  Same order of work as wave_count and
+// wave_scatter, so the same result.
+constexpr int kSmallRows = kSmallMax / 16 / kWave;   // 16 waves cover kSmallMax slots
+struct SmallChunk {
+  uint32_t key[kSmallRows];
+  uint64_t m[kSmallRows];
+};
+
+__device__ void small_load(const int32_t* ids, int64_t c0, int64_t c1, int E, int nbits, SmallChunk& ch) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int r = 0; r < kSmallRows; ++r) ch.key[r] = slot_key(ids, c0 + r * kWave + lane, c1, E);
+#pragma unroll
+  for (int r = 0; r < kSmallRows; ++r) ch.m[r] = (c0 + r * kWave < c1) ? match_any(ch.key[r], nbits) : 0ull;   // uniform
+}
+
+__device__ void small_count(const SmallChunk& ch, int64_t c0, int64_t c1, int E, int* hist_row) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int r = 0; r < kSmallRows; ++r)
+    if (c0 + r * kWave < c1 && ch.key[r] < (uint32_t)E && lane == __builtin_ctzll(ch.m[r]))
+      hist_row[ch.key[r]] += __popcll(ch.m[r]);
+}
+
+__device__ void small_scatter(const SmallChunk& ch, int64_t c0, int64_t c1, int E, int* base_row,
+                              int32_t* sorted_slot, int32_t* slot_row) {
+  const int lane = lane_id();
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int r = 0; r < kSmallRows; ++r) {
+    if (c0 + r * kWave >= c1) continue;                     // uniform
+    const int64_t s = c0 + r * kWave + lane;
+    const uint32_t key = ch.key[r];
+    if (s < c1) {
+      if (key < (uint32_t)E) {
+        const int pos = base_row[key] + __popcll(ch.m[r] & below);
+        sorted_slot[pos] = (int32_t)s;
+        slot_row[s] = pos;
+      } else {
+        slot_row[s] = -1;
+      }
+    }
+    // every lane has read base_row[key] above; LDS ops of one wave stay in order
+    if (key < (uint32_t)E && lane == __builtin_ctzll(ch.m[r])) base_row[key] += __popcll(ch.m[r]);
+  }
+}
+
 // Exclusive scan of data[0, n) (LDS) by the whole workgroup; returns the total.
 __device__ int block_exclusive_scan(int* data, int n, int* wave_tmp) {
   const int tid = threadIdx.x, nt = blockDim.x;
@@ -123,10 +172,11 @@ __device__ int block_exclusive_scan(int* data, int n, int* wave_tmp) {
   return total;
 }
 
-// Write the row-tile list of height bm from cnt[e] and offs[e] (LDS).  scratch
-// (LDS, E entries) is clobbered.  All threads must call.
+// Write the row-tile list of height bm from cnt[e] and offs[e] (LDS), into
+// tiles (and into tiles2 too, when given: two lists of the same height).
+// scratch (LDS, E entries) is clobbered.  All threads must call.
 __device__ void build_tiles(const int* cnt, const int* offs, int E, int bm, int* scratch, int* wave_tmp,
-                            Tile* tiles, int32_t* ntiles) {
+                            Tile* tiles, int32_t* ntiles, Tile* tiles2 = nullptr, int32_t* ntiles2 = nullptr) {
   for (int e = threadIdx.x; e < E; e += blockDim.x) scratch[e] = ceil_div(cnt[e], bm);
   __syncthreads();
   const int total = block_exclusive_scan(scratch, E, wave_tmp);
@@ -139,9 +189,13 @@ __device__ void build_tiles(const int* cnt, const int* offs, int E, int bm, int*
       t.nrows = min(bm, cnt[e] - j * bm);
       t.pad = 0;
       tiles[scratch[e] + j] = t;
+      if (tiles2) tiles2[scratch[e] + j] = t;
     }
   }
-  if (threadIdx.x == 0) *ntiles = total;
+  if (threadIdx.x == 0) {
+    *ntiles = total;
+    if (ntiles2) *ntiles2 = total;
+  }
   __syncthreads();
 }
 
@@ -163,7 +217,9 @@ __global__ __launch_bounds__(NW * kWave) void k_route_small(const int32_t* __res
   __syncthreads();
   const int64_t L = (int64_t)ceil_div(ceil_div(S, NW), kWave) * kWave;
   const int64_t c0 = min((int64_t)S, w * L), c1 = min((int64_t)S, c0 + L);
-  wave_count(ids, c0, c1, E, nbits, hist + w * E);
+  SmallChunk ch;
+  small_load(ids, c0, c1, E, nbits, ch);
+  small_count(ch, c0, c1, E, hist + w * E);
   __syncthreads();
   // per expert: prefix over waves, total count
   for (int e = tid; e < E; e += blockDim.x) {
@@ -186,10 +242,14 @@ __global__ __launch_bounds__(NW * kWave) void k_route_small(const int32_t* __res
   }
   for (int i = tid; i < NW * E; i += blockDim.x) hist[i] += offs[i % E];
   __syncthreads();
-  wave_scatter(ids, c0, c1, E, nbits, hist + w * E, sorted_slot, slot_row);
+  small_scatter(ch, c0, c1, E, hist + w * E, sorted_slot, slot_row);
   for (int i = total + tid; i < S; i += blockDim.x) sorted_slot[i] = -1;
-  if (tiles_a) build_tiles(cnt, offs, E, bm_a, scratch, wave_tmp, tiles_a, ntiles_a);
-  if (tiles_b) build_tiles(cnt, offs, E, bm_b, scratch, wave_tmp, tiles_b, ntiles_b);
+  if (tiles_a && tiles_b && bm_a == bm_b) {
+    build_tiles(cnt, offs, E, bm_a, scratch, wave_tmp, tiles_a, ntiles_a, tiles_b, ntiles_b);
+  } else {
+    if (tiles_a) build_tiles(cnt, offs, E, bm_a, scratch, wave_tmp, tiles_a, ntiles_a);
+    if (tiles_b) build_tiles(cnt, offs, E, bm_b, scratch, wave_tmp, tiles_b, ntiles_b);
+  }
 }
 
 // Three-kernel path.  ghist[gw][E]: per-wave counts, then per-wave bases.
@@ -284,8 +344,12 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict
   __syncthreads();
   if (blockIdx.x == 0) {           // uniform over the workgroup
     for (int e = tid; e <= E; e += blockDim.x) offsets[e] = offs[e];
-    if (tiles_a) build_tiles(cnt, offs, E, bm_a, scratch, wave_tmp, tiles_a, ntiles_a);
-    if (tiles_b) build_tiles(cnt, offs, E, bm_b, scratch, wave_tmp, tiles_b, ntiles_b);
+    if (tiles_a && tiles_b && bm_a == bm_b) {
+      build_tiles(cnt, offs, E, bm_a, scratch, wave_tmp, tiles_a, ntiles_a, tiles_b, ntiles_b);
+    } else {
+      if (tiles_a) build_tiles(cnt, offs, E, bm_a, scratch, wave_tmp, tiles_a, ntiles_a);
+      if (tiles_b) build_tiles(cnt, offs, E, bm_b, scratch, wave_tmp, tiles_b, ntiles_b);
+    }
   }
   int* row = rows + w * E;
   const int64_t gw = (int64_t)blockIdx.x * 4 + w;
@@ -347,6 +411,9 @@ hipError_t launch_route(const int32_t* ids, int T, int K, int E, int32_t* counts
                        offsets, sorted_slot, slot_row, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b);
     return hipGetLastError();
   }
+  // the one-workgroup kernel holds at most kSmallRows rows of 64 slots per
+  // wave in registers: 4 waves up to 512 slots, 16 waves up to kSmallMax
+  static_assert(512 / 4 <= kSmallRows * kWave && kSmallMax / 16 <= kSmallRows * kWave, "chunk exceeds registers");
   if (S <= kSmallMax) {
     constexpr int NW = 16;
     const size_t lds = sizeof(int) * (size_t)(NW * E + 3 * E + 1 + NW);
