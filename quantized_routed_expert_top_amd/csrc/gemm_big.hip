@@ -94,6 +94,7 @@ struct Big {
   __device__ static void run(const GemmProblem& p, int cb, int e, int row0, int nrows, RowSrc src, uint8_t* lds) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, kb = lane >> 4;
     const int wm = wave & 1, wn = wave >> 1;
+    const int live = min(TM, max(0, (nrows - wm * 64 + 15) >> 4));   // 16-row blocks holding rows (uniform)
     const int NG = p.kdim / kGroup;
     const int n0 = cb * BNO;
 
@@ -229,6 +230,7 @@ struct Big {
           for (int j = 0; j < TN; ++j) bv[j] = b_operand_bf16<WB>(wcur.b[j], t);
 #pragma unroll
           for (int i = 0; i < TM; ++i) {
+            if (i >= live) continue;
             const bf16x8_t av =
                 __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(base + a_base[t] + i * 16 * GB));
 #pragma unroll
@@ -246,6 +248,7 @@ struct Big {
         constexpr float kOff = (WB == 4) ? 136.0f : 128.0f;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
+          if (i >= live) continue;
           const f32x4_t rsum = *reinterpret_cast<const f32x4_t*>(aux + wm * 64 + i * 16 + 4 * kb);
 #pragma unroll
           for (int j = 0; j < TN; ++j)
