@@ -109,7 +109,7 @@ def cpu_baseline(wl, x_bits, ids, w, budget_s=12.0):
     same workload (repeated until ~budget_s of CPU time, at least once)."""
     import numpy as np
     import oracle
-    from quantized_routed_expert_top_amd.synthetic import touched_experts
+    from harness.synthetic import touched_experts
     if wl.T > 512:
         tokens = np.arange(min(wl.T, 64))
         sample = f"first {len(tokens)} tokens of the {wl.T}-token batch"
@@ -136,7 +136,7 @@ def router_bench(args, wl):
     import numpy as np
     import torch
     import quantized_routed_expert_top_amd as qre
-    from quantized_routed_expert_top_amd.inputs import gen_router_logits
+    from harness.inputs import gen_router_logits
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -225,8 +225,8 @@ def main():
     import numpy as np
     import torch
     import quantized_routed_expert_top_amd as qre
-    from quantized_routed_expert_top_amd.inputs import WORKLOADS
-    from quantized_routed_expert_top_amd.synthetic import algorithmic_bytes, gpu_problem
+    from harness.inputs import WORKLOADS
+    from harness.synthetic import algorithmic_bytes, gpu_problem
 
     wl = WORKLOADS[args.workload]
     if args.stage == "router":

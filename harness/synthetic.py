@@ -10,8 +10,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import QuantizedExperts, quantize_weights
-from .inputs import GATE, UP, DOWN, Workload, gen_routing, gen_x, iter_expert_weights
+from quantized_routed_expert_top_amd import QuantizedExperts, quantize_weights
+from harness.inputs import GATE, UP, DOWN, Workload, gen_routing, gen_x, iter_expert_weights
 
 
 def x_tensor(x_bits: np.ndarray, device) -> torch.Tensor:

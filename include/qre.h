@@ -28,14 +28,13 @@
  *    last HIP error code, see qre_last_hip_error), and may be called from
  *    several threads on different streams.
  *  - Work is enqueued on `stream` and the call returns without synchronizing,
- *    except qre_read_dropped_slots, which synchronizes `stream`.
+ *    except qre_read_device_error, which synchronizes `stream`.
  *  - Arguments are validated on the host before anything is enqueued.  On any
  *    error code nothing has been enqueued.  A problem with zero tokens is valid
- *    and enqueues nothing (qre_route and qre_build_tiles still write their
- *    per-expert outputs).
+ *    and enqueues nothing (qre_route still writes its per-expert outputs).
  *  - Device pointers must be 16-byte aligned (QRE_ERR_ALIGN otherwise).
  *  - A routed expert id outside [0, E) drops that slot: it contributes zero to
- *    the output and is counted (see qre_read_dropped_slots).  Duplicate ids
+ *    the output and is counted (see qre_read_device_error).  Duplicate ids
  *    within a token are legal; each slot is computed and summed.
  *  - Non-finite inputs give unspecified (but memory-safe) results.
  *
@@ -100,17 +99,23 @@ typedef struct qre_weights {
   const void* down_q; const void* down_s;
 } qre_weights;
 
-/* Bytes of device workspace qre_moe_forward needs for `desc` (host out). */
+/* Bytes of device workspace qre_moe_forward needs for `desc` (host out): the
+ * routing permutation, the GEMM row-tile lists, the intermediate h (BF16
+ * [T*K][I]) and y (BF16 [T*K][H]) in sorted-row order, and in INT8 mode the
+ * INT8 codes and FP32 scales of x and h (model card, paragraph on
+ * --int8-expert-activations).  QRE_ERR_* for an invalid descriptor. */
 int qre_workspace_bytes(const qre_desc* desc, size_t* bytes);
 
-/* The whole routed-expert feed-forward: x, topk_ids, topk_w, weights -> out.
+/* The whole routed-expert feed-forward (minnow README, "Quantization": fused
+ * gate/up/SiLU kernels, GPU routing of decode blocks; model card,
+ * "Checkpoints and precision"): x, topk_ids, topk_w, weights -> out.
  * Runs the permutation, the INT8 activation quantizer (act_int8 only), the
  * fused gate/up/SiLU grouped GEMM, the down grouped GEMM and the combine.  For
  * up to 2048 slots with the usual expert shapes the permutation is computed
  * inside the gate/up kernel (each expert's workgroups find that expert's slots)
  * instead of by a separate launch; the results are the same.
  * `workspace` (>= qre_workspace_bytes) holds the permutation, h and y; after
- * the call it also holds what qre_read_dropped_slots reads. */
+ * the call it also holds what qre_read_device_error reads. */
 int qre_moe_forward(const qre_desc* desc, const void* x, const int32_t* topk_ids,
                     const float* topk_w, const qre_weights* weights, void* out,
                     void* workspace, size_t workspace_bytes, qre_stream_t stream);
@@ -125,10 +130,12 @@ int qre_moe_forward_timed(const qre_desc* desc, const void* x, const int32_t* to
                           void* workspace, size_t workspace_bytes, void* const* events,
                           qre_stream_t stream);
 
-/* Number of slots whose expert id was outside [0, E) in the last
- * qre_moe_forward that used `workspace` (host out).  Synchronizes `stream`. */
-int qre_read_dropped_slots(const qre_desc* desc, const void* workspace, int32_t* n_dropped,
-                           qre_stream_t stream);
+/* Number of slots whose expert id was outside [0, E) (host out) in the last
+ * routing that used `workspace`: a qre_moe_forward or qre_route workspace
+ * (every workspace starts with this counter).  Such a slot is a precondition
+ * violation of the caller; it is dropped (contributes zero) and counted.
+ * Synchronizes `stream`, so the count is that of the last call enqueued. */
+int qre_read_device_error(const void* workspace, int32_t* n_bad_ids, qre_stream_t stream);
 
 /* Device addresses, inside a qre_moe_forward workspace, of the permutation the
  * last call computed (layouts of qre_route; host out).  Reading them after
@@ -146,19 +153,14 @@ int qre_workspace_permutation(const qre_desc* desc, void* workspace, int32_t** c
  *   sorted_slot[S]   sorted_slot[offsets[e] + j] = j-th smallest slot with id e;
  *                    entries at and past offsets[E] are -1
  *   slot_row[S]      position of slot s in sorted_slot, or -1 if dropped
- * Bit-exact and deterministic (no atomics decide any order).  Uses desc->T, K,
- * E (and H, I, weight_bits, act_int8 to size the GEMM row tiles).  `workspace`
- * (>= qre_stage_workspace_bytes) receives the routing scratch and the row-tile
- * lists that qre_gate_up and qre_down read.  counts and offsets are written
- * even when T == 0. */
-int qre_route(const qre_desc* desc, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
-              int32_t* sorted_slot, int32_t* slot_row, void* workspace, size_t workspace_bytes,
-              qre_stream_t stream);
-
-/* Rebuild the row-tile lists in `workspace` from offsets[E+1] alone, for a
- * permutation that did not come from qre_route. */
-int qre_build_tiles(const qre_desc* desc, const int32_t* offsets, void* workspace,
-                    size_t workspace_bytes, qre_stream_t stream);
+ * Bit-exact and deterministic (no atomics decide any order).  `workspace`
+ * (>= qre_route_workspace_bytes, 16-byte aligned) holds the routing scratch
+ * and the dropped-slot counter of qre_read_device_error.  counts and offsets
+ * are written even when T == 0. */
+int qre_route_workspace_bytes(int32_t T, int32_t K, int32_t E, size_t* bytes);
+int qre_route(const int32_t* topk_ids, int32_t T, int32_t K, int32_t E, int32_t* counts,
+              int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row, void* workspace,
+              size_t workspace_bytes, qre_stream_t stream);
 
 /* Per-row, per-128 INT8 quantizer (model card, --int8-expert-activations):
  * s = max|v| / 127 in FP32 (IEEE division), q = clamp(rint(v / s), -127, 127),
@@ -168,29 +170,43 @@ int qre_quantize_act(const void* v, int32_t rows, int32_t cols, int8_t* q, float
                      qre_stream_t stream);
 
 /* Fused gate/up projection and SiLU*mul for every valid sorted row r
- * (expert e with offsets[e] <= r < offsets[e+1], token t = sorted_slot[r] / K):
+ * (expert e with offsets[e] <= r < offsets[e+1], token t = sorted_slot[r] / K)
+ * (minnow README, "Quantization": fused gate/up/SiLU; model card, "Checkpoints
+ * and precision": gate and up projections, weights dequantized to BF16 in
+ * registers, INT32 group dot products combined in FP32 with INT8 activations):
  *   h[r][i] = bf16( silu(g) * u ),  g = sum_h x[t][h] Wg[e][i][h],  u likewise.
  * BF16 mode reads x (bf16 [T][H]); INT8 mode reads xq (int8 [T][H]) and xs
- * (fp32 [T][H/128]) and combines INT32 group sums in FP32.  h: bf16 [T*K][I]
- * (rows past offsets[E] are not written).  `workspace` must hold the row-tile
- * lists of this routing, written by qre_route or qre_build_tiles.  One kernel. */
+ * (fp32 [T][H/128]), combines INT32 group sums in FP32, and, when hq and hs
+ * are given, also writes h quantized per 128 values (the input of the INT8
+ * down projection): hq int8 [T*K][I], hs fp32 [T*K][I/128], exactly what
+ * qre_quantize_act gives for h.  h: bf16 [T*K][I], optional in INT8 mode
+ * when hq/hs are given.  Rows past offsets[E] are not written.  sorted_slot
+ * and offsets are qre_route's outputs (or any stable permutation in the same
+ * form).  `workspace` (>= qre_stage_workspace_bytes) receives the row-tile
+ * list built from offsets.  QRE_ERR_MODE if an input of the mode is missing,
+ * or hq/hs are given in BF16 mode. */
 int qre_gate_up(const qre_desc* desc, const void* x, const int8_t* xq, const float* xs,
-                const int32_t* sorted_slot, const qre_weights* weights, void* h,
-                const void* workspace, size_t workspace_bytes, qre_stream_t stream);
+                const int32_t* sorted_slot, const int32_t* offsets, const qre_weights* weights,
+                void* h, int8_t* hq, float* hs, void* workspace, size_t workspace_bytes,
+                qre_stream_t stream);
 
-/* Down projection for every valid sorted row r: y[r][j] = bf16( sum_i h[r][i] Wd[e][j][i] ).
- * BF16 mode reads h (bf16 [T*K][I]); INT8 mode reads hq (int8 [T*K][I]) and hs
- * (fp32 [T*K][I/128]).  y: bf16 [T*K][H].  Row tiles come from `workspace` as
- * for qre_gate_up.  One kernel. */
+/* Down projection for every valid sorted row r (model card, "Checkpoints and
+ * precision": down projection of the routed experts; expert outputs return to
+ * BF16): y[r][j] = bf16( sum_i h[r][i] Wd[e][j][i] ).  BF16 mode reads h
+ * (bf16 [T*K][I]); INT8 mode reads hq (int8 [T*K][I]) and hs
+ * (fp32 [T*K][I/128]).  y: bf16 [T*K][H].  offsets and `workspace` as for
+ * qre_gate_up. */
 int qre_down(const qre_desc* desc, const void* h, const int8_t* hq, const float* hs,
-             const qre_weights* weights, void* y, const void* workspace, size_t workspace_bytes,
-             qre_stream_t stream);
+             const int32_t* offsets, const qre_weights* weights, void* y, void* workspace,
+             size_t workspace_bytes, qre_stream_t stream);
 
-/* Workspace bytes the stage entry points need for `desc` (routing scratch and
- * the two GEMM row-tile lists). */
+/* Workspace bytes qre_gate_up and qre_down need for `desc` (the row-tile
+ * lists, and in INT8 mode room for h when only hq/hs are asked for). */
 int qre_stage_workspace_bytes(const qre_desc* desc, size_t* bytes);
 
-/* Per-token combine: out[t][j] = bf16( fma chain over k ascending of
+/* Per-token combine (the top-k weighted sum of the routed experts' outputs;
+ * the order, k ascending with one FMA per term, is this library's reading,
+ * which makes the result deterministic): out[t][j] = bf16( fma chain over k ascending of
  * topk_w[t][k] * y[slot_row[t*K+k]][j] ) in FP32, starting from 0; a slot with
  * slot_row = -1 is skipped.  y bf16 [T*K][H] in sorted-row order. */
 int qre_combine(const void* y, const int32_t* slot_row, const float* topk_w, int32_t T, int32_t K,

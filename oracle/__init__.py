@@ -68,7 +68,7 @@ def lib():
         L.orc_down.argtypes = [P, P, P, P, P, P, P, P]
         L.orc_combine.argtypes = [P, P, P, i32, i32, i32, P, i64, P, P]
         L.orc_moe_forward.restype = C.c_int
-        L.orc_moe_forward.argtypes = [P, P, P, P, P, P, i64, P, P]
+        L.orc_moe_forward.argtypes = [P, P, P, P, P, P, i64, P, P, P]
         L.orc_num_threads.restype = C.c_int
         _lib = L
     return _lib
@@ -266,9 +266,11 @@ def combine(y_bf16, slot_row, topk_w, *, T, K, H, tokens=None):
 
 
 def moe_forward(x_bf16, topk_ids, topk_w, W: QWeights, *, E, bits, act_int8=False, I=None,
-                tokens=None):
+                tokens=None, return_y=False):
     """Whole feed-forward. Returns (out float32 before final rounding, out bf16
-    bits, number of dropped slots); rows follow `tokens` when given."""
+    bits, number of dropped slots); rows follow `tokens` when given.  With
+    return_y, a fourth item: the BF16 expert outputs each row combines,
+    [n, K, H] bits in slot order (zeros for a dropped slot)."""
     x = _c(x_bf16, np.uint16)
     ids = _c(topk_ids, np.int32)
     T, H = x.shape
@@ -280,12 +282,13 @@ def moe_forward(x_bf16, topk_ids, topk_w, W: QWeights, *, E, bits, act_int8=Fals
     o32 = np.zeros((n, H), dtype=np.float32)
     o16 = np.zeros((n, H), dtype=np.uint16)
     d = _shape(T, H, I, E, K, bits, act_int8)
+    y = np.zeros((n, K, H), dtype=np.uint16) if return_y else None
     rc = lib().orc_moe_forward(C.byref(d), _p(x), _p(ids), _p(_c(topk_w, np.float32)),
                                C.byref(W._struct()), _p(tok), 0 if tok is None else len(tok),
-                               _p(o32), _p(o16))
+                               _p(o32), _p(o16), _p(y))
     if rc < 0:
         raise ValueError(f"orc_moe_forward: {rc}")
-    return o32, o16, rc
+    return (o32, o16, rc, y) if return_y else (o32, o16, rc)
 
 
 # ---- workload weights ------------------------------------------------------------
@@ -295,7 +298,7 @@ def workload_experts(wl, experts, threads=None) -> QWeights:
     (the float32 weights come from the shared input generators); the other
     experts are left zero."""
     from concurrent.futures import ThreadPoolExecutor
-    from quantized_routed_expert_top_amd.inputs import GATE, UP, DOWN, default_threads, gen_expert_weight
+    from harness.inputs import GATE, UP, DOWN, default_threads, gen_expert_weight
     b = wl.weight_bits
     gq = np.zeros((wl.E, wl.I, packed_cols(wl.H, b)), np.uint8)
     gs = np.zeros((wl.E, wl.I, wl.H // GROUP), np.uint16)

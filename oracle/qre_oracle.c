@@ -333,6 +333,27 @@ static float orc_int8_dot(const int8_t* xq, const float* xs, const int8_t* wq, c
     return acc;
 }
 
+/* Work items of the expert loops: runs of at most ORC_CHUNK sorted rows of
+ * one expert, so that one expert with many rows is spread over threads (each
+ * item expands its expert's weights itself).  Returns a malloc'ed array
+ * {n, e0, r0_0, r1_0, e1, ...}. */
+#define ORC_CHUNK 64
+static int32_t* orc_row_chunks(const int32_t* offsets, int32_t E)
+{
+    int64_t n = 0;
+    for (int32_t e = 0; e < E; ++e) n += (offsets[e + 1] - offsets[e] + ORC_CHUNK - 1) / ORC_CHUNK;
+    int32_t* c = (int32_t*)malloc(sizeof(int32_t) * (size_t)(1 + 3 * n));
+    c[0] = (int32_t)n;
+    int64_t k = 0;
+    for (int32_t e = 0; e < E; ++e)
+        for (int32_t r = offsets[e]; r < offsets[e + 1]; r += ORC_CHUNK, ++k) {
+            c[1 + 3 * k] = e;
+            c[2 + 3 * k] = r;
+            c[3 + 3 * k] = r + ORC_CHUNK < offsets[e + 1] ? r + ORC_CHUNK : offsets[e + 1];
+        }
+    return c;
+}
+
 /* Gate/up for every sorted row of every expert, or only for rows whose flag is
  * set in row_mask (may be NULL).  A16: x bf16 [T][H].  A8: xq [T][H], xs [T][H/128].
  * h: bf16 bits [S][I] indexed by sorted row. */
@@ -343,9 +364,11 @@ int orc_gate_up(const orc_shape* d, const uint16_t* x, const int8_t* xq, const f
     const int64_t H = d->H, I = d->I, G_H = H / ORC_GROUP;
     const int bits = d->bits;
     int overflow = 0;
+    int32_t* chunks = orc_row_chunks(offsets, d->E);
+    const int64_t nchunks = chunks[0];
     #pragma omp parallel for schedule(dynamic, 1) reduction(|:overflow)
-    for (int32_t e = 0; e < d->E; ++e) {
-        int32_t r0 = offsets[e], r1 = offsets[e + 1];
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int32_t e = chunks[1 + 3 * c], r0 = chunks[2 + 3 * c], r1 = chunks[3 + 3 * c];
         int any = 0;
         for (int32_t r = r0; r < r1; ++r) if (!row_mask || row_mask[r]) { any = 1; break; }
         if (!any) continue;
@@ -389,6 +412,7 @@ int orc_gate_up(const orc_shape* d, const uint16_t* x, const int8_t* xq, const f
         }
         free(xr); free(wg); free(wu); free(cg); free(cu);
     }
+    free(chunks);
     return overflow ? -3 : 0;
 }
 
@@ -400,9 +424,11 @@ int orc_down(const orc_shape* d, const uint16_t* h, const int8_t* hq, const floa
     const int64_t H = d->H, I = d->I, G_I = I / ORC_GROUP;
     const int bits = d->bits;
     int overflow = 0;
+    int32_t* chunks = orc_row_chunks(offsets, d->E);
+    const int64_t nchunks = chunks[0];
     #pragma omp parallel for schedule(dynamic, 1) reduction(|:overflow)
-    for (int32_t e = 0; e < d->E; ++e) {
-        int32_t r0 = offsets[e], r1 = offsets[e + 1];
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int32_t e = chunks[1 + 3 * c], r0 = chunks[2 + 3 * c], r1 = chunks[3 + 3 * c];
         int any = 0;
         for (int32_t r = r0; r < r1; ++r) if (!row_mask || row_mask[r]) { any = 1; break; }
         if (!any) continue;
@@ -436,6 +462,7 @@ int orc_down(const orc_shape* d, const uint16_t* h, const int8_t* hq, const floa
         }
         free(hr); free(wd); free(cd);
     }
+    free(chunks);
     return overflow ? -3 : 0;
 }
 
@@ -466,10 +493,12 @@ void orc_combine(const uint16_t* y, const int32_t* slot_row, const float* topk_w
 /* The whole feed-forward.  tokens (may be NULL = all tokens) restricts the
  * work to the listed tokens; out rows follow the list.  Scratch h/y are
  * allocated here at [S][I] and [S][H] (only the needed rows are written).
+ * y_tok (may be NULL) receives the BF16 expert outputs that each listed token
+ * combines, [n][K][H] in slot order (zeros for a dropped slot).
  * Returns the number of dropped slots (>= 0), or a negative error. */
 int orc_moe_forward(const orc_shape* d, const uint16_t* x, const int32_t* ids, const float* topk_w,
                     const orc_weights* W, const int64_t* tokens, int64_t ntok,
-                    float* out_f32, uint16_t* out_bf16)
+                    float* out_f32, uint16_t* out_bf16, uint16_t* y_tok)
 {
     const int64_t T = d->T, H = d->H, I = d->I, K = d->K, S = T * K;
     if (H % ORC_GROUP || I % ORC_GROUP || (d->bits != 4 && d->bits != 8)) return -1;
@@ -505,6 +534,17 @@ int orc_moe_forward(const orc_shape* d, const uint16_t* x, const int32_t* ids, c
     }
     if (rc == 0) rc = orc_down(d, h, hq, hs, offsets, W, mask, y);
     if (rc == 0) orc_combine(y, slot_row, topk_w, d->T, d->K, d->H, tokens, ntok, out_f32, out_bf16);
+    if (rc == 0 && y_tok) {
+        for (int64_t n = 0; n < n_out; ++n) {
+            const int64_t t = tokens ? tokens[n] : n;
+            for (int64_t k = 0; k < K; ++k) {
+                const int32_t r = slot_row[t * K + k];
+                uint16_t* dst = y_tok + (n * K + k) * H;
+                if (r < 0) memset(dst, 0, sizeof(uint16_t) * (size_t)H);
+                else memcpy(dst, y + (int64_t)r * H, sizeof(uint16_t) * (size_t)H);
+            }
+        }
+    }
     free(counts); free(offsets); free(sorted_slot); free(slot_row); free(mask);
     free(h); free(y); free(xq); free(xs); free(hq); free(hs);
     return rc == 0 ? nbad : rc;

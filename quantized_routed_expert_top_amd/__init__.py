@@ -61,13 +61,13 @@ def _lib():
         L.qre_stage_workspace_bytes.argtypes = [P, P]
         L.qre_moe_forward.argtypes = [P, P, P, P, P, P, P, sz, P]
         L.qre_moe_forward_timed.argtypes = [P, P, P, P, P, P, P, sz, P, P]
-        L.qre_read_dropped_slots.argtypes = [P, P, P, P]
+        L.qre_read_device_error.argtypes = [P, P, P]
         L.qre_workspace_permutation.argtypes = [P, P, P, P, P, P]
-        L.qre_route.argtypes = [P, P, P, P, P, P, P, sz, P]
-        L.qre_build_tiles.argtypes = [P, P, P, sz, P]
+        L.qre_route_workspace_bytes.argtypes = [i32, i32, i32, P]
+        L.qre_route.argtypes = [P, i32, i32, i32, P, P, P, P, P, sz, P]
         L.qre_quantize_act.argtypes = [P, i32, i32, P, P, P]
-        L.qre_gate_up.argtypes = [P, P, P, P, P, P, P, P, sz, P]
-        L.qre_down.argtypes = [P, P, P, P, P, P, P, sz, P]
+        L.qre_gate_up.argtypes = [P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.qre_down.argtypes = [P, P, P, P, P, P, P, P, sz, P]
         L.qre_combine.argtypes = [P, P, P, i32, i32, i32, P, P]
         L.qre_topk_softmax.argtypes = [P, i32, i32, i32, P, P, P]
         L.qre_quantize_weights.argtypes = [P, i64, i64, i32, P, P, P]
@@ -255,22 +255,23 @@ def workspace_permutation(T, H, I, E, K, bits, act_int8, workspace):
     return tuple(views)
 
 
-def read_dropped_slots(T, H, I, E, K, bits, act_int8, workspace) -> int:
+def read_device_error(workspace) -> int:
+    """Dropped-slot count (ids outside [0, E)) of the last routing that used
+    `workspace` (a moe_forward or route workspace); synchronizes the stream."""
+    _need(workspace, "workspace", torch.uint8)
     n = C.c_int32(0)
-    _check("qre_read_dropped_slots", _lib().qre_read_dropped_slots(
-        C.byref(_desc(T, H, I, E, K, bits, act_int8)), _ptr(workspace), C.byref(n), _stream()))
+    _check("qre_read_device_error", _lib().qre_read_device_error(_ptr(workspace), C.byref(n), _stream()))
     return n.value
 
 
 def stage_workspace(T, H, I, E, K, bits=4, act_int8=False, device="cuda"):
-    """Workspace for the stage entry points (routing scratch, GEMM row tiles)."""
+    """Workspace for the stage GEMM entry points (row-tile lists)."""
     return _workspace(stage_workspace_bytes(T, H, I, E, K, bits, act_int8), device)
 
 
-def route(topk_ids, E, H=GROUP, I=GROUP, bits=4, act_int8=False, workspace=None):
-    """(counts[E], offsets[E+1], sorted_slot[S], slot_row[S], workspace).  The
-    workspace also receives the GEMM row tiles for a problem with these H, I,
-    bits and mode, for gate_up / down."""
+def route(topk_ids, E, workspace=None):
+    """(counts[E], offsets[E+1], sorted_slot[S], slot_row[S], workspace): the
+    stable counting sort of the T*K slots by expert id."""
     T, K = topk_ids.shape
     _need(topk_ids, "topk_ids", torch.int32, (T, K))
     dev = topk_ids.device
@@ -280,22 +281,13 @@ def route(topk_ids, E, H=GROUP, I=GROUP, bits=4, act_int8=False, workspace=None)
     sorted_slot = torch.empty(max(S, 1), dtype=torch.int32, device=dev)[:S]
     slot_row = torch.empty(max(S, 1), dtype=torch.int32, device=dev)[:S]
     if workspace is None:
-        workspace = stage_workspace(T, H, I, E, K, bits, act_int8, dev)
-    d = _desc(T, H, I, E, K, bits, act_int8)
-    _check("qre_route", _lib().qre_route(C.byref(d), _ptr(topk_ids), _ptr(counts), _ptr(offsets), _ptr(sorted_slot),
+        n = C.c_size_t(0)
+        _check("qre_route_workspace_bytes", _lib().qre_route_workspace_bytes(T, K, E, C.byref(n)))
+        workspace = _workspace(n.value, dev)
+    _need(workspace, "workspace", torch.uint8)
+    _check("qre_route", _lib().qre_route(_ptr(topk_ids), T, K, E, _ptr(counts), _ptr(offsets), _ptr(sorted_slot),
                                          _ptr(slot_row), _ptr(workspace), workspace.numel(), _stream()))
     return counts, offsets, sorted_slot, slot_row, workspace
-
-
-def build_tiles(offsets, T, H, I, E, K, bits=4, act_int8=False, workspace=None):
-    """Write the GEMM row tiles of the permutation `offsets` into a stage workspace."""
-    _need(offsets, "offsets", torch.int32, (E + 1,))
-    if workspace is None:
-        workspace = stage_workspace(T, H, I, E, K, bits, act_int8, offsets.device)
-    d = _desc(T, H, I, E, K, bits, act_int8)
-    _check("qre_build_tiles", _lib().qre_build_tiles(C.byref(d), _ptr(offsets), _ptr(workspace), workspace.numel(),
-                                                     _stream()))
-    return workspace
 
 
 def quantize_act(v):
@@ -327,8 +319,11 @@ def quantize_weights(w, bits, out=None):
     return q, s
 
 
-def gate_up(x, sorted_slot, W: QuantizedExperts, K, workspace, act_int8=False, xq=None, xs=None, h=None):
-    """h[S, I] bf16 by sorted row; `workspace` holds the row tiles (route / build_tiles)."""
+def gate_up(x, sorted_slot, offsets, W: QuantizedExperts, K, act_int8=False, xq=None, xs=None, h=None,
+            want_hq=False, h_out=True, workspace=None):
+    """h[S, I] bf16 by sorted row.  INT8 mode with want_hq also returns the
+    per-128 INT8 quantization of h: (h, hq int8 [S, I], hs fp32 [S, I/128]);
+    h_out=False then skips h (returned as None)."""
     if act_int8:
         T, H = xq.shape
         _need(xq, "xq", torch.int8, (T, H))
@@ -339,23 +334,32 @@ def gate_up(x, sorted_slot, W: QuantizedExperts, K, workspace, act_int8=False, x
         _need(x, "x", torch.bfloat16, (T, H))
         dev = x.device
     S = T * K
+    E = W.E
     _need(sorted_slot, "sorted_slot", torch.int32, (S,))
-    if h is None:
+    _need(offsets, "offsets", torch.int32, (E + 1,))
+    if h is None and (h_out or not want_hq):
         h = torch.empty((S, W.I), dtype=torch.bfloat16, device=dev)
-    _need(h, "h", torch.bfloat16, (S, W.I))
+    if h is not None:
+        _need(h, "h", torch.bfloat16, (S, W.I))
+    hq = hs = None
+    if want_hq:
+        hq = torch.empty((S, W.I), dtype=torch.int8, device=dev)
+        hs = torch.empty((S, W.I // GROUP), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = stage_workspace(T, H, W.I, E, K, W.bits, act_int8, dev)
     _need(workspace, "workspace", torch.uint8)
-    d = _desc(T, H, W.I, W.E, K, W.bits, act_int8)
+    d = _desc(T, H, W.I, E, K, W.bits, act_int8)
     ws_struct = W._struct()
     _check("qre_gate_up", _lib().qre_gate_up(C.byref(d), _ptr(x), _ptr(xq), _ptr(xs), _ptr(sorted_slot),
-                                             C.byref(ws_struct), _ptr(h), _ptr(workspace), workspace.numel(),
-                                             _stream()))
-    return h
+                                             _ptr(offsets), C.byref(ws_struct), _ptr(h), _ptr(hq), _ptr(hs),
+                                             _ptr(workspace), workspace.numel(), _stream()))
+    return (h, hq, hs) if want_hq else h
 
 
-def down(h, W: QuantizedExperts, T, K, workspace, act_int8=False, hq=None, hs=None, y=None):
-    """y[S, H] bf16 by sorted row; `workspace` holds the row tiles (route / build_tiles)."""
+def down(h, offsets, W: QuantizedExperts, T, K, act_int8=False, hq=None, hs=None, y=None, workspace=None):
+    """y[S, H] bf16 by sorted row."""
     S = T * K
-    I, H = W.I, W.H
+    I, H, E = W.I, W.H, W.E
     if act_int8:
         _need(hq, "hq", torch.int8, (S, I))
         _need(hs, "hs", torch.float32, (S, I // GROUP))
@@ -363,14 +367,17 @@ def down(h, W: QuantizedExperts, T, K, workspace, act_int8=False, hq=None, hs=No
     else:
         _need(h, "h", torch.bfloat16, (S, I))
         dev = h.device
+    _need(offsets, "offsets", torch.int32, (E + 1,))
     if y is None:
         y = torch.empty((S, H), dtype=torch.bfloat16, device=dev)
     _need(y, "y", torch.bfloat16, (S, H))
+    if workspace is None:
+        workspace = stage_workspace(T, H, I, E, K, W.bits, act_int8, dev)
     _need(workspace, "workspace", torch.uint8)
-    d = _desc(T, H, I, W.E, K, W.bits, act_int8)
+    d = _desc(T, H, I, E, K, W.bits, act_int8)
     ws_struct = W._struct()
-    _check("qre_down", _lib().qre_down(C.byref(d), _ptr(h), _ptr(hq), _ptr(hs), C.byref(ws_struct), _ptr(y),
-                                       _ptr(workspace), workspace.numel(), _stream()))
+    _check("qre_down", _lib().qre_down(C.byref(d), _ptr(h), _ptr(hq), _ptr(hs), _ptr(offsets), C.byref(ws_struct),
+                                       _ptr(y), _ptr(workspace), workspace.numel(), _stream()))
     return y
 
 

@@ -237,50 +237,6 @@ struct Gemm16 {
     }
   }
 
-  // One wave, whole reduction of NG (compile-time) groups, in chunks of GW
-  // groups with two chunks in flight: the loads of chunk c+2 are issued as soon
-  // as chunk c is consumed.  Everything is unrolled, so each wait is exact.
-  template <int NG>
-  __device__ void run_stream() const {
-    constexpr int NC = (NG + GW - 1) / GW;
-    f32x4_t acc[FN][NM];
-#pragma unroll
-    for (int f = 0; f < FN; ++f)
-#pragma unroll
-      for (int m = 0; m < NM; ++m) acc[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    Buf b[2][GW];
-#pragma unroll
-    for (int c = 0; c < 2 && c < NC; ++c) {
-#pragma unroll
-      for (int j = 0; j < GW; ++j) {
-        load<false>(b[c][j], c * GW + j);
-        __builtin_amdgcn_sched_barrier(0);     // keep the groups' loads in order
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-#pragma unroll
-      for (int j = 0; j < GW; ++j)
-        if (c * GW + j < NG) group(b[c & 1][j], acc);
-      // finish this chunk's scaling before moving on: without this the FMA
-      // chain is deferred to the end and every group's partials stay live
-#pragma unroll
-      for (int f = 0; f < FN; ++f)
-#pragma unroll
-        for (int m = 0; m < NM; ++m) asm volatile("" : "+v"(acc[f][m]));
-      if (c + 2 < NC) {
-#pragma unroll
-        for (int j = 0; j < GW; ++j) {
-          load<false>(b[c & 1][j], (c + 2) * GW + j);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int f = 0; f < FN; ++f) store(acc, f);
-  }
-
   // red: LDS [NW][FN][NM][64] of f32x4 partial sums.
   __device__ void run_split(f32x4_t* red) const {
     f32x4_t acc[FN][NM];
@@ -668,20 +624,6 @@ __global__ __launch_bounds__(256) void k_gemm16(GemmProblem p) {
   g.run_split(red);
 }
 
-// Streaming kernel (reduction of NG groups known at compile time): every wave
-// owns its own 16 x 16*FN tile over the whole reduction; a workgroup is four
-// neighbouring column tiles of one row tile.
-template <int WB, bool A8, bool DUAL, int FN, int GW, int NG>
-__global__ __launch_bounds__(256) void k_gemm16_stream(GemmProblem p) {
-  using K = Gemm16<WB, A8, DUAL, FN, GW>;
-  if ((int)blockIdx.y >= *p.ntiles) return;
-  const int col0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * K::BN;
-  if (col0 >= p.n) return;                                  // wave-uniform
-  const Tile td = p.tiles[blockIdx.y];
-  K g(p, td, col0);
-  g.template run_stream<NG>();
-}
-
 template <int WB, bool A8, bool DUAL, int FN, int GW>
 hipError_t launch_split(const GemmProblem& p, hipStream_t stream) {
   constexpr int BN = 16 * FN;
@@ -690,18 +632,6 @@ hipError_t launch_split(const GemmProblem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int WB, bool A8, bool DUAL, int FN, int GW, int NG>
-hipError_t launch_stream(const GemmProblem& p, hipStream_t stream) {
-  constexpr int BN = 4 * 16 * FN;
-  const dim3 grid((p.n + BN - 1) / BN, (unsigned)p.max_tiles);
-  hipLaunchKernelGGL((k_gemm16_stream<WB, A8, DUAL, FN, GW, NG>), grid, dim3(256), 0, stream, p);
-  return hipGetLastError();
-}
-
-// Kernel choice by reduction length (G = kdim / 128): the usual expert shapes
-// get the streaming kernel, anything else the split-reduction kernel.  The
-// fused gate/up GEMM streams two matrices, so one 16-column fragment per wave;
-// the down GEMM streams one, so two.
 // Largest activation tile (rows x kdim x element bytes) the decode kernel stages in LDS.
 constexpr int64_t kDecLdsMax = 64 * 1024;
 

@@ -182,7 +182,10 @@ __device__ __forceinline__ ExpertRows route_expert(const RouteOut& ra, int e, bo
   if (writer && tid == 0) {
     ra.counts[e] = count;
     ra.offsets[e] = off;
-    if (e == ra.E - 1) ra.offsets[ra.E] = off + count;
+    if (e == ra.E - 1) {
+      ra.offsets[ra.E] = off + count;
+      *ra.dropped = ra.S - (off + count);
+    }
   }
   if (writer && e == ra.E - 1)
     for (int i = off + count + tid; i < ra.S; i += blockDim.x) ra.sorted_slot[i] = -1;

@@ -1,7 +1,7 @@
 // Host side of the C ABI declared in include/qre.h: argument validation,
 // workspace layout and the launch sequence of the routed-expert feed-forward.
 // No entry point allocates memory or synchronizes (except
-// qre_read_dropped_slots); all validation happens before the first launch.
+// qre_read_device_error); all validation happens before the first launch.
 #include <stdint.h>
 #include <string.h>
 
@@ -39,27 +39,38 @@ struct Carver {
   }
 };
 
-// Scratch shared by qre_moe_forward and the stage entry points: the two GEMM
-// row-tile lists and the routing scratch.  qre_moe_forward's workspace starts
-// with the same block.
+// Every workspace (qre_moe_forward's and the stage entry points') starts with
+// a 256-byte header; its first int32 is the number of dropped slots (ids
+// outside [0, E)) of the last routing that used the workspace.
+constexpr size_t kHeaderInts = kAlign / sizeof(int32_t);
+
+// Scratch shared by qre_moe_forward and the stage entry points: the header,
+// the two GEMM row-tile lists and the routing scratch (and, for the stage
+// gate/up in INT8 mode, room for the BF16 h its quantizer reads when the
+// caller asks for hq/hs only).  qre_moe_forward's workspace starts with the
+// same block.
 struct StageLayout {
+  int32_t* header;
   int32_t* ntiles;            // [2]: gate/up, down
   Tile *tiles_gu, *tiles_dn;
   void* route_scratch;
+  uint16_t* h_tmp;            // stage layout, INT8 mode only
   int bm_gu, bm_dn;
   int64_t mt_gu, mt_dn;
 };
 
-void carve_stage(const qre_desc& d, Carver& c, StageLayout& L) {
+void carve_stage(const qre_desc& d, Carver& c, StageLayout& L, bool stage) {
   const int64_t S = (int64_t)d.T * d.K;
   L.bm_gu = gemm_tile_rows(S, d.E, 2 * d.I, d.H);
   L.bm_dn = gemm_tile_rows(S, d.E, d.H, d.I);
   L.mt_gu = max_tiles(S, d.E, L.bm_gu);
   L.mt_dn = max_tiles(S, d.E, L.bm_dn);
+  L.header = c.take<int32_t>(kHeaderInts);
   L.ntiles = c.take<int32_t>(2);
   L.tiles_gu = c.take<Tile>(L.mt_gu);
   L.tiles_dn = c.take<Tile>(L.mt_dn);
   L.route_scratch = c.take<uint8_t>(route_scratch_bytes(S, d.E));
+  L.h_tmp = (stage && d.act_int8) ? c.take<uint16_t>((size_t)S * d.I) : nullptr;
 }
 
 struct Layout {
@@ -76,7 +87,7 @@ Layout make_layout(const qre_desc& d, void* ws) {
   Layout L;
   const int64_t S = (int64_t)d.T * d.K;
   Carver c(ws);
-  carve_stage(d, c, L.st);
+  carve_stage(d, c, L.st, false);
   L.counts = c.take<int32_t>(d.E);
   L.offsets = c.take<int32_t>(d.E + 1);
   L.sorted_slot = c.take<int32_t>(S);
@@ -97,16 +108,19 @@ Layout make_layout(const qre_desc& d, void* ws) {
 size_t stage_bytes(const qre_desc& d) {
   Carver c(nullptr);
   StageLayout L;
-  carve_stage(d, c, L);
+  carve_stage(d, c, L, true);
   return c.off;
 }
 
 StageLayout stage_layout(const qre_desc& d, const void* ws) {
   Carver c(const_cast<void*>(ws));
   StageLayout L;
-  carve_stage(d, c, L);
+  carve_stage(d, c, L, true);
   return L;
 }
+
+// Routing alone: the header, then the routing scratch.
+size_t route_bytes(int64_t S, int E) { return kHeaderInts * sizeof(int32_t) + align_up(route_scratch_bytes(S, E)); }
 
 int check_desc(const qre_desc* d) {
   if (!d) return QRE_ERR_NULL;
@@ -251,11 +265,11 @@ static int moe_forward_impl(const qre_desc* desc, const void* x, const int32_t* 
   // Decode-sized problems: the permutation is folded into the gate/up kernel;
   // otherwise the routing kernel builds it (and the row-tile lists).
   const bool routed = routed_applicable(S, d.E, d.H, d.I, d.act_int8);
-  const RouteOut ro = {topk_ids, (int)S, d.E, L.counts, L.offsets, L.sorted_slot, L.slot_row};
+  const RouteOut ro = {topk_ids, (int)S, d.E, L.counts, L.offsets, L.sorted_slot, L.slot_row, st.header};
   hipError_t e = mark(0);
   if (e == hipSuccess && !routed)
-    e = launch_route(topk_ids, d.T, d.K, d.E, L.counts, L.offsets, L.sorted_slot, L.slot_row, st.route_scratch,
-                     st.tiles_gu, st.ntiles, st.bm_gu, st.tiles_dn, st.ntiles + 1, st.bm_dn, s);
+    e = launch_route(topk_ids, d.T, d.K, d.E, L.counts, L.offsets, L.sorted_slot, L.slot_row, st.header,
+                     st.route_scratch, st.tiles_gu, st.ntiles, st.bm_gu, st.tiles_dn, st.ntiles + 1, st.bm_dn, s);
   if (e == hipSuccess && d.act_int8) e = launch_quantize_act(static_cast<const uint16_t*>(x), d.T, d.H, L.xq, L.xs, s);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = routed ? launch_gate_up_routed(gu, ro, s) : launch_gemm(gu, s);
@@ -297,24 +311,15 @@ int qre_workspace_permutation(const qre_desc* desc, void* workspace, int32_t** c
   return QRE_OK;
 }
 
-int qre_read_dropped_slots(const qre_desc* desc, const void* workspace, int32_t* n_dropped, qre_stream_t stream) {
-  int rc = check_desc(desc);
-  if (rc) return rc;
-  if (!n_dropped) return QRE_ERR_NULL;
-  const qre_desc& d = *desc;
-  const int64_t S = (int64_t)d.T * d.K;
-  if (S == 0) {
-    *n_dropped = 0;
-    return QRE_OK;
-  }
-  if (!workspace) return QRE_ERR_NULL;
-  const Layout L = make_layout(d, const_cast<void*>(workspace));
-  int32_t valid = 0;
+int qre_read_device_error(const void* workspace, int32_t* n_bad_ids, qre_stream_t stream) {
+  if (!workspace || !n_bad_ids) return QRE_ERR_NULL;
+  if (!aligned16(workspace)) return QRE_ERR_ALIGN;
+  int32_t n = 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(&valid, L.offsets + d.E, sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  hipError_t e = hipMemcpyAsync(&n, workspace, sizeof(int32_t), hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_status(e);
-  *n_dropped = (int32_t)(S - valid);
+  *n_bad_ids = n;
   return QRE_OK;
 }
 
@@ -325,39 +330,32 @@ static int check_stage_ws(const qre_desc& d, const void* workspace, size_t works
   return QRE_OK;
 }
 
-int qre_route(const qre_desc* desc, const int32_t* topk_ids, int32_t* counts, int32_t* offsets,
+int qre_route_workspace_bytes(int32_t T, int32_t K, int32_t E, size_t* bytes) {
+  if (!bytes) return QRE_ERR_NULL;
+  if (T < 0 || K <= 0 || E <= 0 || K > E) return QRE_ERR_SHAPE;
+  if (E > QRE_MAX_EXPERTS || (int64_t)T * K >= (1ll << 31)) return QRE_ERR_LIMIT;
+  *bytes = route_bytes((int64_t)T * K, E);
+  return QRE_OK;
+}
+
+int qre_route(const int32_t* topk_ids, int32_t T, int32_t K, int32_t E, int32_t* counts, int32_t* offsets,
               int32_t* sorted_slot, int32_t* slot_row, void* workspace, size_t workspace_bytes,
               qre_stream_t stream) {
-  int rc = check_desc(desc);
+  size_t need = 0;
+  int rc = qre_route_workspace_bytes(T, K, E, &need);
   if (rc) return rc;
-  const qre_desc& d = *desc;
-  if (!counts || !offsets) return QRE_ERR_NULL;
-  if (!aligned16(counts) || !aligned16(offsets)) return QRE_ERR_ALIGN;
-  const int64_t S = (int64_t)d.T * d.K;
+  if (!counts || !offsets || !workspace) return QRE_ERR_NULL;
+  if (!aligned16(counts) || !aligned16(offsets) || !aligned16(workspace)) return QRE_ERR_ALIGN;
+  const int64_t S = (int64_t)T * K;
   if (S > 0) {
     if (!topk_ids || !sorted_slot || !slot_row) return QRE_ERR_NULL;
     if (!aligned16(topk_ids) || !aligned16(sorted_slot) || !aligned16(slot_row)) return QRE_ERR_ALIGN;
   }
-  rc = check_stage_ws(d, workspace, workspace_bytes);
-  if (rc) return rc;
-  const StageLayout st = stage_layout(d, workspace);
-  return hip_status(launch_route(topk_ids, d.T, d.K, d.E, counts, offsets, sorted_slot, slot_row, st.route_scratch,
-                                 st.tiles_gu, st.ntiles, st.bm_gu, st.tiles_dn, st.ntiles + 1, st.bm_dn,
-                                 reinterpret_cast<hipStream_t>(stream)));
-}
-
-int qre_build_tiles(const qre_desc* desc, const int32_t* offsets, void* workspace, size_t workspace_bytes,
-                    qre_stream_t stream) {
-  int rc = check_desc(desc);
-  if (rc) return rc;
-  const qre_desc& d = *desc;
-  if (!offsets) return QRE_ERR_NULL;
-  if (!aligned16(offsets)) return QRE_ERR_ALIGN;
-  rc = check_stage_ws(d, workspace, workspace_bytes);
-  if (rc) return rc;
-  const StageLayout st = stage_layout(d, workspace);
-  return hip_status(launch_build_tiles(offsets, d.E, st.tiles_gu, st.ntiles, st.bm_gu, st.tiles_dn, st.ntiles + 1,
-                                       st.bm_dn, reinterpret_cast<hipStream_t>(stream)));
+  if (workspace_bytes < need) return QRE_ERR_WORKSPACE;
+  int32_t* header = static_cast<int32_t*>(workspace);
+  void* scratch = static_cast<uint8_t*>(workspace) + kHeaderInts * sizeof(int32_t);
+  return hip_status(launch_route(topk_ids, T, K, E, counts, offsets, sorted_slot, slot_row, header, scratch,
+                                 nullptr, nullptr, 0, nullptr, nullptr, 0, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int qre_quantize_act(const void* v, int32_t rows, int32_t cols, int8_t* q, float* s, qre_stream_t stream) {
@@ -383,8 +381,8 @@ int qre_quantize_weights(const float* w, int64_t rows, int64_t cols, int32_t bit
 }
 
 int qre_gate_up(const qre_desc* desc, const void* x, const int8_t* xq, const float* xs, const int32_t* sorted_slot,
-                const qre_weights* weights, void* h, const void* workspace, size_t workspace_bytes,
-                qre_stream_t stream) {
+                const int32_t* offsets, const qre_weights* weights, void* h, int8_t* hq, float* hs, void* workspace,
+                size_t workspace_bytes, qre_stream_t stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
   const qre_desc& d = *desc;
@@ -392,20 +390,30 @@ int qre_gate_up(const qre_desc* desc, const void* x, const int8_t* xq, const flo
   rc = check_stage_ws(d, workspace, workspace_bytes);
   if (rc) return rc;
   if (d.act_int8 ? (!xq || !xs) : !x) return QRE_ERR_MODE;
-  if (!sorted_slot || !h) return QRE_ERR_NULL;
+  if (!d.act_int8 && (hq || hs)) return QRE_ERR_MODE;
+  if (d.act_int8 && ((hq == nullptr) != (hs == nullptr))) return QRE_ERR_MODE;
+  if (!sorted_slot || !offsets) return QRE_ERR_NULL;
+  if (!h && !hq) return QRE_ERR_NULL;
   rc = check_weights(weights, true, false);
   if (rc) return rc;
   if (!aligned16(d.act_int8 ? (const void*)xq : x) || (d.act_int8 && !aligned16(xs)) || !aligned16(sorted_slot) ||
-      !aligned16(h))
+      !aligned16(offsets) || (h && !aligned16(h)) || (hq && (!aligned16(hq) || !aligned16(hs))))
     return QRE_ERR_ALIGN;
   const StageLayout st = stage_layout(d, workspace);
-  return hip_status(launch_gemm(gate_up_problem(d, x, xq, xs, sorted_slot, *weights, st.tiles_gu, st.ntiles, st.mt_gu,
-                                                st.bm_gu, h),
-                                reinterpret_cast<hipStream_t>(stream)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* hout = h ? h : st.h_tmp;
+  hipError_t e = launch_build_tiles(offsets, d.E, st.tiles_gu, st.ntiles, st.bm_gu, nullptr, nullptr, 0, s);
+  if (e == hipSuccess)
+    e = launch_gemm(gate_up_problem(d, x, xq, xs, sorted_slot, *weights, st.tiles_gu, st.ntiles, st.mt_gu, st.bm_gu,
+                                    hout),
+                    s);
+  if (e == hipSuccess && hq)
+    e = launch_quantize_act(static_cast<const uint16_t*>(hout), (int)((int64_t)d.T * d.K), d.I, hq, hs, s);
+  return hip_status(e);
 }
 
-int qre_down(const qre_desc* desc, const void* h, const int8_t* hq, const float* hs, const qre_weights* weights,
-             void* y, const void* workspace, size_t workspace_bytes, qre_stream_t stream) {
+int qre_down(const qre_desc* desc, const void* h, const int8_t* hq, const float* hs, const int32_t* offsets,
+             const qre_weights* weights, void* y, void* workspace, size_t workspace_bytes, qre_stream_t stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
   const qre_desc& d = *desc;
@@ -413,15 +421,18 @@ int qre_down(const qre_desc* desc, const void* h, const int8_t* hq, const float*
   rc = check_stage_ws(d, workspace, workspace_bytes);
   if (rc) return rc;
   if (d.act_int8 ? (!hq || !hs) : !h) return QRE_ERR_MODE;
-  if (!y) return QRE_ERR_NULL;
+  if (!y || !offsets) return QRE_ERR_NULL;
   rc = check_weights(weights, false, true);
   if (rc) return rc;
-  if (!aligned16(d.act_int8 ? (const void*)hq : h) || (d.act_int8 && !aligned16(hs)) || !aligned16(y))
+  if (!aligned16(d.act_int8 ? (const void*)hq : h) || (d.act_int8 && !aligned16(hs)) || !aligned16(y) ||
+      !aligned16(offsets))
     return QRE_ERR_ALIGN;
   const StageLayout st = stage_layout(d, workspace);
-  return hip_status(launch_gemm(down_problem(d, h, hq, hs, *weights, st.tiles_dn, st.ntiles + 1, st.mt_dn, st.bm_dn,
-                                             y),
-                                reinterpret_cast<hipStream_t>(stream)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_build_tiles(offsets, d.E, st.tiles_dn, st.ntiles + 1, st.bm_dn, nullptr, nullptr, 0, s);
+  if (e == hipSuccess)
+    e = launch_gemm(down_problem(d, h, hq, hs, *weights, st.tiles_dn, st.ntiles + 1, st.mt_dn, st.bm_dn, y), s);
+  return hip_status(e);
 }
 
 int qre_combine(const void* y, const int32_t* slot_row, const float* topk_w, int32_t T, int32_t K, int32_t H,

@@ -49,10 +49,12 @@ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; 
 // build for up to two GEMM row-tile heights; the large variant is three kernels.
 // `ws` (route scratch) must hold route_scratch_bytes(S, E) bytes.
 size_t route_scratch_bytes(int64_t S, int E);
+// `dropped` (may be null) receives S - offsets[E], the slots whose id was
+// outside [0, E).  Either tile list may be null.
 hipError_t launch_route(const int32_t* ids, int T, int K, int E, int32_t* counts, int32_t* offsets,
-                        int32_t* sorted_slot, int32_t* slot_row, void* ws, Tile* tiles_a, int32_t* ntiles_a,
-                        int bm_a, Tile* tiles_b, int32_t* ntiles_b, int bm_b, hipStream_t stream);
-// Tile list from offsets alone (used by the stage entry points).
+                        int32_t* sorted_slot, int32_t* slot_row, int32_t* dropped, void* ws, Tile* tiles_a,
+                        int32_t* ntiles_a, int bm_a, Tile* tiles_b, int32_t* ntiles_b, int bm_b, hipStream_t stream);
+// Tile list from offsets alone (used by the stage entry points); tiles_b may be null.
 hipError_t launch_build_tiles(const int32_t* offsets, int E, Tile* tiles_a, int32_t* ntiles_a, int bm_a,
                               Tile* tiles_b, int32_t* ntiles_b, int bm_b, hipStream_t stream);
 // Upper bound on the number of row tiles of height bm over S sorted rows and E experts.
@@ -94,6 +96,7 @@ struct RouteOut {
   const int32_t* ids;
   int S, E;
   int32_t *counts, *offsets, *sorted_slot, *slot_row;
+  int32_t* dropped;       // S - offsets[E]
 };
 constexpr int64_t kRoutedMaxSlots = 2048;
 bool routed_applicable(int64_t S, int E, int H, int I, int act_int8);

@@ -204,7 +204,7 @@ template <int NW>
 __global__ __launch_bounds__(NW * kWave) void k_route_small(const int32_t* __restrict__ ids, int S, int E,
                                                             int nbits, int32_t* counts, int32_t* offsets,
                                                             int32_t* sorted_slot, int32_t* slot_row,
-                                                            Tile* tiles_a, int32_t* ntiles_a, int bm_a,
+                                                            int32_t* dropped, Tile* tiles_a, int32_t* ntiles_a, int bm_a,
                                                             Tile* tiles_b, int32_t* ntiles_b, int bm_b) {
   extern __shared__ int lds[];
   int* hist = lds;                 // [NW][E]
@@ -234,7 +234,10 @@ __global__ __launch_bounds__(NW * kWave) void k_route_small(const int32_t* __res
   }
   __syncthreads();
   const int total = block_exclusive_scan(offs, E, wave_tmp);
-  if (tid == 0) offs[E] = total;
+  if (tid == 0) {
+    offs[E] = total;
+    if (dropped) *dropped = S - total;
+  }
   __syncthreads();
   for (int e = tid; e <= E; e += blockDim.x) {
     offsets[e] = offs[e];
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(256) void k_route_prefix(int32_t* ghist, int nwaves
 // wave_tmp[4].
 __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict__ ids, int S, int E, int nbits,
                                                        const int32_t* ghist, const int32_t* counts, int32_t* offsets,
-                                                       Tile* tiles_a, int32_t* ntiles_a, int bm_a, Tile* tiles_b,
+                                                       int32_t* dropped, Tile* tiles_a, int32_t* ntiles_a, int bm_a, Tile* tiles_b,
                                                        int32_t* ntiles_b, int bm_b, int32_t* sorted_slot,
                                                        int32_t* slot_row) {
   extern __shared__ int lds[];
@@ -344,6 +347,7 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict
   __syncthreads();
   if (blockIdx.x == 0) {           // uniform over the workgroup
     for (int e = tid; e <= E; e += blockDim.x) offsets[e] = offs[e];
+    if (tid == 0 && dropped) *dropped = S - total;
     if (tiles_a && tiles_b && bm_a == bm_b) {
       build_tiles(cnt, offs, E, bm_a, scratch, wave_tmp, tiles_a, ntiles_a, tiles_b, ntiles_b);
     } else {
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(256) void k_build_tiles(const int32_t* offsets, int
   }
   __syncthreads();
   build_tiles(cnt, offs, E, bm_a, scratch, wave_tmp, tiles_a, ntiles_a);
-  build_tiles(cnt, offs, E, bm_b, scratch, wave_tmp, tiles_b, ntiles_b);
+  if (tiles_b) build_tiles(cnt, offs, E, bm_b, scratch, wave_tmp, tiles_b, ntiles_b);
 }
 
 int bits_for(int E) {
@@ -400,15 +404,15 @@ int64_t max_tiles(int64_t S, int E, int bm) {
 }
 
 hipError_t launch_route(const int32_t* ids, int T, int K, int E, int32_t* counts, int32_t* offsets,
-                        int32_t* sorted_slot, int32_t* slot_row, void* ws, Tile* tiles_a, int32_t* ntiles_a,
-                        int bm_a, Tile* tiles_b, int32_t* ntiles_b, int bm_b, hipStream_t stream) {
+                        int32_t* sorted_slot, int32_t* slot_row, int32_t* dropped, void* ws, Tile* tiles_a,
+                        int32_t* ntiles_a, int bm_a, Tile* tiles_b, int32_t* ntiles_b, int bm_b, hipStream_t stream) {
   const int64_t S = (int64_t)T * K;
   const int nbits = bits_for(E);
   if (S <= 512) {
     constexpr int NW = 4;
     const size_t lds = sizeof(int) * (size_t)(NW * E + 3 * E + 1 + NW);
     hipLaunchKernelGGL(k_route_small<NW>, dim3(1), dim3(NW * kWave), lds, stream, ids, (int)S, E, nbits, counts,
-                       offsets, sorted_slot, slot_row, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b);
+                       offsets, sorted_slot, slot_row, dropped, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b);
     return hipGetLastError();
   }
   // the one-workgroup kernel holds at most kSmallRows rows of 64 slots per
@@ -418,7 +422,7 @@ hipError_t launch_route(const int32_t* ids, int T, int K, int E, int32_t* counts
     constexpr int NW = 16;
     const size_t lds = sizeof(int) * (size_t)(NW * E + 3 * E + 1 + NW);
     hipLaunchKernelGGL(k_route_small<NW>, dim3(1), dim3(NW * kWave), lds, stream, ids, (int)S, E, nbits, counts,
-                       offsets, sorted_slot, slot_row, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b);
+                       offsets, sorted_slot, slot_row, dropped, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b);
     return hipGetLastError();
   }
   int32_t* ghist = static_cast<int32_t*>(ws);
@@ -433,7 +437,7 @@ hipError_t launch_route(const int32_t* ids, int T, int K, int E, int32_t* counts
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_route_scatter, dim3(nblocks), dim3(256), sizeof(int) * (size_t)(7 * E + 5), stream, ids,
-                     (int)S, E, nbits, ghist, counts, offsets, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b,
+                     (int)S, E, nbits, ghist, counts, offsets, dropped, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b,
                      sorted_slot, slot_row);
   return hipGetLastError();
 }

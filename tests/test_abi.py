@@ -83,8 +83,18 @@ def test_forward_argument_errors_need_no_gpu():
     assert L.qre_quantize_act(P(16), 4, 100, P(16), P(16), None) == -2
     assert L.qre_quantize_weights(P(16), 4, 256, 3, P(16), P(16), None) == -3
     assert L.qre_combine(P(16), P(16), P(16), 4, 2, 100, P(16), None) == -2
-    assert L.qre_gate_up(C.byref(_desc(act_int8=1)), P(16), None, None, P(16), C.byref(w), P(16), P(16),
-                         1 << 24, None) == -8
+    # INT8 mode without xq/xs; hq/hs in BF16 mode; only one of hq/hs
+    assert L.qre_gate_up(C.byref(_desc(act_int8=1)), P(16), None, None, P(16), P(16), C.byref(w), P(16), None, None,
+                         P(16), 1 << 30, None) == -8
+    assert L.qre_gate_up(C.byref(_desc()), P(16), None, None, P(16), P(16), C.byref(w), P(16), P(16), P(16),
+                         P(16), 1 << 30, None) == -8
+    assert L.qre_gate_up(C.byref(_desc(act_int8=1)), None, P(16), P(16), P(16), P(16), C.byref(w), P(16), P(16), None,
+                         P(16), 1 << 30, None) == -8
+    # offsets are required; the workspace must hold the row tiles
+    assert L.qre_gate_up(C.byref(_desc()), P(16), None, None, P(16), None, C.byref(w), P(16), None, None,
+                         P(16), 1 << 30, None) == -1
+    assert L.qre_down(C.byref(_desc()), P(16), None, None, None, C.byref(w), P(16), P(16), 1 << 30, None) == -1
+    assert L.qre_down(C.byref(_desc()), P(16), None, None, P(16), C.byref(w), P(16), P(16), 16, None) == -6
     # router: K > E, limits, null, misaligned, empty
     assert L.qre_topk_softmax(P(16), 4, 8, 9, P(16), P(16), None) == -2
     assert L.qre_topk_softmax(P(16), 4, 8, 0, P(16), P(16), None) == -2
@@ -93,9 +103,13 @@ def test_forward_argument_errors_need_no_gpu():
     assert L.qre_topk_softmax(None, 4, 256, 8, P(16), P(16), None) == -1
     assert L.qre_topk_softmax(P(16), 4, 256, 8, P(20), P(16), None) == -5
     assert L.qre_topk_softmax(None, 0, 256, 8, None, None, None) == 0
-    d8k = _desc(T=8192)
-    assert L.qre_route(C.byref(d8k), P(16), P(16), P(16), P(16), P(16), None, 0, None) == -1   # needs workspace
+    # routing: needs its workspace (large slot counts use routing scratch)
+    assert L.qre_route(P(16), 8192, 8, 256, P(16), P(16), P(16), P(16), None, 0, None) == -1
     n = C.c_size_t(0)
-    assert L.qre_stage_workspace_bytes(C.byref(d8k), C.byref(n)) == 0
-    assert L.qre_route(C.byref(d8k), P(16), P(16), P(16), P(16), P(16), P(16), n.value - 1, None) == -6
-    assert L.qre_build_tiles(C.byref(d8k), P(16), P(16), n.value - 1, None) == -6
+    assert L.qre_route_workspace_bytes(8192, 8, 256, C.byref(n)) == 0 and n.value > 256
+    assert L.qre_route(P(16), 8192, 8, 256, P(16), P(16), P(16), P(16), P(16), n.value - 1, None) == -6
+    assert L.qre_route_workspace_bytes(4, 9, 8, C.byref(n)) == -2          # K > E
+    assert L.qre_route_workspace_bytes(4, 8, 1024, C.byref(n)) == -9       # E > QRE_MAX_EXPERTS
+    # the device-error read needs a workspace
+    assert L.qre_read_device_error(None, P(16), None) == -1
+    assert L.qre_read_device_error(P(20), P(16), None) == -5

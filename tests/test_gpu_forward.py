@@ -16,10 +16,10 @@ import torch
 
 import oracle
 import quantized_routed_expert_top_amd as qre
-from quantized_routed_expert_top_amd.inputs import (WORKLOADS, Workload, gen_routing, gen_x, sample_tokens,
-                                                    topk_softmax, f32_to_bf16_bits)
-from quantized_routed_expert_top_amd.synthetic import gpu_experts, touched_experts, x_tensor
-from gpu_helpers import assert_parity, bf16_np, oracle_experts, to_gpu_experts
+from harness.inputs import (WORKLOADS, Workload, gen_routing, gen_x, sample_tokens, topk_softmax,
+                            f32_to_bf16_bits)
+from harness.synthetic import gpu_experts, touched_experts, x_tensor
+from gpu_helpers import assert_forward_parity, bf16_np, oracle_experts, to_gpu_experts
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -40,9 +40,9 @@ def _check(wl: Workload, tokens=None, x_bits=None, ids=None, w=None, Wg=None, Wo
     if Wg is None:
         Wg = to_gpu_experts(Wo, wl.weight_bits) if tokens is None else gpu_experts(wl, DEV)
     out = bf16_np(_run_gpu(x_bits, ids, w, Wg, wl.act_int8))
-    ref32, _, _ = oracle.moe_forward(x_bits, ids, w, Wo, E=wl.E, bits=wl.weight_bits, act_int8=wl.act_int8,
-                                     tokens=None if tokens is None else toks)
-    return assert_parity(out[toks], ref32, what=wl.name)
+    ref32, _, _, y_tok = oracle.moe_forward(x_bits, ids, w, Wo, E=wl.E, bits=wl.weight_bits, act_int8=wl.act_int8,
+                                            tokens=None if tokens is None else toks, return_y=True)
+    return assert_forward_parity(out[toks], ref32, y_tok, w[toks], what=wl.name)
 
 
 SMALL = [
@@ -51,7 +51,7 @@ SMALL = [
     Workload("small_c", T=100, H=256, I=128, E=16, K=4, weight_bits=4, act_int8=True, seed=13),
     Workload("small_d", T=77, H=640, I=256, E=12, K=6, weight_bits=8, act_int8=True, seed=14,
              outlier_frac=0.02),
-    # more than 2048 slots: the separate routing launch and the row-tile GEMMs
+    # more than 2048 slots: the separate routing launch and the 8-row tile GEMMs
     Workload("small_e", T=300, H=256, I=128, E=16, K=8, weight_bits=4, act_int8=False, seed=15),
     Workload("small_f", T=260, H=384, I=256, E=20, K=8, weight_bits=8, act_int8=True, seed=16),
     # reductions that are multiples of 512 (permutation folded into gate/up;
@@ -112,6 +112,23 @@ def test_full_size_workload_sampled(name):
     print(f"  {name}: {st}", flush=True)
 
 
+@pytest.mark.parametrize("bits,a8", [(4, False), (8, False), (4, True), (8, True)])
+def test_decode_block_wide_hidden(bits, a8):
+    """A 32-token block at H = 4096, I = 1536: the decode gate/up kernel with
+    a 32-group reduction (permutation folded in), every output compared."""
+    wl = Workload("dec_h4096", T=32, H=4096, I=1536, E=64, K=8, weight_bits=bits, act_int8=a8, seed=41)
+    _check(wl)
+
+
+@pytest.mark.parametrize("bits,a8", [(4, False), (8, False), (4, True), (8, True)])
+def test_batched_blocks_wide_hidden_sampled(bits, a8):
+    """Sixteen 32-token blocks at H = 4096, I = 1536, E = 256: the gate/up
+    row tiles (4096-wide reduction) run the split-reduction kernel; sampled
+    tokens (first and last included)."""
+    wl = Workload("cb_h4096", T=512, H=4096, I=1536, E=256, K=8, weight_bits=bits, act_int8=a8, seed=42)
+    _check(wl, tokens=sample_tokens(wl.T, 8, seed=2))
+
+
 def test_decode_modes_at_full_size():
     """The decode shape in the three other weight/activation modes."""
     for bits, a8 in ((8, False), (4, True), (8, True)):
@@ -142,7 +159,7 @@ def test_edge_cases():
     ws = torch.empty(qre.workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.K, 4), dtype=torch.uint8, device=DEV)
     qre.moe_forward(x_tensor(x_bits, DEV), torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV), Wg,
                     workspace=ws)
-    assert qre.read_dropped_slots(wl.T, wl.H, wl.I, wl.E, wl.K, 4, False, ws) == 3
+    assert qre.read_device_error(ws) == 3
     # the same at a reduction of 4 groups, INT8 weights
     wl_st = Workload("dup_st", T=40, H=512, I=256, E=6, K=3, weight_bits=8, act_int8=False, seed=24)
     ids_st, w_st = gen_routing(wl_st)
@@ -181,7 +198,7 @@ def test_invariances_decode_shape():
     (32, 2048, 512, 256, 8, 4, True),      # the same with INT8 activations
     (40, 256, 128, 6, 3, 8, True),
     (300, 256, 128, 16, 8, 4, False),      # > 2048 slots: separate routing launch
-    (300, 512, 512, 64, 8, 4, True),       # > 2048 slots, split-reduction expert kernels
+    (300, 512, 512, 64, 8, 4, True),       # > 2048 slots, 16-row tile kernels
 ])
 def test_forward_permutation_matches_oracle(T, H, I, E, K, bits, a8):
     """The permutation a forward call leaves in its workspace equals the
@@ -202,4 +219,4 @@ def test_forward_permutation_matches_oracle(T, H, I, E, K, bits, a8):
     ref = oracle.route(ids, E)
     for g, r in zip(got, ref[:4]):
         np.testing.assert_array_equal(g, r)
-    assert qre.read_dropped_slots(T, H, I, E, K, bits, a8, ws) == ref[4] == 2
+    assert qre.read_device_error(ws) == ref[4] == 2

@@ -8,8 +8,8 @@ import torch
 
 import oracle
 import quantized_routed_expert_top_amd as qre
-from quantized_routed_expert_top_amd.inputs import WORKLOADS, Workload, gen_router_logits, gen_x
-from gpu_helpers import assert_parity, bf16_np, oracle_experts, to_gpu_experts
+from harness.inputs import WORKLOADS, Workload, gen_router_logits, gen_x
+from gpu_helpers import assert_forward_parity, bf16_np, oracle_experts, to_gpu_experts
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -83,13 +83,13 @@ def test_router_feeds_forward():
     ids_ref, w_ref = oracle.topk_softmax(logits, wl.K)
     Wo = oracle_experts(wl, range(wl.E))
     x_bits = gen_x(wl)
-    ref32, _, _ = oracle.moe_forward(x_bits, ids_ref, w_ref, Wo, E=wl.E, bits=wl.weight_bits)
+    ref32, _, _, y_tok = oracle.moe_forward(x_bits, ids_ref, w_ref, Wo, E=wl.E, bits=wl.weight_bits, return_y=True)
     ids, w = qre.topk_softmax(torch.from_numpy(logits).to(DEV), wl.K)
     x = torch.from_numpy(x_bits.view(np.int16)).to(DEV).view(torch.bfloat16)
     out = qre.moe_forward(x, ids, w, to_gpu_experts(Wo, wl.weight_bits, DEV))
     torch.cuda.synchronize()
     np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
-    assert_parity(bf16_np(out), ref32, what="router_ffn")
+    assert_forward_parity(bf16_np(out), ref32, y_tok, w_ref, what="router_ffn")
 
 
 def test_router_non_finite_logits_keep_ids_valid():

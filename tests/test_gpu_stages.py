@@ -9,8 +9,8 @@ import torch
 
 import oracle
 import quantized_routed_expert_top_amd as qre
-from quantized_routed_expert_top_amd.inputs import Workload, f32_to_bf16_bits, topk_softmax
-from gpu_helpers import assert_parity, bf16_np, bf16_to_f64, oracle_experts, to_gpu_experts
+from harness.inputs import Workload, f32_to_bf16_bits, topk_softmax
+from gpu_helpers import assert_parity, assert_rounding_level, bf16_np, bf16_to_f64, oracle_experts, to_gpu_experts
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -111,6 +111,12 @@ STAGE_SHAPES = [
     (64, 512, 256, 8, 2),
     (45, 384, 128, 5, 3),
     (32, 2048, 512, 256, 8),
+    # reductions of 6 and 7 groups, and a 4096-wide one whose 16-row
+    # activation tile exceeds 64 KB: the split-reduction kernel (16- and
+    # 8-row tiles)
+    (40, 768, 896, 8, 2),
+    (12, 896, 768, 8, 2),
+    (48, 4096, 256, 6, 2),
 ]
 
 
@@ -134,25 +140,32 @@ def test_gate_up_and_down_stages(shape, bits, act_int8):
     shp = dict(T=T, H=H, I=I, E=E, K=K, bits=bits)
     Wg = to_gpu_experts(Wo, bits)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
-    ws = qre.build_tiles(t(offsets), T, H, I, E, K, bits, act_int8)
     nvalid = int(offsets[-1])
     if act_int8:
         xq, xs = oracle.quantize_act(x)
         h_ref = oracle.gate_up(None, sorted_slot, offsets, Wo, act_int8=True, xq=xq, xs=xs, **shp)
-        h_gpu = qre.gate_up(None, t(sorted_slot), Wg, K, ws, act_int8=True, xq=t(xq), xs=t(xs))
+        h_gpu, hq_gpu, hs_gpu = qre.gate_up(None, t(sorted_slot), t(offsets), Wg, K, act_int8=True, xq=t(xq),
+                                            xs=t(xs), want_hq=True)
+        # the h quantization gate/up writes equals the quantizer applied to its h
+        hq2, hs2 = qre.quantize_act(h_gpu)
+        np.testing.assert_array_equal(hq_gpu.cpu().numpy()[:nvalid], hq2.cpu().numpy()[:nvalid])
+        np.testing.assert_array_equal(hs_gpu.cpu().numpy()[:nvalid], hs2.cpu().numpy()[:nvalid])
     else:
         h_ref = oracle.gate_up(x, sorted_slot, offsets, Wo, **shp)
-        h_gpu = qre.gate_up(t(x.view(np.int16)).view(torch.bfloat16), t(sorted_slot), Wg, K, ws)
-    assert_parity(bf16_np(h_gpu)[:nvalid], bf16_to_f64(h_ref[:nvalid]), what="h")
+        h_gpu = qre.gate_up(t(x.view(np.int16)).view(torch.bfloat16), t(sorted_slot), t(offsets), Wg, K)
+    tag = f"{shape} W{bits}A{8 if act_int8 else 16}"
+    assert_parity(bf16_np(h_gpu)[:nvalid], bf16_to_f64(h_ref[:nvalid]), what=f"h {tag}")
+    assert_rounding_level(bf16_np(h_gpu)[:nvalid], h_ref[:nvalid], what=f"h {tag}")
     # down, fed the oracle's h
     if act_int8:
         hq, hs = oracle.quantize_act(h_ref)
         y_ref = oracle.down(None, offsets, Wo, act_int8=True, hq=hq, hs=hs, **shp)
-        y_gpu = qre.down(None, Wg, T, K, ws, act_int8=True, hq=t(hq), hs=t(hs))
+        y_gpu = qre.down(None, t(offsets), Wg, T, K, act_int8=True, hq=t(hq), hs=t(hs))
     else:
         y_ref = oracle.down(h_ref, offsets, Wo, **shp)
-        y_gpu = qre.down(t(h_ref.view(np.int16)).view(torch.bfloat16), Wg, T, K, ws)
-    assert_parity(bf16_np(y_gpu)[:nvalid], bf16_to_f64(y_ref[:nvalid]), what="y")
+        y_gpu = qre.down(t(h_ref.view(np.int16)).view(torch.bfloat16), t(offsets), Wg, T, K)
+    assert_parity(bf16_np(y_gpu)[:nvalid], bf16_to_f64(y_ref[:nvalid]), what=f"y {tag}")
+    assert_rounding_level(bf16_np(y_gpu)[:nvalid], y_ref[:nvalid], what=f"y {tag}")
 
 
 @pytest.mark.parametrize("act_int8", [False, True])
@@ -194,15 +207,14 @@ def test_gemm_exact_arithmetic_case(bits, act_int8):
     shp = dict(T=T, H=H, I=I, E=E, K=K, bits=bits)
     Wg = to_gpu_experts(Wo, bits)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
-    ws = qre.build_tiles(t(offsets), T, H, I, E, K, bits, act_int8)
     if act_int8:
         xq, xs = oracle.quantize_act(x)
         assert np.all(xs == 2.0 ** -2)
         h_ref = oracle.gate_up(None, sorted_slot, offsets, Wo, act_int8=True, xq=xq, xs=xs, **shp)
-        h_gpu = qre.gate_up(None, t(sorted_slot), Wg, K, ws, act_int8=True, xq=t(xq), xs=t(xs))
+        h_gpu = qre.gate_up(None, t(sorted_slot), t(offsets), Wg, K, act_int8=True, xq=t(xq), xs=t(xs))
     else:
         h_ref = oracle.gate_up(x, sorted_slot, offsets, Wo, **shp)
-        h_gpu = qre.gate_up(t(x.view(np.int16)).view(torch.bfloat16), t(sorted_slot), Wg, K, ws)
+        h_gpu = qre.gate_up(t(x.view(np.int16)).view(torch.bfloat16), t(sorted_slot), t(offsets), Wg, K)
     assert np.mean(bf16_to_f64(h_ref) != 0) > 0.5
     np.testing.assert_array_equal(bf16_np(h_gpu), h_ref)
     # down on an exactly representable h (INT8 grid of scale 2^-3)
@@ -212,10 +224,10 @@ def test_gemm_exact_arithmetic_case(bits, act_int8):
     if act_int8:
         hq, hs = oracle.quantize_act(hb)
         y_ref = oracle.down(None, offsets, Wo, act_int8=True, hq=hq, hs=hs, **shp)
-        y_gpu = qre.down(None, Wg, T, K, ws, act_int8=True, hq=t(hq), hs=t(hs))
+        y_gpu = qre.down(None, t(offsets), Wg, T, K, act_int8=True, hq=t(hq), hs=t(hs))
     else:
         y_ref = oracle.down(hb, offsets, Wo, **shp)
-        y_gpu = qre.down(t(hb.view(np.int16)).view(torch.bfloat16), Wg, T, K, ws)
+        y_gpu = qre.down(t(hb.view(np.int16)).view(torch.bfloat16), t(offsets), Wg, T, K)
     np.testing.assert_array_equal(bf16_np(y_gpu), y_ref)
 
 
@@ -239,6 +251,54 @@ def test_extreme_codes_decode(bits):
     shp = dict(T=T, H=H, I=I, E=1, K=1, bits=bits)
     h_ref = oracle.gate_up(x, sorted_slot, offsets, Wo, **shp)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
-    ws = qre.build_tiles(t(offsets), T, H, I, 1, 1, bits)
-    h_gpu = qre.gate_up(t(x.view(np.int16)).view(torch.bfloat16), t(sorted_slot), to_gpu_experts(Wo, bits), 1, ws)
+    h_gpu = qre.gate_up(t(x.view(np.int16)).view(torch.bfloat16), t(sorted_slot), t(offsets),
+                        to_gpu_experts(Wo, bits), 1)
     assert_parity(bf16_np(h_gpu), bf16_to_f64(h_ref), what="h")
+
+
+@pytest.mark.parametrize("act_int8", [False, True])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gate_up_silu_overflow(bits, act_int8):
+    """Gates g <= -89: exp(-g) overflows FP32 on the GPU, so SiLU(g) * u must
+    come out as a signed zero, which is also what the oracle's double SiLU
+    rounds to in BF16 (|h| < 2^-133).  Tokens alternate between x0 = +1016 and
+    -1016 (exactly 127 * 8, so the INT8 activation scale is exactly 8); the
+    gate code qmax at input 0 gives g = +-1016 qmax / 64 (+-111.125 INT4,
+    +-2016.125 INT8), up codes c in -3..3 give u = 15.875 c, and every product
+    is exact in FP32, so all of h is compared bit for bit (as values)."""
+    T, H, I, E, K = 16, 256, 128, 1, 1
+    qmax = 7 if bits == 4 else 127
+    rng = np.random.default_rng(90 + bits + act_int8)
+    x = np.zeros((T, H), np.float32)
+    x[:, 0] = np.where(np.arange(T) % 2 == 0, 1016.0, -1016.0)
+    x[:, 128] = 1016.0 * (np.arange(T) % 3 == 0)
+    xb = f32_to_bf16_bits(x)
+    gate = np.zeros((I, H), np.float32)
+    gate[:, 0] = qmax * 2.0 ** -6
+    gate[:, 128] = qmax * 2.0 ** -6 * (np.arange(I) % 2)        # second group: +-0 or g += 111/2016
+    up = np.zeros((I, H), np.float32)
+    up[:, 0] = rng.integers(-3, 4, size=I) * 2.0 ** -6
+    up[:, 1] = qmax * 2.0 ** -6                                  # sets the scale; x[:, 1] = 0
+    up[:, 129] = qmax * 2.0 ** -6
+    down = np.zeros((H, I), np.float32)
+    down[:, 0] = qmax * 2.0 ** -6
+    qs = [oracle.quantize_weights(m, bits) for m in (gate, up, down)]
+    Wo = oracle.QWeights(*(a[None] for a in (qs[0][0], qs[0][1], qs[1][0], qs[1][1], qs[2][0], qs[2][1])))
+    ids = np.zeros((T, K), np.int32)
+    counts, offsets, sorted_slot, slot_row, _ = oracle.route(ids, E)
+    shp = dict(T=T, H=H, I=I, E=E, K=K, bits=bits)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    Wg = to_gpu_experts(Wo, bits)
+    if act_int8:
+        xq, xs = oracle.quantize_act(xb)
+        assert np.all(xs[:, 0] == 8.0)
+        h_ref = oracle.gate_up(None, sorted_slot, offsets, Wo, act_int8=True, xq=xq, xs=xs, **shp)
+        h_gpu = qre.gate_up(None, t(sorted_slot), t(offsets), Wg, K, act_int8=True, xq=t(xq), xs=t(xs))
+    else:
+        h_ref = oracle.gate_up(xb, sorted_slot, offsets, Wo, **shp)
+        h_gpu = qre.gate_up(t(xb.view(np.int16)).view(torch.bfloat16), t(sorted_slot), t(offsets), Wg, K)
+    g = bf16_to_f64(bf16_np(h_gpu))
+    r = bf16_to_f64(h_ref)
+    neg = np.arange(T) % 2 == 1
+    assert np.all(r[neg] == 0) and np.count_nonzero(r[~neg]) > I
+    np.testing.assert_array_equal(g, r)

@@ -13,7 +13,8 @@ import numpy as np
 import pytest
 
 import oracle
-from quantized_routed_expert_top_amd.inputs import f32_to_bf16_bits, bf16_bits_to_f32
+from harness.inputs import f32_to_bf16_bits, bf16_bits_to_f32
+from np_ref import np_quantize_act
 
 
 def _scale_values(s_bits):
@@ -118,3 +119,32 @@ def test_act_quantizer_ties_scaling_and_sign():
     np.testing.assert_array_equal(s2, s1 * 2)
     np.testing.assert_array_equal(q3, -q1)
     np.testing.assert_array_equal(s3, s1)
+
+
+
+def test_act_quantizer_bit_exact_vs_numpy():
+    """Bit-exact against the numpy statement above on scales that are not
+    powers of two (the quotient v / s is then rounded to FP32 before rint, so a
+    reciprocal-multiply or a double-precision quotient would differ), with
+    outlier groups, zero groups, and tiny and huge magnitudes (ties at exact
+    power-of-two scales are pinned above)."""
+    rng = np.random.default_rng(15)
+    v = rng.standard_normal((64, 1024)).astype(np.float32)
+    v[:, rng.choice(1024, 10, replace=False)] *= 20.0
+    v[7, 256:384] = 0.0
+    v[9, :128] *= 1e-30
+    v[11, 128:256] *= 1e30
+    vb = f32_to_bf16_bits(v)
+    q, s = oracle.quantize_act(vb)
+    nq, ns = np_quantize_act(vb)
+    np.testing.assert_array_equal(s.view(np.uint32), ns.view(np.uint32))
+    np.testing.assert_array_equal(q, nq)
+    m64 = np.abs(bf16_bits_to_f32(vb)).reshape(64, 8, 128).max(axis=2).astype(np.float64)
+    assert np.mean(ns.astype(np.float64) * 127 != m64) > 0.5          # most scales are inexact quotients
+    # a reciprocal multiply is a plausible mistake this pin must see: on these
+    # inputs it gives different codes somewhere
+    vf = bf16_bits_to_f32(vb).reshape(64, 8, 128)
+    recip = (np.float32(1.0) / np.where(ns == 0, np.float32(1), ns)).astype(np.float32)
+    alt = np.clip(np.rint((vf * recip[..., None]).astype(np.float32)), -127, 127).reshape(64, 1024)
+    alt[np.repeat(ns == 0, 128, axis=1)] = 0
+    assert np.any(alt.astype(np.int8) != nq)

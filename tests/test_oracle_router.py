@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from quantized_routed_expert_top_amd.inputs import topk_softmax as np_topk_softmax
+from harness.inputs import topk_softmax as np_topk_softmax
 
 U = 2.0 ** -24   # FP32 unit roundoff
 
