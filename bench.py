@@ -9,10 +9,18 @@ batch already resident in HBM.  Steps are replayed from HIP graphs (one per
 weight copy) and rotate over enough copies of the packed weights that the
 256 MB last-level cache cannot serve them.  Prints one JSON line.
 
+The headline is the 32-token W4A16 block (decode_w4a16): `value` is its
+tokens/s over exactly K timed steps.  By default the same process then times
+the 8192-token W8A8 prefill (`prefill` object: its own timed steps, the
+gate/up MFMA fraction and the whole step's INT8 MFMA fraction) and a plain
+streaming read of device memory (`hbm_read_probe`: the measured read ceiling
+next to the published 8 TB/s).
+
 The roofline object is for the dominant kernel (the fused gate/up GEMM): its
 algorithmic bytes per launch (packed weights + scales of the touched experts)
-over its average duration, measured here with HIP events recorded on the
-kernel's stream around each launch.
+over its average duration, measured here with HIP events recorded by the
+library on the kernel's stream around each launch, less the duration of an
+empty event pair measured the same way.
 """
 import argparse
 import hashlib
@@ -31,17 +39,21 @@ I8_PEAK_TOPS = 5000.0
 METRIC = "routed-expert FFN tokens/s; % HBM peak (32-tok block) & % MFMA peak (prefill)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_{}.txt")
 CSRC = os.path.join(ROOT, "quantized_routed_expert_top_amd", "csrc")
+STAGES = ("route_and_quantize_x", "gate_up", "quantize_h", "down", "combine")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def is_big(wl) -> bool:
+    return wl.T * wl.K >= 64 * wl.E
+
+
 def gemm_sources(wl) -> list:
-    """Source files of the gate/up kernel a workload runs: the 128-row tile
+    """Source files of the dominant kernel a workload runs: the 128-row tile
     kernels at 64 or more slots per expert, else the per-expert kernels."""
-    big = wl.T * wl.K >= 64 * wl.E
-    return [os.path.join(CSRC, f) for f in (("gemm_big.hip" if big else "gemm.hip"), "gemm_common.h")]
+    return [os.path.join(CSRC, f) for f in (("gemm_big.hip" if is_big(wl) else "gemm.hip"), "gemm_common.h")]
 
 
 def source_digest(wl) -> str:
@@ -55,8 +67,7 @@ def source_digest(wl) -> str:
 def read_traffic(wl):
     """HBM bytes per gate/up launch from the committed rocprofv3 counter
     summary, or None if absent or taken on a different kernel source."""
-    workload = wl.name
-    path = TRAFFIC_FILE.format(workload)
+    path = TRAFFIC_FILE.format(wl.name)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -81,6 +92,7 @@ class HipEvents:
         self.C = C
         self.lib = C.CDLL("libamdhip64.so")
         self.lib.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
         self.lib.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
         self.lib.hipEventDestroy.argtypes = [C.c_void_p]
         self.events = []
@@ -91,6 +103,10 @@ class HipEvents:
             raise RuntimeError("hipEventCreate failed")
         self.events.append(h.value)
         return h.value
+
+    def record(self, ev, stream_handle):
+        if self.lib.hipEventRecord(ev, stream_handle) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, a, b):
         ms = self.C.c_float()
@@ -104,9 +120,21 @@ class HipEvents:
         self.events = []
 
 
-def cpu_baseline(wl, x_bits, ids, w, budget_s=12.0):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, x_bits, ids, w, budget_s=8.0, budget_1t_s=5.0):
     """The oracle as it stands, on this host's cores, over whole blocks of the
-    same workload (repeated until ~budget_s of CPU time, at least once)."""
+    same workload (repeated until ~budget_s of wall time, at least once),
+    with all the threads OpenMP gives it and again with one thread."""
     import numpy as np
     import oracle
     from harness.synthetic import touched_experts
@@ -118,16 +146,197 @@ def cpu_baseline(wl, x_bits, ids, w, budget_s=12.0):
         sample = f"whole {wl.T}-token batch"
     tok = np.arange(wl.T) if tokens is None else tokens
     Wo = oracle.workload_experts(wl, touched_experts(ids[tok], wl.E))
-    runs, t_total = 0, 0.0
-    while runs == 0 or t_total < budget_s:
+
+    def timed(budget):
+        runs, t_total = 0, 0.0
+        while runs == 0 or t_total < budget:
+            t0 = time.perf_counter()
+            oracle.moe_forward(x_bits, ids, w, Wo, E=wl.E, bits=wl.weight_bits, act_int8=wl.act_int8, tokens=tokens)
+            t_total += time.perf_counter() - t0
+            runs += 1
+        return runs, t_total
+
+    threads = oracle.num_threads()
+    runs, t_total = timed(budget_s)
+    oracle.set_num_threads(1)
+    runs1, t1 = timed(budget_1t_s)
+    oracle.set_num_threads(threads)
+    return {"value": round(runs * len(tok) / t_total, 2), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "sample": f"{sample}, {runs} run(s), {t_total:.1f} s",
+            "one_thread": {"value": round(runs1 * len(tok) / t1, 2), "unit": "tokens/s", "cores": 1,
+                           "sample": f"{sample}, {runs1} run(s), {t1:.1f} s"},
+            "cpu_model": cpu_model(), "build": "gcc -O2 -ffp-contract=off -fopenmp, no intrinsics, no BLAS"}
+
+
+def empty_pair_us(hip, stream_handle, n=50):
+    """Mean duration of two events recorded back to back (the cost an event
+    pair adds to a kernel's measured duration)."""
+    import numpy as np
+    pairs = [(hip.create(), hip.create()) for _ in range(n)]
+    for a, b in pairs:
+        hip.record(a, stream_handle)
+        hip.record(b, stream_handle)
+    import torch
+    torch.cuda.synchronize()
+    return float(np.mean([hip.elapsed_ms(a, b) for a, b in pairs[5:]])) * 1e3
+
+
+def time_workload(wl, steps, warmup, eager, copies_arg, dev, hip):
+    """Problem setup, K timed steps (graph replay), a median of 5 further
+    loops, and per-kernel durations from the library's events.  Returns a
+    dict of measurements plus the problem (for the CPU baseline)."""
+    import numpy as np
+    import torch
+    import quantized_routed_expert_top_amd as qre
+    from harness.synthetic import algorithmic_bytes, gpu_problem
+
+    log(f"[bench] workload {wl.name}: generating and quantizing weights on the GPU")
+    t0 = time.perf_counter()
+    P = gpu_problem(wl, dev)
+    log(f"[bench] problem ready in {time.perf_counter() - t0:.1f} s")
+    alg = algorithmic_bytes(wl, P["ids"])
+    W0 = P["W"]
+    R = copies_arg or max(1, math.ceil((1 << 30) / max(alg["gate_up_weights"] + alg["down_weights"], 1)))
+    copies = [W0] + [W0.clone() for _ in range(R - 1)]
+    x, ids_t, w_t = P["x"], P["topk_ids"], P["topk_w"]
+    ws = torch.empty(qre.workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.K, wl.weight_bits, wl.act_int8),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        qre.moe_forward(x, ids_t, w_t, copies[i % R], act_int8=wl.act_int8, out=out, workspace=ws)
+
+    stream = torch.cuda.Stream()
+    graphs = []
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        eager_out = out.clone()
+        if not eager:
+            for r in range(R):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    step(r)
+                graphs.append(g)
+            for i in range(max(2 * R, min(warmup, 4 * R))):
+                graphs[i % R].replay()
+            torch.cuda.synchronize()
+            if not torch.equal(out, eager_out):
+                raise RuntimeError("graph replay differs from eager output")
+
+        def run(i):
+            if eager:
+                step(i)
+            else:
+                graphs[i % R].replay()
+
+        # ---- timed region: K whole steps ----
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
-        oracle.moe_forward(x_bits, ids, w, Wo, E=wl.E, bits=wl.weight_bits, act_int8=wl.act_int8, tokens=tokens)
-        t_total += time.perf_counter() - t0
-        runs += 1
-        if t_total > 3 * budget_s:
-            break
-    return {"value": runs * len(tok) / t_total, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "sample": f"{sample}, {runs} run(s), {t_total:.1f} s"}
+        ev0.record(stream)
+        for i in range(steps):
+            run(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu_ms = ev0.elapsed_time(ev1)
+        if not torch.equal(out, eager_out):
+            raise RuntimeError("timed steps changed the output")
+
+        # ---- five further event-timed loops (median) ----
+        nl = max(10, min(steps, 200))
+        loop_ms = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(nl):
+                run(i)
+            b.record(stream)
+            torch.cuda.synchronize()
+            loop_ms.append(a.elapsed_time(b) / nl)
+
+        # ---- per-kernel durations: the same kernels, with HIP events between steps ----
+        sh = stream.cuda_stream
+        pair_us = empty_pair_us(hip, sh)
+        nk = max(20, min(steps, 200))
+        evs = [[hip.create() for _ in range(6)] for _ in range(nk)]
+        for i in range(nk):
+            qre.moe_forward_timed(x, ids_t, w_t, copies[i % R], evs[i], act_int8=wl.act_int8, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        if not torch.equal(out, eager_out):
+            raise RuntimeError("timed forward differs from qre_moe_forward")
+    dur = np.array([[hip.elapsed_ms(e[j], e[j + 1]) for j in range(5)] for e in evs[2:]]).mean(axis=0) * 1e3
+    dur = np.maximum(dur - pair_us, 0.0)
+    plan = qre.forward_plan(wl.T, wl.H, wl.I, wl.E, wl.K, wl.weight_bits, wl.act_int8)
+    return {
+        "wl": wl, "P": P, "alg": alg, "R": R, "steps": steps, "wall": wall, "gpu_ms": gpu_ms, "plan": plan,
+        "median_loop_ms": float(np.median(loop_ms)), "loops_ms": [round(v, 5) for v in loop_ms],
+        "kernels_us": {k: round(float(v), 2) for k, v in zip(STAGES, dur)}, "event_pair_us": round(pair_us, 2),
+    }
+
+
+def hbm_probe(dev, hip, nbytes=2 << 30, reps=10):
+    """Plain streaming read of `nbytes` of device memory (8x the last-level
+    cache), event-timed; returns GB/s."""
+    import numpy as np
+    import torch
+    import quantized_routed_expert_top_amd as qre
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(4096, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            qre.hbm_read_probe(buf, sink)
+        sh = stream.cuda_stream
+        evs = [(hip.create(), hip.create()) for _ in range(reps)]
+        for a, b in evs:
+            hip.record(a, sh)
+            qre.hbm_read_probe(buf, sink)
+            hip.record(b, sh)
+        torch.cuda.synchronize()
+    us = float(np.mean([hip.elapsed_ms(a, b) for a, b in evs])) * 1e3
+    del buf
+    return {"bytes": nbytes, "avg_us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def roofline(res, probe_gbs=None):
+    wl, alg = res["wl"], res["alg"]
+    gu_us = res["kernels_us"]["gate_up"]
+    if is_big(wl):
+        # prefill-sized: 64+ rows per expert on average (the 128-row MFMA
+        # tiles); the gate/up GEMM is a dense contraction for the matrix cores
+        S = wl.T * wl.K
+        gu_flops = 2.0 * S * wl.H * 2 * wl.I
+        peak = I8_PEAK_TOPS if wl.act_int8 else BF16_PEAK_TFLOPS
+        achieved = gu_flops / (gu_us * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": read_traffic(wl),
+                "kernel": "fused gate/up + SiLU*mul GEMM", "avg_us": gu_us, "alg_flops_per_launch": gu_flops,
+                "timing": "HIP events around each launch, less an empty event pair"}
+    gu_bytes = alg["gate_up_weights"]
+    kernel = ("fused permutation + gate/up + SiLU*mul GEMM" if res["plan"] & 1 else "fused gate/up + SiLU*mul GEMM")
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(wl),
+         "kernel": kernel, "avg_us": gu_us, "alg_bytes_per_launch": int(gu_bytes),
+         "timing": "HIP events around each launch, less an empty event pair"}
+    if probe_gbs:
+        r["frac_of_measured_read"] = round(achieved / probe_gbs, 4)
+    return r
+
+
+def step_summary(res):
+    wl, alg = res["wl"], res["alg"]
+    s = res["wall"] / res["steps"]
+    peak = I8_PEAK_TOPS if wl.act_int8 else BF16_PEAK_TFLOPS
+    return {"gpu_ms_per_step": round(res["gpu_ms"] / res["steps"], 5),
+            "median_of_5_loops_ms": round(res["median_loop_ms"], 5),
+            "alg_bytes": int(alg["total"]),
+            "hbm_frac_whole_step": round(alg["total"] / s / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac_whole_step": round(alg["flops"] / s / 1e12 / peak, 5)}
 
 
 def router_bench(args, wl):
@@ -211,6 +420,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough for >= 1 GiB)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill_w8a8 object of the default run")
+    ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read probe")
     ap.add_argument("--stage", choices=["ffn", "router"], default="ffn",
                     help="ffn: the whole feed-forward (default); router: the top-K + softmax router alone")
     ap.add_argument("--copy-probe", action="store_true",
@@ -222,107 +433,28 @@ def main():
               f"multi-GPU path; the per-GPU kernel is what it measures.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
-    import quantized_routed_expert_top_amd as qre
     from harness.inputs import WORKLOADS
-    from harness.synthetic import algorithmic_bytes, gpu_problem
 
     wl = WORKLOADS[args.workload]
     if args.stage == "router":
         return router_bench(args, wl)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    log(f"[bench] workload {wl.name}: generating and quantizing weights on the GPU")
-    t0 = time.perf_counter()
-    P = gpu_problem(wl, dev)
-    log(f"[bench] problem ready in {time.perf_counter() - t0:.1f} s")
-    alg = algorithmic_bytes(wl, P["ids"])
-    W0 = P["W"]
-    R = args.copies or max(1, math.ceil((1 << 30) / max(alg["gate_up_weights"] + alg["down_weights"], 1)))
-    copies = [W0] + [W0.clone() for _ in range(R - 1)]
-    x, ids_t, w_t = P["x"], P["topk_ids"], P["topk_w"]
-    ws = torch.empty(qre.workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.K, wl.weight_bits, wl.act_int8),
-                     dtype=torch.uint8, device=dev)
-    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+    hip = HipEvents()
 
-    def step(i):
-        qre.moe_forward(x, ids_t, w_t, copies[i % R], act_int8=wl.act_int8, out=out, workspace=ws)
-
-    stream = torch.cuda.Stream()
-    graphs = []
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            step(i)
-        torch.cuda.synchronize()
-        eager_out = out.clone()
-        if not args.eager:
-            for r in range(R):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=stream):
-                    step(r)
-                graphs.append(g)
-            for i in range(min(args.warmup, 2 * R)):
-                graphs[i % R].replay()
-            torch.cuda.synchronize()
-            if not torch.equal(out, eager_out):
-                raise RuntimeError("graph replay differs from eager output")
-
-        # ---- timed region: K whole steps ----
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        ev0.record(stream)
-        for i in range(args.steps):
-            if args.eager:
-                step(i)
-            else:
-                graphs[i % R].replay()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        gpu_ms = ev0.elapsed_time(ev1)
-        if not torch.equal(out, eager_out):
-            raise RuntimeError("timed steps changed the output")
-
-        # ---- per-kernel durations: the same kernels, with HIP events between steps ----
-        hip = HipEvents()
-        nk = max(20, min(args.steps, 200))
-        evs = [[hip.create() for _ in range(6)] for _ in range(nk)]
-        for i in range(nk):
-            qre.moe_forward_timed(x, ids_t, w_t, copies[i % R], evs[i], act_int8=wl.act_int8, out=out,
-                                  workspace=ws)
-        torch.cuda.synchronize()
-        if not torch.equal(out, eager_out):
-            raise RuntimeError("timed forward differs from qre_moe_forward")
-    dur = np.array([[hip.elapsed_ms(e[j], e[j + 1]) for j in range(5)] for e in evs[2:]]).mean(axis=0) * 1e3  # us
+    probe = None if args.no_probe else hbm_probe(dev, hip)
+    res = time_workload(wl, args.steps, args.warmup, args.eager, args.copies, dev, hip)
+    pre = None
+    if not args.no_prefill and wl.name != "prefill_w8a8":
+        pw = WORKLOADS["prefill_w8a8"]
+        pre = time_workload(pw, min(args.steps, 100), min(args.warmup, 10), args.eager, 0, dev, hip)
     hip.destroy_all()
 
-    ms_per_step = wall * 1e3 / args.steps
-    tokens_per_s = wl.T * args.steps / wall
-    gu_us, dn_us = float(dur[1]), float(dur[3])
-    gu_bytes = alg["gate_up_weights"]
-    S = wl.T * wl.K
-    if S >= 64 * wl.E:
-        # prefill-sized: 64+ rows per expert on average (the 128-row MFMA
-        # tiles); the gate/up GEMM is a dense contraction for the matrix cores
-        gu_flops = 2.0 * S * wl.H * 2 * wl.I
-        peak = I8_PEAK_TOPS if wl.act_int8 else BF16_PEAK_TFLOPS
-        achieved = gu_flops / (gu_us * 1e-6) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(achieved / peak, 4), "traffic": read_traffic(wl),
-                    "kernel": "fused gate/up + SiLU*mul GEMM", "avg_us": round(gu_us, 2),
-                    "alg_flops_per_launch": gu_flops}
-    else:
-        achieved = gu_bytes / (gu_us * 1e-6) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(wl),
-                    "kernel": "fused gate/up + SiLU*mul GEMM", "avg_us": round(gu_us, 2),
-                    "alg_bytes_per_launch": int(gu_bytes)}
-    step_bytes = alg["total"]
+    ms_per_step = res["wall"] * 1e3 / args.steps
     result = {
         "metric": METRIC,
-        "value": round(tokens_per_s, 1),
+        "value": round(wl.T * args.steps / res["wall"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -334,18 +466,31 @@ def main():
         "dtype": "i8" if wl.act_int8 else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "K": wl.K,
-                   "weight_bits": wl.weight_bits, "act_int8": wl.act_int8, "weight_copies": R,
-                   "launch": "eager" if args.eager else "hipGraph replay", "touched_experts": alg["touched"]},
-        "roofline": roofline,
-        "step": {"gpu_ms_per_step": round(gpu_ms / args.steps, 5),
-                 "alg_bytes": int(step_bytes),
-                 "hbm_frac_whole_step": round(step_bytes / (wall / args.steps) / 1e9 / HBM_PEAK_GBS, 4),
-                 "mfma_frac_whole_step": round(alg["flops"] / (wall / args.steps) / 1e12 /
-                                               (I8_PEAK_TOPS if wl.act_int8 else BF16_PEAK_TFLOPS), 5)},
-        "kernels_us": {"route_and_quantize_x": round(float(dur[0]), 2), "gate_up": round(gu_us, 2),
-                       "quantize_h": round(float(dur[2]), 2), "down": round(dn_us, 2),
-                       "combine": round(float(dur[4]), 2)},
+                   "weight_bits": wl.weight_bits, "act_int8": wl.act_int8, "weight_copies": res["R"],
+                   "launch": "eager" if args.eager else "hipGraph replay", "touched_experts": res["alg"]["touched"]},
+        "roofline": roofline(res, probe["gbs"] if probe else None),
+        "step": step_summary(res),
+        "kernels_us": res["kernels_us"],
+        "event_pair_us": res["event_pair_us"],
+        "plan": {"route_in_gate_up": bool(res["plan"] & 1), "combine_in_down": bool(res["plan"] & 2)},
     }
+    if probe:
+        result["hbm_read_probe"] = probe
+        result["step"]["frac_of_measured_read_whole_step"] = round(
+            res["alg"]["total"] / (res["wall"] / args.steps) / 1e9 / probe["gbs"], 4)
+    if pre is not None:
+        pw = pre["wl"]
+        pr = roofline(pre)
+        ps = step_summary(pre)
+        result["prefill"] = {
+            "workload": pw.name, "T": pw.T, "H": pw.H, "I": pw.I, "E": pw.E, "K": pw.K,
+            "weight_bits": pw.weight_bits, "act_int8": pw.act_int8, "dtype": "i8", "weight_copies": pre["R"],
+            "steps": pre["steps"], "ms_per_step": round(pre["wall"] * 1e3 / pre["steps"], 5),
+            "tokens_per_s": round(pw.T * pre["steps"] / pre["wall"], 1),
+            "gate_up_us": pr["avg_us"], "gate_up_mfma_frac": pr["frac"], "gate_up_tops": pr["achieved"],
+            "step_i8_mfma_frac": ps["mfma_frac_whole_step"], "step": ps, "kernels_us": pre["kernels_us"],
+            "gate_up_traffic": pr["traffic"],
+        }
     if args.copy_probe:
         n = 256 << 20
         a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -356,6 +501,7 @@ def main():
         result["copy_probe_bytes"] = n
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
+        P = res["P"]
         result["cpu_baseline"] = cpu_baseline(wl, P["x_bits"], P["ids"], P["w"])
     print(json.dumps(result), flush=True)
 

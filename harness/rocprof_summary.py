@@ -1,7 +1,7 @@
 """Text summaries of rocprofv3 output (the SQLite database it writes).
 
-    python -m quantized_routed_expert_top_amd.rocprof_summary kernels DIR [--top N]
-    python -m quantized_routed_expert_top_amd.rocprof_summary counters DIR [--kernel SUBSTR]
+    python -m harness.rocprof_summary kernels DIR [--top N]
+    python -m harness.rocprof_summary counters DIR [--kernel SUBSTR]
 
 `kernels` prints, per kernel name, the number of dispatches and the average,
 minimum, maximum and total duration (from a --kernel-trace run); `counters`

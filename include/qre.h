@@ -239,6 +239,22 @@ int qre_topk_softmax(const float* logits, int32_t T, int32_t E, int32_t K, int32
 int qre_quantize_weights(const float* w, int64_t rows, int64_t cols, int32_t bits, void* q,
                          void* s, qre_stream_t stream);
 
+/* Measurement aid: what qre_moe_forward launches for `desc` (host out, a bit
+ * mask).  QRE_PLAN_ROUTE_IN_GATE_UP: the permutation is computed inside the
+ * gate/up kernel (no routing launch).  QRE_PLAN_COMBINE_IN_DOWN: the combine
+ * runs inside the down kernel (no combine launch).  QRE_PLAN_BIG_TILES:
+ * 128-row MFMA tiles (64 or more slots per expert). */
+#define QRE_PLAN_ROUTE_IN_GATE_UP 1
+#define QRE_PLAN_COMBINE_IN_DOWN 2
+#define QRE_PLAN_BIG_TILES 4
+int qre_forward_plan(const qre_desc* desc, int32_t* plan);
+
+/* Measurement aid: a streaming read of `bytes` (a nonzero multiple of 16) of
+ * device memory `buf`, folded into words stored to `sink` (device, at least
+ * 4096 bytes).  Its duration gives the HBM read bandwidth the memory-bound
+ * kernels are compared with, next to the published peak. */
+int qre_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, qre_stream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char* qre_status_string(int status);
 

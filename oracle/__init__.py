@@ -70,6 +70,7 @@ def lib():
         L.orc_moe_forward.restype = C.c_int
         L.orc_moe_forward.argtypes = [P, P, P, P, P, P, i64, P, P, P]
         L.orc_num_threads.restype = C.c_int
+        L.orc_set_num_threads.argtypes = [C.c_int]
         _lib = L
     return _lib
 
@@ -94,6 +95,11 @@ def _c(a, dtype):
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from now on."""
+    lib().orc_set_num_threads(int(n))
 
 
 # ---- number formats --------------------------------------------------------

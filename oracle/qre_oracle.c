@@ -598,3 +598,13 @@ int orc_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads the expert loops use from now on (benchmark baselines). */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

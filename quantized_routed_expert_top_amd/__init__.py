@@ -71,6 +71,8 @@ def _lib():
         L.qre_combine.argtypes = [P, P, P, i32, i32, i32, P, P]
         L.qre_topk_softmax.argtypes = [P, i32, i32, i32, P, P, P]
         L.qre_quantize_weights.argtypes = [P, i64, i64, i32, P, P, P]
+        L.qre_hbm_read_probe.argtypes = [P, sz, P, P]
+        L.qre_forward_plan.argtypes = [P, P]
         _L = L
     return _L
 
@@ -405,3 +407,26 @@ def combine(y, slot_row, topk_w, out=None):
     _need(out, "out", torch.bfloat16, (T, H))
     _check("qre_combine", _lib().qre_combine(_ptr(y), _ptr(slot_row), _ptr(topk_w), T, K, H, _ptr(out), _stream()))
     return out
+
+
+def hbm_read_probe(buf, sink):
+    """Measurement aid: stream-read the bytes of `buf` (any contiguous GPU
+    tensor, a multiple of 16 bytes) into `sink` (uint8, >= 4096 bytes)."""
+    if not (buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf must be a contiguous GPU tensor")
+    _need(sink, "sink", torch.uint8)
+    if sink.numel() < 4096:
+        raise ValueError("sink must hold 4096 bytes")
+    _check("qre_hbm_read_probe", _lib().qre_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                                           _stream()))
+
+
+PLAN_ROUTE_IN_GATE_UP, PLAN_COMBINE_IN_DOWN, PLAN_BIG_TILES = 1, 2, 4
+
+
+def forward_plan(T, H, I, E, K, bits, act_int8=False) -> int:
+    """Bit mask of what moe_forward launches for this problem (PLAN_*)."""
+    n = C.c_int32(0)
+    _check("qre_forward_plan", _lib().qre_forward_plan(C.byref(_desc(T, H, I, E, K, bits, act_int8)), C.byref(n)))
+    return n.value
+

@@ -311,14 +311,20 @@ struct Dec16 {
   __device__ static uint32_t lds_chunk(int row, int chunk) { return (uint32_t)(row * ROWB + ((chunk ^ swz(row)) << 4)); }
 
   // Tile: rows [row0, row0 + nrows) (sorted order) of expert e; src(r) gives
-  // the A-source row of local row r (a token for gate/up, a sorted row for down).
-  template <class RowSrc>
-  __device__ static void run(const GemmProblem& p, int e, int row0, int nrows, RowSrc src_row, uint8_t* lds) {
+  // the A-source row of local row r (a token for gate/up, a sorted row for
+  // down); store(m, col, v) receives the FP32 result of local row m < nrows
+  // (SiLU(gate) * up for the fused projection) before any rounding.
+  // Column block cb: the workgroup's waves take columns (4 cb + wave) 16 FN.
+  // With stage = false the rows staged by an earlier call (same tile) are
+  // reused: no staging, no barrier.
+  template <class RowSrc, class Store>
+  __device__ static void run(const GemmProblem& p, int e, int row0, int nrows, RowSrc src_row, Store store,
+                             uint8_t* lds, int cb, bool stage = true) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, kb = lane >> 4;
     // 1. per-wave descriptors, weight offsets, all scales of its columns and
     //    the first DEPTH groups of weights: issued before the activation rows
     //    are staged, so the weight stream starts at once
-    const int col0 = min((blockIdx.x * 4 + wave) * 16 * FN, p.n - 16 * FN);   // a surplus wave re-reads the last tile and stores nothing
+    const int col0 = min((cb * 4 + wave) * 16 * FN, p.n - 16 * FN);   // a surplus wave re-reads the last tile and stores nothing
     const int64_t mat_bytes = (int64_t)p.n * NG * W_GROUP_BYTES;
     const int64_t smat_bytes = (int64_t)p.n * NG * 2;
     rsrc_t rw[NM], rs[NM];
@@ -405,6 +411,7 @@ struct Dec16 {
     // 2. stage the tile's activation rows (and INT8 scales) into LDS
     const uint8_t* a = static_cast<const uint8_t*>(p.a);
     float* xs_lds = reinterpret_cast<float*>(lds + (size_t)BMR * ROWB);   // [NG][16]
+    if (stage) {
     for (int idx = tid; idx < nrows * CPR; idx += blockDim.x) {
       const int r = idx / CPR, c = idx % CPR;
       const int64_t src = src_row(r);
@@ -431,7 +438,8 @@ struct Dec16 {
       }
     }
     __syncthreads();
-    if ((blockIdx.x * 4 + wave) * 16 * FN >= p.n) return;   // wave-uniform, after the barrier
+    }
+    if ((cb * 4 + wave) * 16 * FN >= p.n) return;   // wave-uniform, after the barrier
 
     // 3. the weight stream
 
@@ -528,10 +536,9 @@ struct Dec16 {
         }
     }
     // 5. epilogue: lane holds rows 4kb+r of column li of each fragment
-    uint16_t* out = static_cast<uint16_t*>(p.out);
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
-      const int64_t col = col0 + f * 16 + li;
+      const int col = col0 + f * 16 + li;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 4 * kb + r;
@@ -539,10 +546,20 @@ struct Dec16 {
           float o;
           if constexpr (DUAL) o = silu(acc[f][0][r]) * acc[f][1][r];
           else o = acc[f][0][r];
-          out[(int64_t)(row0 + m) * p.n + col] = (uint16_t)f32_to_bf16_bits(o);
+          store(m, col, o);
         }
       }
     }
+  }
+};
+
+// Store functor of the row-tile kernels: BF16 rows of p.out from row0.
+struct GlobalRowStore {
+  uint16_t* out;
+  int64_t row0;
+  int n;
+  __device__ void operator()(int m, int col, float v) const {
+    out[(row0 + m) * n + col] = (uint16_t)f32_to_bf16_bits(v);
   }
 };
 
@@ -553,10 +570,12 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmProblem p) {
   if ((int)blockIdx.y >= *p.ntiles) return;
   const Tile td = p.tiles[blockIdx.y];
   const int row0 = td.row0;
+  const GlobalRowStore st{static_cast<uint16_t*>(p.out), row0, p.n};
   if (p.gather_k) {
-    K::run(p, td.e, row0, td.nrows, [&](int r) { return (int64_t)(p.sorted_slot[row0 + r] / p.gather_k); }, dec_lds);
+    K::run(p, td.e, row0, td.nrows, [&](int r) { return (int64_t)(p.sorted_slot[row0 + r] / p.gather_k); }, st,
+           dec_lds, blockIdx.x);
   } else {
-    K::run(p, td.e, row0, td.nrows, [&](int r) { return (int64_t)(row0 + r); }, dec_lds);
+    K::run(p, td.e, row0, td.nrows, [&](int r) { return (int64_t)(row0 + r); }, st, dec_lds, blockIdx.x);
   }
 }
 
@@ -584,7 +603,7 @@ __global__ __launch_bounds__(256) void k_gate_up_routed(GemmProblem p, RouteOut 
     int ev = e;
     asm volatile("" : "+s"(ev));
     K::run(p, ev, off + t0, min(BMR, count - t0), [&](int r) { return (int64_t)(rows[t0 + r] / p.gather_k); },
-           dec_lds);
+           GlobalRowStore{static_cast<uint16_t*>(p.out), off + t0, p.n}, dec_lds, blockIdx.x);
     __syncthreads();                                        // the LDS tile is reused by the next row tile
   }
 }
@@ -599,7 +618,8 @@ __global__ __launch_bounds__(256) void k_down_routed(GemmProblem p, const int32_
     const int row0 = off + t0;
     int ev = e;                                             // opaque: no hoisting of weight loads
     asm volatile("" : "+s"(ev));
-    K::run(p, ev, row0, min(BMR, count - t0), [&](int r) { return (int64_t)(row0 + r); }, dec_lds);
+    K::run(p, ev, row0, min(BMR, count - t0), [&](int r) { return (int64_t)(row0 + r); },
+           GlobalRowStore{static_cast<uint16_t*>(p.out), row0, p.n}, dec_lds, blockIdx.x);
     __syncthreads();
   }
 }

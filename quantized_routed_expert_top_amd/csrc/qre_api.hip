@@ -14,6 +14,7 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
+
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -454,6 +455,26 @@ int qre_topk_softmax(const float* logits, int32_t T, int32_t E, int32_t K, int32
   if (!logits || !topk_ids || !topk_w) return QRE_ERR_NULL;
   if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w)) return QRE_ERR_ALIGN;
   return hip_status(launch_topk_softmax(logits, T, E, K, topk_ids, topk_w, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qre_forward_plan(const qre_desc* desc, int32_t* plan) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!plan) return QRE_ERR_NULL;
+  const qre_desc& d = *desc;
+  const int64_t S = (int64_t)d.T * d.K;
+  int32_t f = 0;
+  if (routed_applicable(S, d.E, d.H, d.I, d.act_int8)) f |= QRE_PLAN_ROUTE_IN_GATE_UP;
+  if (big_applicable(S, d.E)) f |= QRE_PLAN_BIG_TILES;
+  *plan = f;
+  return QRE_OK;
+}
+
+int qre_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, qre_stream_t stream) {
+  if (!buf || !sink) return QRE_ERR_NULL;
+  if (!aligned16(buf) || !aligned16(sink)) return QRE_ERR_ALIGN;
+  if (bytes == 0 || bytes % 16) return QRE_ERR_SHAPE;
+  return hip_status(launch_hbm_read(buf, (int64_t)bytes, sink, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

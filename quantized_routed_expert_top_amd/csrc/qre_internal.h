@@ -41,6 +41,29 @@ __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo, uint32_t
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Maximum over the 16 lanes of an aligned 16-lane segment.
+__device__ __forceinline__ float seg16_max(float m) {
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 16));
+  return m;
+}
+
+// INT8 activation code of x for the group scale sc != 0 (r = 1 / sc, rounded
+// to FP32): q = clamp(rint(x / sc), -127, 127) with x / sc rounded to FP32
+// first, as defined (model card, paragraph on --int8-expert-activations).
+// Fast form: y = x * r; both roundings keep |y - x / sc| <= 3 * 2^-24 *
+// |x / sc| <= 2.3e-5 for |x / sc| <= 127, and the FP32 quotient is as close,
+// so when y is more than 2^-14 from every half-integer rint(y) is the rint of
+// the quotient.  Otherwise (rare), and for non-finite y (a subnormal scale
+// whose reciprocal overflows), the quotient itself is taken.
+__device__ __forceinline__ float act_code(float x, float sc, float r) {
+  constexpr float kMargin = 0x1p-14f;
+  const float y = x * r;
+  float qf = rintf(y);
+  if (!(fabsf(y - qf) <= 0.5f - kMargin)) qf = rintf(x / sc);
+  return fminf(127.0f, fmaxf(-127.0f, qf));
+}
+
 // ---------------------------------------------------------------------------
 // Launchers (all enqueue on `stream` and return the launch status)
 // ---------------------------------------------------------------------------
@@ -103,9 +126,16 @@ bool routed_applicable(int64_t S, int E, int H, int I, int act_int8);
 hipError_t launch_gate_up_routed(const GemmProblem& p, const RouteOut& ro, hipStream_t stream);
 hipError_t launch_down_routed(const GemmProblem& p, const RouteOut& ro, hipStream_t stream);
 
+
+
 // Combine.
 hipError_t launch_combine(const uint16_t* y, const int32_t* slot_row, const float* topk_w, int T, int K,
                           int H, uint16_t* out, hipStream_t stream);
+
+// Streaming-read probe over `bytes` (a multiple of 16) of `buf`; sink holds
+// kProbeSinkWords words.
+constexpr int kProbeSinkWords = 1024;
+hipError_t launch_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
 
 // Router: top-K of E logits per token (one wave per token), softmax weights.
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int K, int32_t* ids, float* w,

@@ -17,106 +17,87 @@
 // lane shuffles inside the segment.  Both are HBM-streaming passes.
 #include <hip/hip_fp16.h>
 
+#include <algorithm>
+
 #include "qre_internal.h"
 
 namespace qre {
 namespace {
 
-__device__ __forceinline__ float seg16_max(float m) {
-#pragma unroll
-  for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 16));
-  return m;
-}
+// Grid-stride over (row, group) pairs, one 16-lane segment each; the grid is
+// bounded, so any size the entry point accepts launches.
+constexpr int64_t kMaxQuantBlocks = 1 << 16;
 
 __global__ __launch_bounds__(256) void k_quantize_act(const uint16_t* __restrict__ v, int64_t ngroups, int G,
                                                       int8_t* __restrict__ q, float* __restrict__ s) {
-  const int64_t gid = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;   // (row, group) index
   const int sub = threadIdx.x & 15;
-  if (gid >= ngroups) return;                                        // whole 16-lane segments leave together
-  const int64_t row = gid / G, g = gid % G;
-  const int64_t off = row * (int64_t)G * kGroup + g * kGroup + sub * 8;
-  const uint4 raw = *reinterpret_cast<const uint4*>(v + off);
-  float x[8];
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  for (int64_t gid = (int64_t)blockIdx.x * 16 + threadIdx.x / 16; gid < ngroups; gid += (int64_t)gridDim.x * 16) {
+    // whole 16-lane segments take the same trips
+    const int64_t row = gid / G, g = gid % G;
+    const int64_t off = row * (int64_t)G * kGroup + g * kGroup + sub * 8;
+    const uint4 raw = *reinterpret_cast<const uint4*>(v + off);
+    float x[8];
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    x[2 * j] = bf16_bits_to_f32(w[j] & 0xffffu);
-    x[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = bf16_bits_to_f32(w[j] & 0xffffu);
+      x[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
+    m = seg16_max(m);
+    const float sc = m / 127.0f;
+    const bool zero = !(sc != 0.0f);
+    const float r = 1.0f / (zero ? 1.0f : sc);
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int qv = zero ? 0 : (int)act_code(x[j], sc, r);
+      packed[j / 4] |= (uint32_t)(qv & 0xff) << (8 * (j % 4));
+    }
+    *reinterpret_cast<uint2*>(q + off) = make_uint2(packed[0], packed[1]);
+    if (sub == 0) s[gid] = sc;
   }
-  float m = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
-  m = seg16_max(m);
-  const float sc = m / 127.0f;
-  // q = rint(x / sc) with x / sc rounded to FP32 first, as defined.  Fast
-  // form: y = x * r with r = 1 / sc, both rounded to FP32, so
-  // |y - x / sc| <= 3 * 2^-24 * |x / sc| <= 2.3e-5 for |x / sc| <= 127, and
-  // the FP32 quotient is as close; when y is more than kMargin from every
-  // half-integer, rint(y) is the rint of the quotient.  Otherwise (rare), and
-  // for non-finite y, the quotient itself is taken.
-  constexpr float kMargin = 0x1p-14f;
-  const bool zero = !(sc != 0.0f);
-  const float r = 1.0f / (zero ? 1.0f : sc);
-  float qf[8];
-  uint32_t need = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float y = x[j] * r;
-    qf[j] = rintf(y);
-    need |= (fabsf(y - qf[j]) <= 0.5f - kMargin) ? 0u : 1u << j;
-  }
-  if (need != 0u && !zero) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if ((need >> j) & 1u) qf[j] = rintf(x[j] / sc);
-  }
-  uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int qv = zero ? 0 : (int)fminf(127.0f, fmaxf(-127.0f, qf[j]));
-    packed[j / 4] |= (uint32_t)(qv & 0xff) << (8 * (j % 4));
-  }
-  *reinterpret_cast<uint2*>(q + off) = make_uint2(packed[0], packed[1]);
-  if (sub == 0) s[gid] = sc;
 }
 
 __global__ __launch_bounds__(256) void k_quantize_weights(const float* __restrict__ w, int64_t ngroups, int G,
                                                           int bits, uint8_t* __restrict__ q,
                                                           uint16_t* __restrict__ s) {
-  const int64_t gid = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
   const int sub = threadIdx.x & 15;
-  if (gid >= ngroups) return;
-  const int64_t row = gid / G, g = gid % G;
-  const int64_t off = row * (int64_t)G * kGroup + g * kGroup + sub * 8;
-  const float4 a = *reinterpret_cast<const float4*>(w + off);
-  const float4 b = *reinterpret_cast<const float4*>(w + off + 4);
-  const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  float m = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
-  m = seg16_max(m);
-  const float qmax = bits == 4 ? 7.0f : 127.0f;
-  const float qmin = bits == 4 ? -8.0f : -127.0f;
-  const __half s16 = __float2half_rn(m / qmax);
-  const float sf = __half2float(s16);
-  int codes[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) codes[j] = sf != 0.0f ? (int)fminf(qmax, fmaxf(qmin, rintf(x[j] / sf))) : 0;
-  if (bits == 4) {
-    uint32_t packed = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) packed |= (uint32_t)(codes[j] & 0xf) << (4 * j);
-    *reinterpret_cast<uint32_t*>(q + (off >> 1)) = packed;
-  } else {
-    uint32_t p0 = 0, p1 = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      p0 |= (uint32_t)(codes[j] & 0xff) << (8 * j);
-      p1 |= (uint32_t)(codes[j + 4] & 0xff) << (8 * j);
+  for (int64_t gid = (int64_t)blockIdx.x * 16 + threadIdx.x / 16; gid < ngroups; gid += (int64_t)gridDim.x * 16) {
+    const int64_t row = gid / G, g = gid % G;
+    const int64_t off = row * (int64_t)G * kGroup + g * kGroup + sub * 8;
+    const float4 a = *reinterpret_cast<const float4*>(w + off);
+    const float4 b = *reinterpret_cast<const float4*>(w + off + 4);
+    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float m = 0.0f;
+  #pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
+    m = seg16_max(m);
+    const float qmax = bits == 4 ? 7.0f : 127.0f;
+    const float qmin = bits == 4 ? -8.0f : -127.0f;
+    const __half s16 = __float2half_rn(m / qmax);
+    const float sf = __half2float(s16);
+    int codes[8];
+  #pragma unroll
+    for (int j = 0; j < 8; ++j) codes[j] = sf != 0.0f ? (int)fminf(qmax, fmaxf(qmin, rintf(x[j] / sf))) : 0;
+    if (bits == 4) {
+      uint32_t packed = 0;
+  #pragma unroll
+      for (int j = 0; j < 8; ++j) packed |= (uint32_t)(codes[j] & 0xf) << (4 * j);
+      *reinterpret_cast<uint32_t*>(q + (off >> 1)) = packed;
+    } else {
+      uint32_t p0 = 0, p1 = 0;
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p0 |= (uint32_t)(codes[j] & 0xff) << (8 * j);
+        p1 |= (uint32_t)(codes[j + 4] & 0xff) << (8 * j);
+      }
+      *reinterpret_cast<uint2*>(q + off) = make_uint2(p0, p1);
     }
-    *reinterpret_cast<uint2*>(q + off) = make_uint2(p0, p1);
+    if (sub == 0) s[gid] = __half_as_ushort(s16);
   }
-  if (sub == 0) s[gid] = __half_as_ushort(s16);
 }
 
 }  // namespace
@@ -125,7 +106,7 @@ hipError_t launch_quantize_act(const uint16_t* v, int rows, int cols, int8_t* q,
   const int G = cols / kGroup;
   const int64_t ngroups = (int64_t)rows * G;
   if (ngroups == 0) return hipSuccess;
-  const int64_t blocks = (ngroups + 15) / 16;
+  const int64_t blocks = std::min((ngroups + 15) / 16, kMaxQuantBlocks);
   hipLaunchKernelGGL(k_quantize_act, dim3((unsigned)blocks), dim3(256), 0, stream, v, ngroups, G, q, s);
   return hipGetLastError();
 }
@@ -135,7 +116,7 @@ hipError_t launch_quantize_weights(const float* w, int64_t rows, int64_t cols, i
   const int G = (int)(cols / kGroup);
   const int64_t ngroups = rows * G;
   if (ngroups == 0) return hipSuccess;
-  const int64_t blocks = (ngroups + 15) / 16;
+  const int64_t blocks = std::min((ngroups + 15) / 16, kMaxQuantBlocks);
   hipLaunchKernelGGL(k_quantize_weights, dim3((unsigned)blocks), dim3(256), 0, stream, w, ngroups, G, bits, q, s);
   return hipGetLastError();
 }

@@ -113,3 +113,4 @@ def test_forward_argument_errors_need_no_gpu():
     # the device-error read needs a workspace
     assert L.qre_read_device_error(None, P(16), None) == -1
     assert L.qre_read_device_error(P(20), P(16), None) == -5
+

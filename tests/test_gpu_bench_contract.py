@@ -43,6 +43,12 @@ def test_default_workload_line():
     assert j["roofline"]["bound"] == "hbm" and j["roofline"]["unit"] == "GB/s"
     # tokens/s and ms/step describe the same timed region
     assert abs(j["value"] * j["ms_per_step"] / 1e3 - j["config"]["T"]) / j["config"]["T"] < 1e-3
+    # the prefill half of the metric and the measured read ceiling ride on the same line
+    pf = j["prefill"]
+    assert pf["workload"] == "prefill_w8a8" and pf["tokens_per_s"] > 0 and 0 < pf["gate_up_mfma_frac"] < 1
+    assert 0 < pf["step_i8_mfma_frac"] < 1 and pf["steps"] == 20
+    pr = j["hbm_read_probe"]
+    assert 0 < pr["frac_of_peak"] < 1 and 0 < j["roofline"]["frac_of_measured_read"] < 1.2
 
 
 def test_router_stage_line_with_cpu_baseline():
