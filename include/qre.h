@@ -120,6 +120,23 @@ int qre_moe_forward(const qre_desc* desc, const void* x, const int32_t* topk_ids
                     const float* topk_w, const qre_weights* weights, void* out,
                     void* workspace, size_t workspace_bytes, qre_stream_t stream);
 
+/* qre_moe_forward for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * workspace is a device array of QRE_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, created when the library is loaded and held until
+ * the process ends; this call allocates nothing.  Problems whose workspace
+ * (qre_workspace_bytes) exceeds that size are rejected with QRE_ERR_LIMIT
+ * (decode blocks and batched blocks at H = 2048 fit; prefill-sized ones do
+ * not).  All calls on one GPU share its array: calls that overlap in time on
+ * one GPU (different streams, different threads) race and give undefined
+ * results; calls ordered on one stream are fine.  The workspace needs no
+ * clearing (every call writes what it reads), and after the call it holds
+ * what qre_read_device_error would read from a caller's workspace. */
+#define QRE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int qre_moe_forward_noalloc(const qre_desc* desc, const void* x, const int32_t* topk_ids,
+                            const float* topk_w, const qre_weights* weights, void* out,
+                            qre_stream_t stream);
+
 /* qre_moe_forward that also records events[i] (each a hipEvent_t created by the
  * caller, or NULL to skip it) on `stream` between its steps: [0] before the
  * permutation, [1] before the gate/up GEMM, [2] after it, [3] before the down

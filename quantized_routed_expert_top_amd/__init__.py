@@ -73,6 +73,7 @@ def _lib():
         L.qre_quantize_weights.argtypes = [P, i64, i64, i32, P, P, P]
         L.qre_hbm_read_probe.argtypes = [P, sz, P, P]
         L.qre_forward_plan.argtypes = [P, P]
+        L.qre_moe_forward_noalloc.argtypes = [P, P, P, P, P, P, P]
         _L = L
     return _L
 
@@ -430,3 +431,25 @@ def forward_plan(T, H, I, E, K, bits, act_int8=False) -> int:
     _check("qre_forward_plan", _lib().qre_forward_plan(C.byref(_desc(T, H, I, E, K, bits, act_int8)), C.byref(n)))
     return n.value
 
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def moe_forward_noalloc(x, topk_ids, topk_w, W: QuantizedExperts, act_int8=False, out=None):
+    """moe_forward through the allocation-free entry point (the library's own
+    per-GPU workspace; workspace sizes above NOALLOC_SCRATCH_BYTES raise)."""
+    T, H = x.shape
+    K = topk_ids.shape[1]
+    _need(x, "x", torch.bfloat16, (T, H))
+    _need(topk_ids, "topk_ids", torch.int32, (T, K))
+    _need(topk_w, "topk_w", torch.float32, (T, K))
+    if W.H != H:
+        raise ValueError("weights and x disagree on H")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, (T, H))
+    d = _desc(T, H, W.I, W.E, K, W.bits, act_int8)
+    ws_struct = W._struct()
+    _check("qre_moe_forward_noalloc", _lib().qre_moe_forward_noalloc(
+        C.byref(d), _ptr(x), _ptr(topk_ids), _ptr(topk_w), C.byref(ws_struct), _ptr(out), _stream()))
+    return out

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "qre.h"
 #include "qre_internal.h"
 
@@ -14,6 +16,13 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
+// Workspace of qre_moe_forward_noalloc: one array per GPU, held until the
+// process ends.  In host code `scratch` is only a handle; its device address
+// on the current GPU comes from hipGetSymbolAddress, taken once per device.
+static __device__ __align__(256) uint8_t scratch[QRE_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 constexpr size_t kAlign = 256;
 
@@ -288,6 +297,31 @@ int qre_moe_forward(const qre_desc* desc, const void* x, const int32_t* topk_ids
                     const qre_weights* weights, void* out, void* workspace, size_t workspace_bytes,
                     qre_stream_t stream) {
   return moe_forward_impl(desc, x, topk_ids, topk_w, weights, out, workspace, workspace_bytes, nullptr,
+                          reinterpret_cast<hipStream_t>(stream));
+}
+
+int qre_moe_forward_noalloc(const qre_desc* desc, const void* x, const int32_t* topk_ids, const float* topk_w,
+                            const qre_weights* weights, void* out, qre_stream_t stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (make_layout(*desc, nullptr).bytes > QRE_NOALLOC_SCRATCH_BYTES) return QRE_ERR_LIMIT;
+  if (desc->T == 0) return QRE_OK;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return QRE_ERR_LIMIT;
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e);
+      g_scratch_ptr[dev] = p;
+    }
+    ws = g_scratch_ptr[dev];
+  }
+  return moe_forward_impl(desc, x, topk_ids, topk_w, weights, out, ws, QRE_NOALLOC_SCRATCH_BYTES, nullptr,
                           reinterpret_cast<hipStream_t>(stream));
 }
 

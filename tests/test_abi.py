@@ -114,3 +114,16 @@ def test_forward_argument_errors_need_no_gpu():
     assert L.qre_read_device_error(None, P(16), None) == -1
     assert L.qre_read_device_error(P(20), P(16), None) == -5
 
+
+def test_noalloc_rejects_oversized_problems_without_a_gpu():
+    """The allocation-free entry point refuses a problem whose workspace
+    exceeds the library's own before any HIP call."""
+    L = qre._lib()
+    w = qre._Weights(16, 16, 16, 16, 16, 16)
+    P = C.c_void_p
+    d = _desc(T=8192, weight_bits=8, act_int8=1)
+    assert L.qre_moe_forward_noalloc(C.byref(d), P(16), P(16), P(16), C.byref(w), P(16), None) == -9
+    assert L.qre_moe_forward_noalloc(C.byref(_desc(weight_bits=5)), P(16), P(16), P(16), C.byref(w), P(16),
+                                     None) == -3
+    n = C.c_size_t(0)
+    assert L.qre_workspace_bytes(C.byref(_desc()), C.byref(n)) == 0 and n.value <= qre.NOALLOC_SCRATCH_BYTES
