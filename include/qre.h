@@ -260,7 +260,8 @@ int qre_quantize_weights(const float* w, int64_t rows, int64_t cols, int32_t bit
  * mask).  QRE_PLAN_ROUTE_IN_GATE_UP: the permutation is computed inside the
  * gate/up kernel (no routing launch).  QRE_PLAN_COMBINE_IN_DOWN: the combine
  * runs inside the down kernel (no combine launch).  QRE_PLAN_BIG_TILES:
- * 128-row MFMA tiles (64 or more slots per expert). */
+ * 128-row MFMA tiles for the gate/up GEMM (64 or more slots per expert and
+ * a hidden size of at most 8192). */
 #define QRE_PLAN_ROUTE_IN_GATE_UP 1
 #define QRE_PLAN_COMBINE_IN_DOWN 2
 #define QRE_PLAN_BIG_TILES 4

@@ -753,7 +753,7 @@ hipError_t launch_routed_mode(const GemmProblem& gu, const GemmProblem& dn, cons
 // Row-tile height: 8 when experts see only a few rows each (decode blocks: the
 // weights stream once per tile either way, and a smaller activation tile leaves
 // LDS for more workgroups), 16 otherwise.
-int gemm_tile_rows(int64_t S, int E, int, int) { return big_applicable(S, E) ? 128 : (S <= 4 * (int64_t)E) ? 8 : 16; }
+int gemm_tile_rows(int64_t S, int E, int, int kdim) { return big_applicable(S, E, kdim) ? 128 : (S <= 4 * (int64_t)E) ? 8 : 16; }
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream) {
   if (p.max_tiles == 0 || p.n == 0) return hipSuccess;
@@ -768,7 +768,7 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream) {
 }
 
 bool routed_applicable(int64_t S, int E, int H, int I, int act_int8) {
-  if (S > kRoutedMaxSlots || big_applicable(S, E)) return false;
+  if (S > kRoutedMaxSlots || big_applicable(S, E, H) || big_applicable(S, E, I)) return false;
   auto ok_g = [](int G) { return (G >= 1 && G <= 5) || G == 8 || G == 12 || G == 16 || G == 32; };
   if (!ok_g(H / kGroup) || !ok_g(I / kGroup)) return false;
   const int64_t rows = (S <= 4 * (int64_t)E) ? 8 : 16;

@@ -323,16 +323,25 @@ struct Big {
 // row r keeps its four chunks at positions c ^ ((r >> 1) & 3).  Rows are 64
 // bytes apart, so any 8 consecutive rows then put a given chunk in 8 distinct
 // 16-byte slots of a 128-byte window and the operand reads (16 rows x one
-// chunk per 16 lanes) are free of bank conflicts.  The tile's activation and
-// weight scales of every group are loaded once, before the first stage, into
-// their own LDS region.  Every stage issues the same four direct loads per
-// thread and nothing else, so one static vmcnt fits all and no register waits
-// on a load in flight.
+// chunk per 16 lanes) are free of bank conflicts.  Every stage issues the same
+// four direct loads per thread and nothing else, so one static vmcnt fits all
+// and no register waits on a load in flight.
+//
+// The weights are the MFMA's A operand and the activations its B operand, so
+// the accumulator holds the tile transposed: a lane owns one activation row
+// and four consecutive output columns, which leave as one 8-byte store after
+// one packed BF16 conversion per pair.  The combination of a group's INT32
+// sums needs the activation scale of the lane's row (one FP32) and the weight
+// scales of its four columns (one 16-byte LDS read).  Both sets of scales of
+// every group are placed in LDS once per workgroup: the activation scales by
+// direct loads as [group][row] FP32; the weight scales, stored [row][group]
+// FP16, are first copied into the LDS of the fourth stage (not loaded before
+// the first round) and converted there into [group][row] FP32.
 template <bool DUAL>
 struct BigW8A8 {
   static constexpr int BM = 128, BNW = 128;
   static constexpr int BNO = DUAL ? 64 : 128;      // output columns per workgroup
-  static constexpr int TM = 4, TN = 4;             // 16x16 tiles per wave (64 x 64)
+  static constexpr int TM = 4, TN = 4;             // 16x16 tiles per wave (64 rows x 64 weight rows)
   static constexpr int HB = kGroup / 2;            // reduction bytes per stage (half a group)
   static constexpr int QA = BM * HB / 16 / 256;    // direct A loads per thread per stage (2)
   static constexpr int QB = BNW * HB / 16 / 256;   // direct B loads per thread per stage (2)
@@ -340,26 +349,27 @@ struct BigW8A8 {
   static constexpr int STAGE = B_OFF + BNW * HB;
   static constexpr int NS = 4;                     // stages; loads run NS - 1 stages ahead
   static constexpr int VM = QA + QB;               // direct loads per thread per stage
-  // After the stages, the tile's scales of every group, loaded once: the
-  // activation scales as [group][row] FP32, the weight scales as stored
-  // ([row][group] FP16) in halves of 64 rows (gate, up) or one of 128 rows,
-  // each padded to whole KB; then a 1 KB sink for the loads of waves with
-  // nothing to load.
-  static constexpr int NHALF = DUAL ? 2 : 1;
-  __host__ __device__ static int xs_bytes(int ng) { return ng * BM * 4; }
-  __host__ __device__ static int ws_half(int ng) { return (BNW / NHALF) * ng * 2; }
-  __host__ __device__ static int ws_half_pad(int ng) { return (ws_half(ng) + 1023) / 1024 * 1024; }
-  __host__ __device__ static size_t lds_bytes(int ng) {
-    return NS * (size_t)STAGE + xs_bytes(ng) + NHALF * ws_half_pad(ng) + 1024;
-  }
+  static constexpr int NHALF = DUAL ? 2 : 1;       // weight-scale sources (gate, up) or one
+  static constexpr int kMaxGroups = 64;            // the FP16 weight-scale copy fits one stage
+  // FP16 weight-scale copy in the fourth stage: NHALF parts of BNW / NHALF
+  // rows, each padded to whole KB (the direct loads move 1 KB per wave)
+  __host__ __device__ static int ws16_part(int ng) { return (BNW / NHALF) * ng * 2; }
+  __host__ __device__ static int ws16_pad(int ng) { return (ws16_part(ng) + 1023) / 1024 * 1024; }
+  // the stages, then the scales of every group: activations [group][row] and
+  // weights [group][weight row], both FP32
+  __host__ __device__ static size_t lds_bytes(int ng) { return NS * (size_t)STAGE + (size_t)ng * (BM + BNW) * 4; }
 
   __device__ static uint32_t chunk_pos(int row, int chunk) {
     return (uint32_t)(row * HB + ((chunk ^ ((row >> 1) & 3)) << 4));
   }
+  // first tile row of the wave's weight tile j (DUAL: j < 2 gate rows, j >= 2
+  // the same columns' up rows, 64 further on)
+  __device__ static int wrow0(int wn, int j) { return DUAL ? (j >> 1) * 64 + wn * 32 + (j & 1) * 16 : wn * 64 + j * 16; }
 
   template <class RowSrc>
   __device__ static void run(const GemmProblem& p, int cb, int e, int row0, int nrows, RowSrc src, uint8_t* lds) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, kb = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, kb = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     const int NG = p.kdim / kGroup;
     const int NH = 2 * NG;                          // stages of this tile
@@ -372,8 +382,10 @@ struct BigW8A8 {
     const rsrc_t ra = make_rsrc(p.a, p.a_rows * (int64_t)NG * kGroup);
     const rsrc_t rx = make_rsrc(p.a_scale, p.a_rows * (int64_t)NG * 4);
 
-    // per-lane source offsets of the direct loads: stage h = 2g + t holds the
-    // chunks 2c + t (c = 0..3) of group g, at offset g * 128 + t * 16 from these
+    // per-lane source offsets of the direct loads (the row's start plus the
+    // chunk pair): stage h = 2g + t then reads the chunks 2c + t of group g,
+    // at the scalar offset g * 128 + t * 16, which stays inside the row.
+    // Rows past the tile's end carry an out-of-range offset (zeros).
     uint32_t a_off[QA], b_off[QB];
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
@@ -388,50 +400,66 @@ struct BigW8A8 {
     }
     auto lds3 = [&](int off) { return (__attribute__((address_space(3))) void*)(lds + off); };
 
-    // the tile's scales of every group (before the first stage's loads, so
-    // the first stage's wait covers them).  Activation scales: load q (of
-    // 2 NG, four bytes a lane) is group q / 2, rows 64 (q % 2) + lane.  Weight
-    // scales: load q of a half copies its bytes [1 KB q, 1 KB q + 1 KB), lanes
-    // past the half's bytes reading zeros into the padding.  Every wave issues
-    // the same number of loads; the spare ones land in the sink.
-    const int XS_OFF = NS * STAGE, WS_OFF = XS_OFF + xs_bytes(NG);
-    const int SINK = WS_OFF + NHALF * ws_half_pad(NG);
-    {
-      const int nx = 2 * NG, nxw = (nx + 3) / 4;
-      for (int k = 0; k < nxw; ++k) {             // uniform
-        const int q = wave + 4 * k;
-        const int r = (q & 1) * 64 + lane;
-        const uint32_t off = q < nx && r < nrows ? (uint32_t)((src(r) * NG + (q >> 1)) * 4) : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lds3(q < nx ? XS_OFF + ((q >> 1) * BM + (q & 1) * 64) * 4 : SINK),
-                                                 4, off, 0, 0, 0);
-      }
-      const int hsz = ws_half(NG), nph = ws_half_pad(NG) / 1024, nw = NHALF * nph, nww = (nw + 3) / 4;
-      for (int k = 0; k < nww; ++k) {             // uniform
-        const int q = wave + 4 * k;
-        const int half = q / nph, b = (q - half * nph) * 1024 + 16 * lane;
-        const uint32_t off = q < nw && b < hsz ? (uint32_t)(n0 * NG * 2 + b) : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(DUAL && half == 1 ? rs1 : rs0,
-                                                 lds3(q < nw ? WS_OFF + half * ws_half_pad(NG) + (q - half * nph) * 1024
-                                                             : SINK),
-                                                 16, off, 0, 0, 0);
-      }
+    const int XS_OFF = NS * STAGE, WS_OFF = XS_OFF + NG * BM * 4, WS16_OFF = (NS - 1) * STAGE;
+    const int wpart = ws16_part(NG), wpad = ws16_pad(NG), nkb = wpad / 1024;
+    // the tile's scales of every group, before the first stage's loads.
+    // Activation scales: load q (of 2 NG, four bytes a lane) is group q / 2,
+    // rows 64 (q % 2) + lane.  Weight scales: load q of a part copies its
+    // bytes [1 KB q, 1 KB q + 1 KB), lanes past the part reading zeros into
+    // the padding.  The waves share the loads; a wave's count varies, which
+    // the static waits below tolerate (they only bound the newer loads).
+    for (int q = wave; q < 2 * NG; q += 4) {       // uniform
+      const int r = (q & 1) * 64 + lane;
+      const uint32_t off = r < nrows ? (uint32_t)((src(r) * NG + (q >> 1)) * 4) : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lds3(XS_OFF + ((q >> 1) * BM + (q & 1) * 64) * 4), 4, off, 0, 0, 0);
     }
-    // stage loads of half-group h into stage st (h past the end: out-of-range no-ops)
+    for (int q = wave; q < NHALF * nkb; q += 4) {  // uniform
+      const int part = q / nkb, b = (q - part * nkb) * 1024 + 16 * lane;
+      const uint32_t off = b < wpart ? (uint32_t)(n0 * NG * 2 + b) : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(DUAL && part == 1 ? rs1 : rs0, lds3(WS16_OFF + part * wpad + (q - part * nkb) * 1024),
+                                               16, off, 0, 0, 0);
+    }
+    // stage loads of half-group h into stage st; past the reduction's end
+    // (the last round) the same loads with an out-of-range offset, so that
+    // every stage keeps the same count
     auto issue = [&](int h, auto stc) {
       constexpr int st = decltype(stc)::value;
-      const uint32_t soff = h < NH ? 0u : kOOB;
-      const int g = h >> 1, t = h & 1;
-      const uint32_t koff = (uint32_t)(g * kGroup + t * 16);
       const int base = st * STAGE;
+      if (h < NH) {                                  // uniform
+        const uint32_t koff = (uint32_t)((h >> 1) * kGroup + (h & 1) * 16);
 #pragma unroll
-      for (int q = 0; q < QA; ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds3(base + (q * 4 + wave) * 1024), 16, a_off[q] + koff, soff, 0,
-                                                 0);
+        for (int q = 0; q < QA; ++q)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds3(base + (q * 4 + wave) * 1024), 16, a_off[q], koff, 0, 0);
 #pragma unroll
-      for (int q = 0; q < QB; ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(DUAL && q == 1 ? rw1 : rw0, lds3(base + B_OFF + (q * 4 + wave) * 1024),
-                                                 16, b_off[q] + koff, soff, 0, 0);
+        for (int q = 0; q < QB; ++q)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(DUAL && q == 1 ? rw1 : rw0, lds3(base + B_OFF + (q * 4 + wave) * 1024),
+                                                   16, b_off[q], koff, 0, 0);
+      } else {
+#pragma unroll
+        for (int q = 0; q < QA; ++q)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds3(base + (q * 4 + wave) * 1024), 16, kOOB, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < QB; ++q)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(DUAL && q == 1 ? rw1 : rw0, lds3(base + B_OFF + (q * 4 + wave) * 1024),
+                                                   16, kOOB, 0, 0, 0);
+      }
     };
+    issue(0, std::integral_constant<int, 0>{});
+    issue(1, std::integral_constant<int, 1>{});
+    issue(2, std::integral_constant<int, 2>{});
+
+    // weight scales to FP32 [group][tile row] (the first round's barrier
+    // publishes them and precedes the first load into the fourth stage)
+    __builtin_amdgcn_s_waitcnt(vmcnt_enc((NS - 1) * VM));   // this thread's scale loads landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();                            // and every thread's
+    asm volatile("" ::: "memory");
+    for (int idx = tid; idx < BNW * NG; idx += 256) {
+      const int g = idx / BNW, n = idx - g * BNW;
+      const int part = DUAL ? n >> 6 : 0, nr = DUAL ? n & 63 : n;
+      const uint16_t w = *reinterpret_cast<const uint16_t*>(lds + WS16_OFF + part * wpad + (nr * NG + g) * 2);
+      *reinterpret_cast<float*>(lds + WS_OFF + idx * 4) = half_bits_to_f32(w);
+    }
 
     // LDS read bases (row tile and column tile offsets are compile-time constants)
     const uint32_t a_rd = chunk_pos(wm * 64 + li, kb);
@@ -443,8 +471,8 @@ struct BigW8A8 {
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     i32x4_t part[TM][TN];
-    f32x4_t xsr[TM];
-    float ws[TN];
+    float xsv[TM];
+    f32x4_t wsv[TN];
 
     // one stage: wait for it, refill the stage read last time, compute
     auto body = [&](int h, auto stc) {
@@ -461,18 +489,12 @@ struct BigW8A8 {
         // a group past the reduction (the last round's): zero operands, zero scales
         const bool gin = (h >> 1) < NG;
         const int g = gin ? h >> 1 : NG - 1;
-        const float* xsl = reinterpret_cast<const float*>(lds + XS_OFF) + g * BM;
+        const float* xsl = reinterpret_cast<const float*>(lds + XS_OFF) + g * BM + wm * 64 + li;
+        const float* wsl = reinterpret_cast<const float*>(lds + WS_OFF) + g * BNW + 4 * kb;
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-          xsr[i] = gin ? *reinterpret_cast<const f32x4_t*>(xsl + wm * 64 + i * 16 + 4 * kb) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < TM; ++i) xsv[i] = gin ? xsl[i * 16] : 0.f;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int half = DUAL ? (j >> 1) : 0;
-          const int rowh = (DUAL ? wn * 32 + (j & 1) * 16 : wn * 64 + j * 16) + li;
-          const uint16_t w =
-              *reinterpret_cast<const uint16_t*>(lds + WS_OFF + half * ws_half_pad(NG) + (rowh * NG + g) * 2);
-          ws[j] = half_bits_to_f32(w);
-        }
+        for (int j = 0; j < TN; ++j) wsv[j] = *reinterpret_cast<const f32x4_t*>(wsl + wrow0(wn, j));
       }
       u32x4_t bv[TN];
 #pragma unroll
@@ -485,7 +507,7 @@ struct BigW8A8 {
         const i32x4_t av = __builtin_bit_cast(i32x4_t, *reinterpret_cast<const u32x4_t*>(base + a_rd + i * 16 * HB));
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          part[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, __builtin_bit_cast(i32x4_t, bv[j]),
+          part[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, bv[j]), av,
                                                              t == 0 ? i32x4_t{0, 0, 0, 0} : part[i][j], 0, 0, 0);
       }
       if constexpr (t == 1) {
@@ -495,13 +517,10 @@ struct BigW8A8 {
           for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-              acc[i][j][v] = __builtin_fmaf((float)part[i][j][v], xsr[i][v] * ws[j], acc[i][j][v]);
+              acc[i][j][v] = __builtin_fmaf((float)part[i][j][v], xsv[i] * wsv[j][v], acc[i][j][v]);
       }
     };
 
-    issue(0, std::integral_constant<int, 0>{});
-    issue(1, std::integral_constant<int, 1>{});
-    issue(2, std::integral_constant<int, 2>{});
     // whole rounds of four stages: with an odd group count the last group is
     // a no-op one (zero operands, zero scales), which keeps every round the
     // same straight-line code and every wait count static
@@ -513,24 +532,30 @@ struct BigW8A8 {
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));        // no load into LDS outlives the workgroup
 
+    // lane: activation row wm*64 + 16 i + li, output columns 4 kb .. 4 kb + 3
+    // of each 16-column tile
     uint16_t* out = static_cast<uint16_t*>(p.out);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i) {
+      const int m = wm * 64 + i * 16 + li;
+      if (m < nrows) {
+        uint16_t* orow = out + (int64_t)(row0 + m) * p.n + n0 + 4 * kb;
+        if constexpr (DUAL) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = wm * 64 + i * 16 + 4 * kb + v;
-        if (r < nrows) {
-          uint16_t* orow = out + (int64_t)(row0 + r) * p.n;
-          if constexpr (DUAL) {
+          for (int j = 0; j < 2; ++j) {
+            float hv[4];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-              orow[n0 + wn * 32 + j * 16 + li] = (uint16_t)f32_to_bf16_bits(silu(acc[i][j][v]) * acc[i][j + 2][v]);
-          } else {
-#pragma unroll
-            for (int j = 0; j < TN; ++j) orow[n0 + wn * 64 + j * 16 + li] = (uint16_t)f32_to_bf16_bits(acc[i][j][v]);
+            for (int v = 0; v < 4; ++v) hv[v] = silu(acc[i][j][v]) * acc[i][j + 2][v];
+            *reinterpret_cast<uint2*>(orow + wn * 32 + j * 16) = uint2{pack2_bf16(hv[0], hv[1]), pack2_bf16(hv[2], hv[3])};
           }
+        } else {
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            *reinterpret_cast<uint2*>(orow + wn * 64 + j * 16) =
+                uint2{pack2_bf16(acc[i][j][0], acc[i][j][1]), pack2_bf16(acc[i][j][2], acc[i][j][3])};
         }
       }
+    }
   }
 };
 
@@ -567,7 +592,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmProblem p) {
 template <bool DUAL>
 hipError_t launch_w8a8_cfg(const GemmProblem& p, hipStream_t stream) {
   using K = BigW8A8<DUAL>;
-  if (p.n % K::BNO != 0) return hipErrorInvalidValue;
+  if (p.n % K::BNO != 0 || p.kdim / kGroup > K::kMaxGroups) return hipErrorInvalidValue;
   const dim3 grid(p.n / K::BNO, (unsigned)((p.max_tiles + 7) / 8 * 8));
   hipLaunchKernelGGL((k_gemm_w8a8<DUAL>), grid, dim3(256), K::lds_bytes(p.kdim / kGroup), stream, p);
   return hipGetLastError();
@@ -584,9 +609,10 @@ hipError_t launch_big_cfg(const GemmProblem& p, hipStream_t stream) {
 
 }  // namespace
 
-bool big_applicable(int64_t S, int E) {
-  // many rows per expert: at least 64 on average
-  return S >= 64 * (int64_t)E;
+bool big_applicable(int64_t S, int E, int kdim) {
+  // many rows per expert: at least 64 on average; a reduction of at most 64
+  // groups (the INT8-activation kernel keeps every group's scales in LDS)
+  return S >= 64 * (int64_t)E && kdim <= BigW8A8<true>::kMaxGroups * kGroup;
 }
 
 hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t stream) {

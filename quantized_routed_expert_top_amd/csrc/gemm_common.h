@@ -42,7 +42,17 @@ __device__ __forceinline__ float bload_f32(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// g * sigmoid(g) with the hardware reciprocal (1 ulp): g -> -inf gives
+// g * rcp(inf) = -0, g -> +inf gives g * rcp(1) = g.
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// Two FP32 values rounded to BF16 (round to nearest even, one v_cvt_pk_bf16_f32)
+// and packed, lo in bits 15:0.
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
 
 __device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
   return __half2float(__ushort_as_half((unsigned short)h));

@@ -499,7 +499,7 @@ int qre_forward_plan(const qre_desc* desc, int32_t* plan) {
   const int64_t S = (int64_t)d.T * d.K;
   int32_t f = 0;
   if (routed_applicable(S, d.E, d.H, d.I, d.act_int8)) f |= QRE_PLAN_ROUTE_IN_GATE_UP;
-  if (big_applicable(S, d.E)) f |= QRE_PLAN_BIG_TILES;
+  if (big_applicable(S, d.E, d.H)) f |= QRE_PLAN_BIG_TILES;
   *plan = f;
   return QRE_OK;
 }

@@ -109,7 +109,7 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 int gemm_tile_rows(int64_t S, int E, int n, int kdim);
 // Many rows per expert: 128-row tiles on the MFMA-bound kernel (gemm_big.hip),
 // used by launch_gemm for problems whose tile height is 128.
-bool big_applicable(int64_t S, int E);
+bool big_applicable(int64_t S, int E, int kdim);
 hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t stream);
 
 // Decode-sized problems (up to kRoutedMaxSlots slots): the gate/up kernel
