@@ -40,6 +40,7 @@ class Workload:
     K: int            # experts per token
     weight_bits: int  # 4 or 8
     act_int8: bool    # INT8 activations (W4A8 / W8A8)
+    fmt: str = "int"  # "int": INT4/INT8 codes, FP16 scale per 128; "nvfp4": E2M1, E4M3 per 16, FP32 outer (W4A4)
     seed: int = 0
     router: str = "normal"     # "normal": logits N(0,1); "zipf": Zipf-biased
     zipf_s: float = 1.1
@@ -69,6 +70,11 @@ WORKLOADS = {
     # large MoE with Zipf(1.1) expert popularity
     "zipf_w4a16": Workload("zipf_w4a16", T=4096, H=4096, I=1536, E=256, K=8, weight_bits=4,
                            act_int8=False, seed=4, router="zipf"),
+    # NVFP4 (W4A4): the small block and the decode block at the mini model's MoE shape
+    "tiny_nvfp4": Workload("tiny_nvfp4", T=32, H=256, I=128, E=8, K=2, weight_bits=4, act_int8=False,
+                           fmt="nvfp4", seed=5),
+    "decode_nvfp4": Workload("decode_nvfp4", T=32, H=2048, I=512, E=256, K=8, weight_bits=4, act_int8=False,
+                             fmt="nvfp4"),
 }
 
 

@@ -71,6 +71,25 @@ def lib():
         L.orc_moe_forward.argtypes = [P, P, P, P, P, P, i64, P, P, P]
         L.orc_num_threads.restype = C.c_int
         L.orc_set_num_threads.argtypes = [C.c_int]
+        L.orc_e2m1_value.restype = C.c_double
+        L.orc_e2m1_value.argtypes = [C.c_int]
+        L.orc_e4m3_value.restype = C.c_double
+        L.orc_e4m3_value.argtypes = [C.c_uint8]
+        L.orc_e4m3_encode.restype = C.c_uint8
+        L.orc_e4m3_encode.argtypes = [C.c_double]
+        L.orc_e2m1_encode.restype = C.c_int
+        L.orc_e2m1_encode.argtypes = [C.c_double]
+        L.orc_fp4_quantize_weights.restype = C.c_int
+        L.orc_fp4_quantize_weights.argtypes = [P, i64, i64, i64, P, P, P]
+        L.orc_fp4_quantize_act.restype = C.c_int
+        L.orc_fp4_quantize_act.argtypes = [P, i64, i64, P, P, P]
+        L.orc_fp4_dequantize.argtypes = [P, P, P, i64, i64, i64, P]
+        L.orc_fp4_gate_up.restype = C.c_int
+        L.orc_fp4_gate_up.argtypes = [P, P, P, P, P, P, P, P, P]
+        L.orc_fp4_down.restype = C.c_int
+        L.orc_fp4_down.argtypes = [P, P, P, P, P, P, P, P]
+        L.orc_fp4_moe_forward.restype = C.c_int
+        L.orc_fp4_moe_forward.argtypes = [P, P, P, P, P, P, i64, P, P, P]
         _lib = L
     return _lib
 
@@ -319,3 +338,152 @@ def workload_experts(wl, experts, threads=None) -> QWeights:
     with ThreadPoolExecutor(threads or default_threads()) as ex:
         list(ex.map(one, [int(e) for e in experts]))
     return QWeights(gq, gs, uq, us, dq, ds)
+
+
+# ---- NVFP4 (W4A4) ------------------------------------------------------------------
+
+FP4_BLOCK = 16
+
+
+def e2m1_value(code: int) -> float:
+    return lib().orc_e2m1_value(int(code))
+
+
+def e4m3_value(b: int) -> float:
+    return lib().orc_e4m3_value(int(b))
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().orc_e4m3_encode(float(v))
+
+
+def e2m1_encode(v: float) -> int:
+    return lib().orc_e2m1_encode(float(v))
+
+
+def fp4_quantize_weights(w: np.ndarray):
+    """w float32 [..., rows, cols] -> (q uint8 [..., rows, cols/2], b uint8 E4M3
+    [..., rows, cols/16], outer float32 [...]): one outer scale per matrix."""
+    w = _c(w, np.float32)
+    lead, (rows, cols) = w.shape[:-2], w.shape[-2:]
+    mats = int(np.prod(lead, dtype=np.int64))
+    q = np.zeros(lead + (rows, cols // 2), dtype=np.uint8)
+    b = np.zeros(lead + (rows, cols // FP4_BLOCK), dtype=np.uint8)
+    o = np.zeros(lead, dtype=np.float32)
+    rc = lib().orc_fp4_quantize_weights(_p(w), mats, rows, cols, _p(q), _p(b), _p(o))
+    if rc != 0:
+        raise ValueError(f"orc_fp4_quantize_weights: {rc}")
+    return q, b, o
+
+
+def fp4_quantize_act(v_bf16: np.ndarray):
+    """v bf16 bits [rows, cols] -> (q uint8 [rows, cols/2], b uint8 [rows, cols/16],
+    row_scale float32 [rows])."""
+    v = _c(v_bf16, np.uint16)
+    rows, cols = v.shape
+    q = np.zeros((rows, cols // 2), dtype=np.uint8)
+    b = np.zeros((rows, cols // FP4_BLOCK), dtype=np.uint8)
+    r = np.zeros(rows, dtype=np.float32)
+    rc = lib().orc_fp4_quantize_act(_p(v), rows, cols, _p(q), _p(b), _p(r))
+    if rc != 0:
+        raise ValueError(f"orc_fp4_quantize_act: {rc}")
+    return q, b, r
+
+
+def fp4_dequantize(q, b, scale, cols: int, rows_per_scale: int) -> np.ndarray:
+    """float64 [rows, cols] = E2M1 * E4M3 * scale[row // rows_per_scale]."""
+    q, b, sc = _c(q, np.uint8), _c(b, np.uint8), _c(scale, np.float32)
+    rows = int(np.prod(q.shape[:-1], dtype=np.int64))
+    out = np.zeros((rows, cols), dtype=np.float64)
+    lib().orc_fp4_dequantize(_p(q), _p(b), _p(sc), rows, cols, int(rows_per_scale), _p(out))
+    return out
+
+
+class _FP4Mat(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("b", C.c_void_p), ("o", C.c_void_p)]
+
+
+class _FP4Weights(C.Structure):
+    _fields_ = [("gate", _FP4Mat), ("up", _FP4Mat), ("down", _FP4Mat)]
+
+
+class FP4Weights:
+    """NVFP4 weights of all experts: codes gate/up [E][I][H/2], down [E][H][I/2];
+    E4M3 block scales [E][rows][cols/16]; FP32 outer scales [E] per matrix."""
+
+    def __init__(self, gate_q, gate_b, gate_o, up_q, up_b, up_o, down_q, down_b, down_o):
+        self.gate_q, self.gate_b, self.gate_o = _c(gate_q, np.uint8), _c(gate_b, np.uint8), _c(gate_o, np.float32)
+        self.up_q, self.up_b, self.up_o = _c(up_q, np.uint8), _c(up_b, np.uint8), _c(up_o, np.float32)
+        self.down_q, self.down_b, self.down_o = _c(down_q, np.uint8), _c(down_b, np.uint8), _c(down_o, np.float32)
+
+    def _struct(self):
+        m = lambda q, b, o: _FP4Mat(_p(q), _p(b), _p(o))
+        return _FP4Weights(m(self.gate_q, self.gate_b, self.gate_o), m(self.up_q, self.up_b, self.up_o),
+                           m(self.down_q, self.down_b, self.down_o))
+
+
+def fp4_gate_up(xq, xb, xr, sorted_slot, offsets, W: FP4Weights, *, T, H, I, E, K, row_mask=None):
+    """h bf16 bits [S, I] by sorted row, from NVFP4-quantized x."""
+    h = np.zeros((T * K, I), dtype=np.uint16)
+    d = _shape(T, H, I, E, K, 4, False)
+    m = None if row_mask is None else _c(row_mask, np.uint8)
+    rc = lib().orc_fp4_gate_up(C.byref(d), _p(_c(xq, np.uint8)), _p(_c(xb, np.uint8)), _p(_c(xr, np.float32)),
+                               _p(_c(sorted_slot, np.int32)), _p(_c(offsets, np.int32)), C.byref(W._struct()),
+                               _p(m), _p(h))
+    if rc != 0:
+        raise ValueError(f"orc_fp4_gate_up: {rc}")
+    return h
+
+
+def fp4_down(hq, hb, hr, offsets, W: FP4Weights, *, T, H, I, E, K, row_mask=None):
+    """y bf16 bits [S, H] by sorted row, from NVFP4-quantized h."""
+    y = np.zeros((T * K, H), dtype=np.uint16)
+    d = _shape(T, H, I, E, K, 4, False)
+    m = None if row_mask is None else _c(row_mask, np.uint8)
+    rc = lib().orc_fp4_down(C.byref(d), _p(_c(hq, np.uint8)), _p(_c(hb, np.uint8)), _p(_c(hr, np.float32)),
+                            _p(_c(offsets, np.int32)), C.byref(W._struct()), _p(m), _p(y))
+    if rc != 0:
+        raise ValueError(f"orc_fp4_down: {rc}")
+    return y
+
+
+def fp4_moe_forward(x_bf16, topk_ids, topk_w, W: FP4Weights, *, E, I=None, tokens=None, return_y=False):
+    """Whole NVFP4 feed-forward; same returns as moe_forward."""
+    x = _c(x_bf16, np.uint16)
+    ids = _c(topk_ids, np.int32)
+    T, H = x.shape
+    K = ids.shape[1]
+    if I is None:
+        I = W.gate_b.shape[-2]
+    tok = None if tokens is None else _c(tokens, np.int64)
+    n = T if tok is None else len(tok)
+    o32 = np.zeros((n, H), dtype=np.float32)
+    o16 = np.zeros((n, H), dtype=np.uint16)
+    d = _shape(T, H, I, E, K, 4, False)
+    y = np.zeros((n, K, H), dtype=np.uint16) if return_y else None
+    rc = lib().orc_fp4_moe_forward(C.byref(d), _p(x), _p(ids), _p(_c(topk_w, np.float32)), C.byref(W._struct()),
+                                   _p(tok), 0 if tok is None else len(tok), _p(o32), _p(o16), _p(y))
+    if rc < 0:
+        raise ValueError(f"orc_fp4_moe_forward: {rc}")
+    return (o32, o16, rc, y) if return_y else (o32, o16, rc)
+
+
+def fp4_workload_experts(wl, experts, threads=None) -> FP4Weights:
+    """Oracle-quantized NVFP4 weights of the listed experts of a seeded
+    workload (float32 weights from the shared input generators); the other
+    experts are left zero."""
+    from concurrent.futures import ThreadPoolExecutor
+    from harness.inputs import GATE, UP, DOWN, default_threads, gen_expert_weight
+    E, H, I = wl.E, wl.H, wl.I
+    arrs = {}
+    for m, (rows, cols) in ((GATE, (I, H)), (UP, (I, H)), (DOWN, (H, I))):
+        arrs[m] = (np.zeros((E, rows, cols // 2), np.uint8), np.zeros((E, rows, cols // FP4_BLOCK), np.uint8),
+                   np.zeros(E, np.float32))
+
+    def one(e):
+        for m, (q, b, o) in arrs.items():
+            q[e], b[e], o[e] = fp4_quantize_weights(gen_expert_weight(wl, e, m))
+
+    with ThreadPoolExecutor(threads or default_threads()) as ex:
+        list(ex.map(one, [int(e) for e in experts]))
+    return FP4Weights(*arrs[GATE], *arrs[UP], *arrs[DOWN])

@@ -25,7 +25,11 @@
  *    "Quantization": fused gate/up/SiLU kernels; model card: gate, up and down
  *    projection weights);
  *  - the CPU path keeps experts compressed and expands one selected expert at a
- *    time (README "Build and run"); this oracle does the same.
+ *    time (README "Build and run"); this oracle does the same;
+ *  - NVFP4 (W4A4): E2M1 weights and inputs, an E4M3 scale per 16 values, an
+ *    FP32 outer scale per expert matrix (weights) or per input row (inputs),
+ *    FP32 accumulation (model card precision table, NVFP4 row; README
+ *    "Quantization").  Its readings are listed in the NVFP4 section below.
  *
  * Readings where the pages are silent (each one is a choice, listed with the
  * design notes):
@@ -607,4 +611,318 @@ void orc_set_num_threads(int n)
 #else
     (void)n;
 #endif
+}
+
+/* ------------------------------------------------------------------------ */
+/* NVFP4 (W4A4).  Model card "LLaDA2.2-flash for minnow", precision table,    */
+/* NVFP4 row: E2M1 FP4 weights with an E4M3 scale per 16 weights and an FP32  */
+/* outer scale per expert matrix; expert inputs dynamically quantized to E2M1 */
+/* with an E4M3 scale per 16 values and an FP32 outer scale per input row.    */
+/* README "Quantization": FP32 accumulation.  Model card, paragraph after the */
+/* table: the non-native path rebuilds the already quantized FP4 operands and */
+/* keeps the activation quantization.                                        */
+/*                                                                            */
+/* Readings where the pages are silent (listed with the design notes):        */
+/*  - outer scale S = max|v| / (6 * 448) in FP32 over the expert matrix        */
+/*    (weights) or the row (activations), so the largest block scale is the   */
+/*    E4M3 maximum 448 and the largest code the E2M1 maximum 6;              */
+/*  - block scale b = E4M3(max|block| / (S * 6)): the FP32 product S * 6, the */
+/*    FP32 quotient, rounded to E4M3 to nearest, ties to even, saturating at  */
+/*    448; S = 0 gives b = 0;                                                 */
+/*  - code c = E2M1(v / (b * S)): the FP32 product b * S, the FP32 quotient,  */
+/*    rounded to E2M1 to nearest, ties to even, saturating at 6; a zero      */
+/*    divisor, or a magnitude that rounds to zero, gives code 0 (+0);         */
+/*  - packing: element 2j in the low nibble of byte j, element 2j + 1 in the  */
+/*    high nibble (as INT4); blocks are 16 consecutive values along the       */
+/*    reduction dimension; scales are stored [rows][cols / 16], one byte each; */
+/*  - the product v = E2M1(c) * E4M3(b) * S is the dequantized value; the     */
+/*    expert matmuls sum exact products of such values (here in double) and   */
+/*    h, y are materialized in BF16 as in the other formats; h is quantized   */
+/*    again (per sorted row) before the down projection.                      */
+/* ------------------------------------------------------------------------ */
+
+#define ORC_FP4_BLOCK 16
+
+/* E2M1: sign, two exponent bits (bias 1), one mantissa bit; exponent field 0
+ * is subnormal (0 or 0.5).  Code bit 3 is the sign. */
+double orc_e2m1_value(int code)
+{
+    const int e = (code >> 1) & 3, m = code & 1;
+    const double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return (code & 8) ? -mag : mag;
+}
+
+/* E4M3 (the FN variant of the OCP 8-bit formats): sign, four exponent bits
+ * (bias 7), three mantissa bits; exponent field 0 is subnormal; all-ones
+ * exponent and mantissa is NaN; no infinities; largest finite 448. */
+double orc_e4m3_value(uint8_t b)
+{
+    const int e = (b >> 3) & 15, m = b & 7;
+    double mag;
+    if (e == 15 && m == 7) mag = NAN;
+    else if (e == 0) mag = ldexp((double)m, -9);
+    else mag = ldexp(1.0 + m / 8.0, e - 7);
+    return (b & 0x80) ? -mag : mag;
+}
+
+/* Nearest E4M3 (ties to even), saturating to +-448; NaN stays NaN. */
+uint8_t orc_e4m3_encode(double v)
+{
+    if (isnan(v)) return 0x7F;
+    double r = orc_round_format(v, 4, -6, 448.0);
+    if (isinf(r)) r = r > 0 ? 448.0 : -448.0;
+    const uint8_t sign = signbit(r) ? 0x80 : 0;
+    const double a = fabs(r);
+    if (a == 0.0) return sign;
+    if (a < ldexp(1.0, -6)) return sign | (uint8_t)ldexp(a, 9);       /* subnormal: a = m * 2^-9 */
+    int ex;
+    const double fr = frexp(a, &ex);                                  /* a = fr * 2^ex, fr in [0.5, 1) */
+    const int e = ex - 1;
+    return sign | (uint8_t)((e + 7) << 3) | (uint8_t)((2.0 * fr - 1.0) * 8.0);
+}
+
+/* Nearest E2M1 code (ties to even), saturating to +-6; a magnitude that
+ * rounds to zero gives code 0. */
+int orc_e2m1_encode(double v)
+{
+    double r = orc_round_format(v, 2, 0, 6.0);
+    if (isinf(r)) r = r > 0 ? 6.0 : -6.0;
+    if (r == 0.0) return 0;
+    const double a = fabs(r);
+    int code = 0;
+    for (int c = 1; c < 8; ++c)
+        if (orc_e2m1_value(c) == a) code = c;
+    return (r < 0 ? 8 : 0) | code;
+}
+
+/* The FP32 outer scale of a set of values with largest magnitude amax. */
+static float orc_fp4_outer(float amax) { return amax / (6.0f * 448.0f); }
+
+/* Quantize one row of `cols` values (float32) with outer scale S into packed
+ * codes (cols / 2 bytes) and E4M3 block scales (cols / 16 bytes). */
+static void orc_fp4_row(const float* v, int64_t cols, float S, uint8_t* q, uint8_t* b)
+{
+    memset(q, 0, (size_t)(cols / 2));
+    const float den = S * 6.0f;
+    for (int64_t blk = 0; blk < cols / ORC_FP4_BLOCK; ++blk) {
+        const float* vb = v + blk * ORC_FP4_BLOCK;
+        float m = 0.0f;
+        for (int j = 0; j < ORC_FP4_BLOCK; ++j) {
+            float a = fabsf(vb[j]);
+            if (a > m) m = a;
+        }
+        const float d = den > 0.0f ? m / den : 0.0f;
+        const uint8_t bs = orc_e4m3_encode((double)d);
+        b[blk] = bs;
+        const float den2 = (float)orc_e4m3_value(bs) * S;
+        for (int j = 0; j < ORC_FP4_BLOCK; ++j) {
+            const int c = den2 > 0.0f ? orc_e2m1_encode((double)(vb[j] / den2)) : 0;
+            const int64_t k = blk * ORC_FP4_BLOCK + j;
+            q[k / 2] |= (uint8_t)(k % 2 == 0 ? c : c << 4);
+        }
+    }
+}
+
+/* Weights: `mats` matrices of [rows][cols] float32, each with its own outer
+ * scale.  q [mats][rows][cols/2], b [mats][rows][cols/16], outer [mats].
+ * Returns 0, or -1 on bad arguments. */
+int orc_fp4_quantize_weights(const float* w, int64_t mats, int64_t rows, int64_t cols,
+                             uint8_t* q, uint8_t* b, float* outer)
+{
+    if (mats < 0 || rows < 0 || cols % ORC_FP4_BLOCK != 0) return -1;
+    for (int64_t mt = 0; mt < mats; ++mt) {
+        const float* wm = w + mt * rows * cols;
+        float amax = 0.0f;
+        for (int64_t i = 0; i < rows * cols; ++i) {
+            float a = fabsf(wm[i]);
+            if (a > amax) amax = a;
+        }
+        const float S = orc_fp4_outer(amax);
+        outer[mt] = S;
+        for (int64_t r = 0; r < rows; ++r)
+            orc_fp4_row(wm + r * cols, cols, S, q + (mt * rows + r) * (cols / 2),
+                        b + (mt * rows + r) * (cols / ORC_FP4_BLOCK));
+    }
+    return 0;
+}
+
+/* Activations: bf16 rows [rows][cols], an outer scale per row. */
+int orc_fp4_quantize_act(const uint16_t* v, int64_t rows, int64_t cols, uint8_t* q, uint8_t* b, float* row_scale)
+{
+    if (rows < 0 || cols % ORC_FP4_BLOCK != 0) return -1;
+    float* f = (float*)malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
+    if (!f) return -2;
+    for (int64_t r = 0; r < rows; ++r) {
+        float amax = 0.0f;
+        for (int64_t j = 0; j < cols; ++j) {
+            f[j] = orc_bf16_to_float(v[r * cols + j]);
+            float a = fabsf(f[j]);
+            if (a > amax) amax = a;
+        }
+        row_scale[r] = orc_fp4_outer(amax);
+        orc_fp4_row(f, cols, row_scale[r], q + r * (cols / 2), b + r * (cols / ORC_FP4_BLOCK));
+    }
+    free(f);
+    return 0;
+}
+
+/* E2M1(c) * E4M3(b) of element k of a packed row, without the outer scale
+ * (a product of at most 6 significant bits, exact in double). */
+static double orc_fp4_elem(const uint8_t* q, const uint8_t* b, int64_t k)
+{
+    const int c = (k % 2 == 0) ? (q[k / 2] & 0xF) : (q[k / 2] >> 4);
+    return orc_e2m1_value(c) * orc_e4m3_value(b[k / ORC_FP4_BLOCK]);
+}
+
+/* Dequantize rows: out[r][k] = E2M1 * E4M3 * scale[r / rows_per_scale]
+ * (float64; one outer scale per `rows_per_scale` rows). */
+void orc_fp4_dequantize(const uint8_t* q, const uint8_t* b, const float* scale, int64_t rows, int64_t cols,
+                        int64_t rows_per_scale, double* out)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < cols; ++k)
+            out[r * cols + k] = orc_fp4_elem(q + r * (cols / 2), b + r * (cols / ORC_FP4_BLOCK), k) *
+                                (double)scale[r / rows_per_scale];
+}
+
+typedef struct {
+    const uint8_t* q;   /* [E][rows][cols/2] */
+    const uint8_t* b;   /* [E][rows][cols/16] */
+    const float* o;     /* [E] */
+} orc_fp4_mat;
+
+typedef struct {
+    orc_fp4_mat gate, up, down;   /* gate/up [E][I][H], down [E][H][I] */
+} orc_fp4_weights;
+
+/* One expert matrix (rows x cols) as unscaled doubles E2M1 * E4M3 (the outer
+ * scale is applied to the dot product). */
+static double* orc_fp4_expand(const orc_fp4_mat* m, int32_t e, int64_t rows, int64_t cols)
+{
+    double* w = (double*)malloc(sizeof(double) * (size_t)(rows * cols));
+    const uint8_t* q = m->q + (int64_t)e * rows * (cols / 2);
+    const uint8_t* b = m->b + (int64_t)e * rows * (cols / ORC_FP4_BLOCK);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < cols; ++k)
+            w[r * cols + k] = orc_fp4_elem(q + r * (cols / 2), b + r * (cols / ORC_FP4_BLOCK), k);
+    return w;
+}
+
+/* Gate/up from quantized x: xq [T][H/2], xb [T][H/16], xr [T].  h bf16 [S][I]
+ * by sorted row; only rows whose row_mask flag is set (NULL = all). */
+int orc_fp4_gate_up(const orc_shape* d, const uint8_t* xq, const uint8_t* xb, const float* xr,
+                    const int32_t* sorted_slot, const int32_t* offsets, const orc_fp4_weights* W,
+                    const uint8_t* row_mask, uint16_t* h)
+{
+    const int64_t H = d->H, I = d->I;
+    int32_t* chunks = orc_row_chunks(offsets, d->E);
+    const int64_t nchunks = chunks[0];
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int32_t e = chunks[1 + 3 * c], r0 = chunks[2 + 3 * c], r1 = chunks[3 + 3 * c];
+        int any = 0;
+        for (int32_t r = r0; r < r1; ++r) if (!row_mask || row_mask[r]) { any = 1; break; }
+        if (!any) continue;
+        double* wg = orc_fp4_expand(&W->gate, e, I, H);
+        double* wu = orc_fp4_expand(&W->up, e, I, H);
+        double* xv = (double*)malloc(sizeof(double) * (size_t)H);
+        for (int32_t r = r0; r < r1; ++r) {
+            if (row_mask && !row_mask[r]) continue;
+            const int64_t t = sorted_slot[r] / d->K;
+            for (int64_t k = 0; k < H; ++k) xv[k] = orc_fp4_elem(xq + t * (H / 2), xb + t * (H / ORC_FP4_BLOCK), k);
+            for (int64_t i = 0; i < I; ++i) {
+                double sg = 0.0, su = 0.0;
+                for (int64_t k = 0; k < H; ++k) {
+                    sg += xv[k] * wg[i * H + k];
+                    su += xv[k] * wu[i * H + k];
+                }
+                const double g = sg * (double)xr[t] * (double)W->gate.o[e];
+                const double u = su * (double)xr[t] * (double)W->up.o[e];
+                h[(int64_t)r * I + i] = orc_bf16_from_double(orc_silu(g) * u);
+            }
+        }
+        free(wg); free(wu); free(xv);
+    }
+    free(chunks);
+    return 0;
+}
+
+/* Down from quantized h: hq [S][I/2], hb [S][I/16], hr [S] by sorted row.
+ * y bf16 [S][H] by sorted row. */
+int orc_fp4_down(const orc_shape* d, const uint8_t* hq, const uint8_t* hb, const float* hr,
+                 const int32_t* offsets, const orc_fp4_weights* W, const uint8_t* row_mask, uint16_t* y)
+{
+    const int64_t H = d->H, I = d->I;
+    int32_t* chunks = orc_row_chunks(offsets, d->E);
+    const int64_t nchunks = chunks[0];
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int32_t e = chunks[1 + 3 * c], r0 = chunks[2 + 3 * c], r1 = chunks[3 + 3 * c];
+        int any = 0;
+        for (int32_t r = r0; r < r1; ++r) if (!row_mask || row_mask[r]) { any = 1; break; }
+        if (!any) continue;
+        double* wd = orc_fp4_expand(&W->down, e, H, I);
+        double* hv = (double*)malloc(sizeof(double) * (size_t)I);
+        for (int32_t r = r0; r < r1; ++r) {
+            if (row_mask && !row_mask[r]) continue;
+            for (int64_t i = 0; i < I; ++i) hv[i] = orc_fp4_elem(hq + (int64_t)r * (I / 2), hb + (int64_t)r * (I / ORC_FP4_BLOCK), i);
+            for (int64_t j = 0; j < H; ++j) {
+                double s = 0.0;
+                for (int64_t i = 0; i < I; ++i) s += hv[i] * wd[j * I + i];
+                y[(int64_t)r * H + j] = orc_bf16_from_double(s * (double)hr[r] * (double)W->down.o[e]);
+            }
+        }
+        free(wd); free(hv);
+    }
+    free(chunks);
+    return 0;
+}
+
+/* The whole NVFP4 feed-forward (same contract as orc_moe_forward; d->bits and
+ * d->act_int8 are ignored).  Returns the number of dropped slots, or < 0. */
+int orc_fp4_moe_forward(const orc_shape* d, const uint16_t* x, const int32_t* ids, const float* topk_w,
+                        const orc_fp4_weights* W, const int64_t* tokens, int64_t ntok,
+                        float* out_f32, uint16_t* out_bf16, uint16_t* y_tok)
+{
+    const int64_t T = d->T, H = d->H, I = d->I, K = d->K, S = T * K;
+    if (H % ORC_FP4_BLOCK || I % ORC_FP4_BLOCK) return -1;
+    int32_t* counts = (int32_t*)malloc(sizeof(int32_t) * (size_t)(d->E > 0 ? d->E : 1));
+    int32_t* offsets = (int32_t*)malloc(sizeof(int32_t) * (size_t)(d->E + 1));
+    int32_t* sorted_slot = (int32_t*)malloc(sizeof(int32_t) * (size_t)(S > 0 ? S : 1));
+    int32_t* slot_row = (int32_t*)malloc(sizeof(int32_t) * (size_t)(S > 0 ? S : 1));
+    uint8_t* mask = (uint8_t*)calloc((size_t)(S > 0 ? S : 1), 1);
+    uint16_t* h = (uint16_t*)calloc((size_t)(S * I > 0 ? S * I : 1), sizeof(uint16_t));
+    uint16_t* y = (uint16_t*)calloc((size_t)(S * H > 0 ? S * H : 1), sizeof(uint16_t));
+    uint8_t* xq = (uint8_t*)calloc((size_t)(T * H / 2 > 0 ? T * H / 2 : 1), 1);
+    uint8_t* xb = (uint8_t*)calloc((size_t)(T * H / ORC_FP4_BLOCK > 0 ? T * H / ORC_FP4_BLOCK : 1), 1);
+    float* xr = (float*)calloc((size_t)(T > 0 ? T : 1), sizeof(float));
+    uint8_t* hq = (uint8_t*)calloc((size_t)(S * I / 2 > 0 ? S * I / 2 : 1), 1);
+    uint8_t* hb = (uint8_t*)calloc((size_t)(S * I / ORC_FP4_BLOCK > 0 ? S * I / ORC_FP4_BLOCK : 1), 1);
+    float* hr = (float*)calloc((size_t)(S > 0 ? S : 1), sizeof(float));
+    const int nbad = orc_route(ids, d->T, d->K, d->E, counts, offsets, sorted_slot, slot_row);
+    const int64_t n_out = tokens ? ntok : T;
+    for (int64_t n = 0; n < n_out; ++n) {
+        const int64_t t = tokens ? tokens[n] : n;
+        for (int64_t k = 0; k < K; ++k) if (slot_row[t * K + k] >= 0) mask[slot_row[t * K + k]] = 1;
+        orc_fp4_quantize_act(x + t * H, 1, H, xq + t * (H / 2), xb + t * (H / ORC_FP4_BLOCK), xr + t);
+    }
+    int rc = orc_fp4_gate_up(d, xq, xb, xr, sorted_slot, offsets, W, mask, h);
+    for (int64_t r = 0; rc == 0 && r < S; ++r)
+        if (mask[r]) orc_fp4_quantize_act(h + r * I, 1, I, hq + r * (I / 2), hb + r * (I / ORC_FP4_BLOCK), hr + r);
+    if (rc == 0) rc = orc_fp4_down(d, hq, hb, hr, offsets, W, mask, y);
+    if (rc == 0) orc_combine(y, slot_row, topk_w, d->T, d->K, d->H, tokens, ntok, out_f32, out_bf16);
+    if (rc == 0 && y_tok) {
+        for (int64_t n = 0; n < n_out; ++n) {
+            const int64_t t = tokens ? tokens[n] : n;
+            for (int64_t k = 0; k < K; ++k) {
+                const int32_t r = slot_row[t * K + k];
+                uint16_t* dst = y_tok + (n * K + k) * H;
+                if (r < 0) memset(dst, 0, sizeof(uint16_t) * (size_t)H);
+                else memcpy(dst, y + (int64_t)r * H, sizeof(uint16_t) * (size_t)H);
+            }
+        }
+    }
+    free(counts); free(offsets); free(sorted_slot); free(slot_row); free(mask); free(h); free(y);
+    free(xq); free(xb); free(xr); free(hq); free(hb); free(hr);
+    return rc == 0 ? nbad : rc;
 }
