@@ -2,15 +2,15 @@
 
 Draws the seeded inputs of ``inputs.py`` and converts the float32 expert
 weights to the packed INT4/INT8 format on the GPU with the library's own
-weight converter (``quantize_weights``), one expert at a time so host memory
-stays bounded.
+weight converter (``quantize_weights``, or ``nvfp4_quantize_weights`` for the
+NVFP4 format), one expert at a time so host memory stays bounded.
 """
 from __future__ import annotations
 
 import numpy as np
 import torch
 
-from quantized_routed_expert_top_amd import QuantizedExperts, quantize_weights
+from quantized_routed_expert_top_amd import Nvfp4Experts, QuantizedExperts, nvfp4_quantize_weights, quantize_weights
 from harness.inputs import GATE, UP, DOWN, Workload, gen_routing, gen_x, iter_expert_weights
 
 
@@ -18,7 +18,9 @@ def x_tensor(x_bits: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).view(torch.bfloat16).to(device)
 
 
-def gpu_experts(wl: Workload, device="cuda", threads: int | None = None) -> QuantizedExperts:
+def gpu_experts(wl: Workload, device="cuda", threads: int | None = None):
+    if wl.fmt == "nvfp4":
+        return gpu_nvfp4_experts(wl, device, threads)
     W = QuantizedExperts.empty(wl.E, wl.H, wl.I, wl.weight_bits, device=device)
     dst = {GATE: (W.gate_q, W.gate_s), UP: (W.up_q, W.up_s), DOWN: (W.down_q, W.down_s)}
     for e, mats in iter_expert_weights(wl, range(wl.E), threads=threads):
@@ -26,6 +28,19 @@ def gpu_experts(wl: Workload, device="cuda", threads: int | None = None) -> Quan
             q, s = dst[m]
             wd = torch.from_numpy(w).to(device, non_blocking=False)
             quantize_weights(wd, wl.weight_bits, out=(q[e], s[e]))
+    torch.cuda.synchronize(device)
+    return W
+
+
+def gpu_nvfp4_experts(wl: Workload, device="cuda", threads: int | None = None) -> Nvfp4Experts:
+    W = Nvfp4Experts.empty(wl.E, wl.H, wl.I, device=device)
+    dst = {GATE: (W.gate_q, W.gate_s, W.gate_o), UP: (W.up_q, W.up_s, W.up_o),
+           DOWN: (W.down_q, W.down_s, W.down_o)}
+    for e, mats in iter_expert_weights(wl, range(wl.E), threads=threads):
+        for m, w in zip((GATE, UP, DOWN), mats):
+            q, sc, o = dst[m]
+            wd = torch.from_numpy(w).to(device, non_blocking=False)
+            nvfp4_quantize_weights(wd[None], out=(q[e:e + 1], sc[e:e + 1], o[e:e + 1]))
     torch.cuda.synchronize(device)
     return W
 
@@ -57,7 +72,7 @@ def algorithmic_bytes(wl: Workload, ids: np.ndarray) -> dict:
     """Bytes the feed-forward itself must move: packed weights and scales of
     the touched experts, plus x, the routing inputs and out."""
     n_touched = len(touched_experts(ids, wl.E))
-    per_w = wl.weight_bits / 8 + 2 / 128
+    per_w = 0.5 + 1 / 16 if wl.fmt == "nvfp4" else wl.weight_bits / 8 + 2 / 128
     gate_up = 2 * wl.I * wl.H * per_w
     down = wl.H * wl.I * per_w
     io = wl.T * wl.H * 2 * 2 + wl.T * wl.K * 8

@@ -273,6 +273,104 @@ int qre_forward_plan(const qre_desc* desc, int32_t* plan);
  * kernels are compared with, next to the published peak. */
 int qre_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, qre_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * NVFP4 (W4A4) experts (model card "LLaDA2.2-flash for minnow", precision
+ * table, NVFP4 row; README "Quantization": FP32 accumulation; model card,
+ * paragraph after the table: without native FP4 tensor cores the already
+ * quantized FP4 operands are rebuilt for 16-bit matrix cores and the input
+ * quantization is kept).  The feed-forward is the one above with:
+ *   - weights: E2M1 codes, an E4M3 scale per 16 consecutive weights along the
+ *     reduction dimension and an FP32 outer scale per expert matrix;
+ *     w = e2m1(c) * e4m3(b) * outer;
+ *   - expert inputs x (gate/up) and h (down), BF16, quantized per row to E2M1
+ *     with an E4M3 scale per 16 values and an FP32 outer scale per row;
+ *   - dot products of the dequantized values accumulated in FP32; h and y
+ *     materialized in BF16.
+ * Quantizer (a reading; the pages give the format only): outer
+ * S = max|v| / 2688 (FP32; 2688 = 6 * 448), block scale b = E4M3 of
+ * max|block| / (S * 6), code = E2M1 of v / (e4m3(b) * S), every product and
+ * quotient rounded to FP32 first, both roundings to nearest-even and
+ * saturating (E4M3 at 448, E2M1 at 6), a zero magnitude stored as code 0,
+ * S = 0 giving all-zero codes and scales.  Finite inputs only.
+ *
+ * Layouts (row-major; a row is one output feature or one input row)
+ *    codes q           bytes [rows][cols/2]   element 2j in the low nibble of
+ *                                             byte j, 2j+1 in the high nibble;
+ *                                             E2M1: bit 3 sign, bits 2:1
+ *                                             exponent (bias 1), bit 0 mantissa
+ *    block scales s    bytes [rows][cols/16]  E4M3 (bias 7, max 448, no inf)
+ *    weights           gate, up [E][I][H] and down [E][H][I] as above, one
+ *                      FP32 outer scale per expert matrix: outer [E]
+ *    quantized inputs  x: [T][H] codes/scales + fp32 [T];
+ *                      h: [T*K][I] codes/scales + fp32 [T*K] (sorted rows)
+ * A descriptor selects NVFP4 with weight_bits = 4, group_size =
+ * QRE_NVFP4_BLOCK and act_int8 = 0 (QRE_ERR_BITS / QRE_ERR_GROUP /
+ * QRE_ERR_MODE otherwise); H and I must be multiples of 128 (QRE_ERR_SHAPE);
+ * the GEMMs stage up to 16 rows of x in LDS as FP16, which bounds H (4992
+ * when T*K > 4E, 10112 otherwise; QRE_ERR_LIMIT beyond).  The shared
+ * conventions above hold, except that the FP32 outer scales (read one value
+ * at a time) need only 4-byte alignment.
+ * ------------------------------------------------------------------------ */
+#define QRE_NVFP4_BLOCK 16
+
+typedef struct qre_nvfp4_matrix {
+  const void* q;        /* codes [E][rows][cols/2] */
+  const void* s;        /* E4M3 block scales [E][rows][cols/16] */
+  const float* outer;   /* FP32 [E] */
+} qre_nvfp4_matrix;
+
+typedef struct qre_nvfp4_weights {
+  qre_nvfp4_matrix gate, up, down;
+} qre_nvfp4_weights;
+
+/* Quantize `mats` float32 matrices w [mats][rows][cols] (cols % 16 == 0) to
+ * codes q [mats][rows][cols/2], block scales s [mats][rows][cols/16] and one
+ * outer scale per matrix, outer [mats] (which also serves as the kernels'
+ * scratch for the matrices' maxima).  Load-time utility. */
+int qre_nvfp4_quantize_weights(const float* w, int64_t mats, int64_t rows, int64_t cols, void* q, void* s,
+                               float* outer, qre_stream_t stream);
+
+/* Quantize BF16 rows v [rows][cols] (cols % 16 == 0) to codes q
+ * [rows][cols/2], block scales s [rows][cols/16] and row_scale [rows]. */
+int qre_nvfp4_quantize_act(const void* v, int32_t rows, int32_t cols, void* q, void* s, float* row_scale,
+                           qre_stream_t stream);
+
+/* Bytes of device workspace qre_nvfp4_moe_forward needs: the permutation,
+ * the row-tile lists, the quantized x, h (BF16 [T*K][I]) and its quantized
+ * form, y (BF16 [T*K][H]). */
+int qre_nvfp4_workspace_bytes(const qre_desc* desc, size_t* bytes);
+
+/* The whole NVFP4 feed-forward: routing permutation, quantization of x, fused
+ * gate/up/SiLU GEMM, quantization of h, down GEMM, combine (same contract and
+ * out layout as qre_moe_forward).  After the call the workspace also holds
+ * what qre_read_device_error reads and what
+ * qre_nvfp4_workspace_permutation points into. */
+int qre_nvfp4_moe_forward(const qre_desc* desc, const void* x, const int32_t* topk_ids, const float* topk_w,
+                          const qre_nvfp4_weights* weights, void* out, void* workspace, size_t workspace_bytes,
+                          qre_stream_t stream);
+
+/* Device pointers into an NVFP4 forward workspace (host out): the
+ * permutation of the last qre_nvfp4_moe_forward that used it. */
+int qre_nvfp4_workspace_permutation(const qre_desc* desc, void* workspace, int32_t** counts, int32_t** offsets,
+                                    int32_t** sorted_slot, int32_t** slot_row);
+
+/* Workspace of the NVFP4 stage calls below (row-tile lists). */
+int qre_nvfp4_stage_workspace_bytes(const qre_desc* desc, size_t* bytes);
+
+/* NVFP4 gate/up stage: from x quantized by qre_nvfp4_quantize_act (xq codes,
+ * xs block scales, xr row scales; [T] rows) and the permutation of qre_route
+ * (sorted_slot, offsets), h [T*K][I] BF16 by sorted row; rows past
+ * offsets[E] are not written. */
+int qre_nvfp4_gate_up(const qre_desc* desc, const void* xq, const void* xs, const float* xr, const int32_t* sorted_slot,
+                      const int32_t* offsets, const qre_nvfp4_weights* weights, void* h, void* workspace,
+                      size_t workspace_bytes, qre_stream_t stream);
+
+/* NVFP4 down stage: from h quantized per sorted row (hq, hs, hr; [T*K] rows),
+ * y [T*K][H] BF16 by sorted row. */
+int qre_nvfp4_down(const qre_desc* desc, const void* hq, const void* hs, const float* hr, const int32_t* offsets,
+                   const qre_nvfp4_weights* weights, void* y, void* workspace, size_t workspace_bytes,
+                   qre_stream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char* qre_status_string(int status);
 

@@ -74,6 +74,14 @@ def _lib():
         L.qre_hbm_read_probe.argtypes = [P, sz, P, P]
         L.qre_forward_plan.argtypes = [P, P]
         L.qre_moe_forward_noalloc.argtypes = [P, P, P, P, P, P, P]
+        L.qre_nvfp4_quantize_weights.argtypes = [P, i64, i64, i64, P, P, P, P]
+        L.qre_nvfp4_quantize_act.argtypes = [P, i32, i32, P, P, P, P]
+        L.qre_nvfp4_workspace_bytes.argtypes = [P, P]
+        L.qre_nvfp4_stage_workspace_bytes.argtypes = [P, P]
+        L.qre_nvfp4_moe_forward.argtypes = [P, P, P, P, P, P, P, sz, P]
+        L.qre_nvfp4_workspace_permutation.argtypes = [P, P, P, P, P, P]
+        L.qre_nvfp4_gate_up.argtypes = [P, P, P, P, P, P, P, P, P, sz, P]
+        L.qre_nvfp4_down.argtypes = [P, P, P, P, P, P, P, P, sz, P]
         _L = L
     return _L
 
@@ -453,3 +461,203 @@ def moe_forward_noalloc(x, topk_ids, topk_w, W: QuantizedExperts, act_int8=False
     _check("qre_moe_forward_noalloc", _lib().qre_moe_forward_noalloc(
         C.byref(d), _ptr(x), _ptr(topk_ids), _ptr(topk_w), C.byref(ws_struct), _ptr(out), _stream()))
     return out
+
+
+# ---- NVFP4 (W4A4) ------------------------------------------------------------------
+
+NVFP4_BLOCK = 16
+
+
+class _Fp4Mat(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("s", C.c_void_p), ("outer", C.c_void_p)]
+
+
+class _Fp4Weights(C.Structure):
+    _fields_ = [("gate", _Fp4Mat), ("up", _Fp4Mat), ("down", _Fp4Mat)]
+
+
+@dataclass
+class Nvfp4Experts:
+    """NVFP4 routed-expert weights on the GPU (layouts of include/qre.h):
+    codes uint8 [E, rows, cols/2], E4M3 block scales uint8 [E, rows, cols/16],
+    FP32 outer scales [E]; gate/up rows I, cols H; down rows H, cols I."""
+    gate_q: torch.Tensor
+    gate_s: torch.Tensor
+    gate_o: torch.Tensor
+    up_q: torch.Tensor
+    up_s: torch.Tensor
+    up_o: torch.Tensor
+    down_q: torch.Tensor
+    down_s: torch.Tensor
+    down_o: torch.Tensor
+
+    @property
+    def E(self):
+        return self.gate_q.shape[0]
+
+    @property
+    def I(self):
+        return self.gate_q.shape[1]
+
+    @property
+    def H(self):
+        return self.down_q.shape[1]
+
+    def tensors(self):
+        return (self.gate_q, self.gate_s, self.gate_o, self.up_q, self.up_s, self.up_o,
+                self.down_q, self.down_s, self.down_o)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in self.tensors())
+
+    def expert_nbytes(self) -> int:
+        return self.nbytes() // self.E
+
+    def clone(self) -> "Nvfp4Experts":
+        return Nvfp4Experts(*(t.clone() for t in self.tensors()))
+
+    def _struct(self):
+        E, H, I = self.E, self.H, self.I
+        for name, (rows, cols) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+            _need(getattr(self, name + "_q"), name + "_q", torch.uint8, (E, rows, cols // 2))
+            _need(getattr(self, name + "_s"), name + "_s", torch.uint8, (E, rows, cols // NVFP4_BLOCK))
+            _need(getattr(self, name + "_o"), name + "_o", torch.float32, (E,))
+        m = lambda n: _Fp4Mat(getattr(self, n + "_q").data_ptr(), getattr(self, n + "_s").data_ptr(),
+                              getattr(self, n + "_o").data_ptr())
+        return _Fp4Weights(m("gate"), m("up"), m("down"))
+
+    @staticmethod
+    def empty(E, H, I, device="cuda"):
+        u8, f32 = torch.uint8, torch.float32
+        mk = lambda rows, cols: (torch.empty((E, rows, cols // 2), dtype=u8, device=device),
+                                 torch.empty((E, rows, cols // NVFP4_BLOCK), dtype=u8, device=device),
+                                 torch.empty((E,), dtype=f32, device=device))
+        return Nvfp4Experts(*mk(I, H), *mk(I, H), *mk(H, I))
+
+
+def _fp4_desc(T, H, I, E, K):
+    return _Desc(T, H, I, E, K, 4, NVFP4_BLOCK, 0)
+
+
+def nvfp4_quantize_weights(w, out=None):
+    """w[..., rows, cols] fp32 -> (q uint8 [..., rows, cols/2], s uint8 E4M3 [..., rows, cols/16],
+    outer fp32 [...]): one outer scale per matrix.  `out` may give (q, s, outer)."""
+    _need(w, "w", torch.float32)
+    lead, (rows, cols) = tuple(w.shape[:-2]), tuple(w.shape[-2:])
+    mats = 1
+    for d in lead:
+        mats *= d
+    if out is None:
+        q = torch.empty(lead + (rows, cols // 2), dtype=torch.uint8, device=w.device)
+        s = torch.empty(lead + (rows, cols // NVFP4_BLOCK), dtype=torch.uint8, device=w.device)
+        o = torch.empty(lead, dtype=torch.float32, device=w.device)
+    else:
+        q, s, o = out
+        _need(q, "q", torch.uint8, lead + (rows, cols // 2))
+        _need(s, "s", torch.uint8, lead + (rows, cols // NVFP4_BLOCK))
+        _need(o, "outer", torch.float32, lead)
+    _check("qre_nvfp4_quantize_weights", _lib().qre_nvfp4_quantize_weights(
+        _ptr(w), mats, rows, cols, _ptr(q), _ptr(s), _ptr(o), _stream()))
+    return q, s, o
+
+
+def nvfp4_quantize_act(v):
+    """v[rows, cols] bf16 -> (q uint8 [rows, cols/2], s uint8 [rows, cols/16], row_scale fp32 [rows])."""
+    rows, cols = v.shape
+    _need(v, "v", torch.bfloat16)
+    q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=v.device)
+    s = torch.empty((rows, cols // NVFP4_BLOCK), dtype=torch.uint8, device=v.device)
+    r = torch.empty((rows,), dtype=torch.float32, device=v.device)
+    _check("qre_nvfp4_quantize_act", _lib().qre_nvfp4_quantize_act(_ptr(v), rows, cols, _ptr(q), _ptr(s), _ptr(r),
+                                                                   _stream()))
+    return q, s, r
+
+
+def nvfp4_workspace_bytes(T, H, I, E, K) -> int:
+    n = C.c_size_t(0)
+    _check("qre_nvfp4_workspace_bytes", _lib().qre_nvfp4_workspace_bytes(C.byref(_fp4_desc(T, H, I, E, K)),
+                                                                         C.byref(n)))
+    return n.value
+
+
+def nvfp4_stage_workspace(T, H, I, E, K, device="cuda"):
+    n = C.c_size_t(0)
+    _check("qre_nvfp4_stage_workspace_bytes",
+           _lib().qre_nvfp4_stage_workspace_bytes(C.byref(_fp4_desc(T, H, I, E, K)), C.byref(n)))
+    return _workspace(n.value, device)
+
+
+def nvfp4_moe_forward(x, topk_ids, topk_w, W: Nvfp4Experts, out=None, workspace=None):
+    """out[T,H] bf16 = NVFP4 routed-expert feed-forward of x[T,H] bf16."""
+    T, H = x.shape
+    K = topk_ids.shape[1]
+    _need(x, "x", torch.bfloat16, (T, H))
+    _need(topk_ids, "topk_ids", torch.int32, (T, K))
+    _need(topk_w, "topk_w", torch.float32, (T, K))
+    if W.H != H:
+        raise ValueError("weights and x disagree on H")
+    d = _fp4_desc(T, H, W.I, W.E, K)
+    if workspace is None:
+        workspace = _workspace(nvfp4_workspace_bytes(T, H, W.I, W.E, K), x.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, (T, H))
+    _need(workspace, "workspace", torch.uint8)
+    ws_struct = W._struct()
+    _check("qre_nvfp4_moe_forward", _lib().qre_nvfp4_moe_forward(
+        C.byref(d), _ptr(x), _ptr(topk_ids), _ptr(topk_w), C.byref(ws_struct), _ptr(out), _ptr(workspace),
+        workspace.numel(), _stream()))
+    return out
+
+
+def nvfp4_workspace_permutation(T, H, I, E, K, workspace):
+    """(counts, offsets, sorted_slot, slot_row) int32 views into an NVFP4 forward workspace."""
+    P = [C.c_void_p() for _ in range(4)]
+    _check("qre_nvfp4_workspace_permutation", _lib().qre_nvfp4_workspace_permutation(
+        C.byref(_fp4_desc(T, H, I, E, K)), _ptr(workspace), *[C.byref(p) for p in P]))
+    base = workspace.data_ptr()
+    S = T * K
+    return tuple(workspace[p.value - base:p.value - base + 4 * n].view(torch.int32)
+                 for p, n in zip(P, (E, E + 1, S, S)))
+
+
+def nvfp4_gate_up(xq, xs, xr, sorted_slot, offsets, W: Nvfp4Experts, K, h=None, workspace=None):
+    """h[T*K, I] bf16 by sorted row, from x quantized by nvfp4_quantize_act."""
+    T = xr.shape[0]
+    H, I, E = W.H, W.I, W.E
+    _need(xq, "xq", torch.uint8, (T, H // 2))
+    _need(xs, "xs", torch.uint8, (T, H // NVFP4_BLOCK))
+    _need(xr, "xr", torch.float32, (T,))
+    S = T * K
+    _need(sorted_slot, "sorted_slot", torch.int32, (S,))
+    _need(offsets, "offsets", torch.int32, (E + 1,))
+    if h is None:
+        h = torch.zeros((S, I), dtype=torch.bfloat16, device=xq.device)
+    _need(h, "h", torch.bfloat16, (S, I))
+    if workspace is None:
+        workspace = nvfp4_stage_workspace(T, H, I, E, K, xq.device)
+    ws_struct = W._struct()
+    _check("qre_nvfp4_gate_up", _lib().qre_nvfp4_gate_up(
+        C.byref(_fp4_desc(T, H, I, E, K)), _ptr(xq), _ptr(xs), _ptr(xr), _ptr(sorted_slot), _ptr(offsets),
+        C.byref(ws_struct), _ptr(h), _ptr(workspace), workspace.numel(), _stream()))
+    return h
+
+
+def nvfp4_down(hq, hs, hr, offsets, W: Nvfp4Experts, T, K, y=None, workspace=None):
+    """y[T*K, H] bf16 by sorted row, from h quantized per sorted row."""
+    H, I, E = W.H, W.I, W.E
+    S = T * K
+    _need(hq, "hq", torch.uint8, (S, I // 2))
+    _need(hs, "hs", torch.uint8, (S, I // NVFP4_BLOCK))
+    _need(hr, "hr", torch.float32, (S,))
+    _need(offsets, "offsets", torch.int32, (E + 1,))
+    if y is None:
+        y = torch.zeros((S, H), dtype=torch.bfloat16, device=hq.device)
+    _need(y, "y", torch.bfloat16, (S, H))
+    if workspace is None:
+        workspace = nvfp4_stage_workspace(T, H, I, E, K, hq.device)
+    ws_struct = W._struct()
+    _check("qre_nvfp4_down", _lib().qre_nvfp4_down(
+        C.byref(_fp4_desc(T, H, I, E, K)), _ptr(hq), _ptr(hs), _ptr(hr), _ptr(offsets), C.byref(ws_struct),
+        _ptr(y), _ptr(workspace), workspace.numel(), _stream()))
+    return y

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqre.so")
-SOURCES = ["qre_api.hip", "route.hip", "quant.hip", "gemm.hip", "gemm_big.hip", "combine.hip", "router.hip", "probe.hip"]
+SOURCES = ["qre_api.hip", "route.hip", "quant.hip", "gemm.hip", "gemm_big.hip", "combine.hip", "router.hip", "probe.hip", "nvfp4.hip"]
 HEADERS = [os.path.join(CSRC, "qre_internal.h"), os.path.join(CSRC, "gemm_common.h"), os.path.join(INCLUDE, "qre.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -29,6 +29,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return QRE_OK;
@@ -207,6 +208,124 @@ GemmProblem down_problem(const qre_desc& d, const void* h, const int8_t* hq, con
   p.max_tiles = mt;
   p.bm = bm;
   p.out = y;
+  p.n = d.H;
+  p.kdim = d.I;
+  return p;
+}
+
+// ---- NVFP4 (W4A4) ----
+
+int check_nvfp4_desc(const qre_desc* d) {
+  if (!d) return QRE_ERR_NULL;
+  if (d->weight_bits != 4) return QRE_ERR_BITS;
+  if (d->group_size != QRE_NVFP4_BLOCK) return QRE_ERR_GROUP;
+  if (d->act_int8 != 0) return QRE_ERR_MODE;
+  if (d->T < 0 || d->H <= 0 || d->I <= 0 || d->E <= 0 || d->K <= 0) return QRE_ERR_SHAPE;
+  if (d->H % QRE_GROUP || d->I % QRE_GROUP) return QRE_ERR_SHAPE;   // the GEMMs step 128 values at a time
+  if (d->K > d->E) return QRE_ERR_SHAPE;
+  if (d->E > QRE_MAX_EXPERTS) return QRE_ERR_LIMIT;
+  const int64_t S = (int64_t)d->T * d->K;
+  if (S >= (1ll << 31)) return QRE_ERR_LIMIT;
+  if (S * d->I * 2 >= (1ll << 31) || (int64_t)d->T * d->H >= (1ll << 31)) return QRE_ERR_LIMIT;
+  if ((int64_t)d->H * d->I >= (1ll << 31)) return QRE_ERR_LIMIT;
+  const int bm = fp4_tile_rows(S, d->E);
+  if (fp4_gemm_lds_bytes(bm, d->H) > kFp4MaxLds) return QRE_ERR_LIMIT;   // the staged rows of x fit in LDS
+  if (max_tiles(S, d->E, bm) > 65535) return QRE_ERR_LIMIT;              // grid.y
+  return QRE_OK;
+}
+
+int check_nvfp4_weights(const qre_nvfp4_weights* w, bool gate_up, bool down) {
+  if (!w) return QRE_ERR_NULL;
+  auto ok = [](const qre_nvfp4_matrix& m) { return m.q && m.s && m.outer; };
+  auto al = [](const qre_nvfp4_matrix& m) { return aligned16(m.q) && aligned16(m.s) && aligned4(m.outer); };
+  if ((gate_up && (!ok(w->gate) || !ok(w->up))) || (down && !ok(w->down))) return QRE_ERR_NULL;
+  if ((gate_up && (!al(w->gate) || !al(w->up))) || (down && !al(w->down))) return QRE_ERR_ALIGN;
+  return QRE_OK;
+}
+
+// Stage scratch: the header, both tile lists and the routing scratch.
+struct Fp4Stage {
+  int32_t* header;
+  int32_t* ntiles;            // [2]: gate/up, down
+  Tile *tiles_gu, *tiles_dn;
+  void* route_scratch;
+  int bm;
+  int64_t mt;
+};
+
+void carve_fp4_stage(const qre_desc& d, Carver& c, Fp4Stage& L) {
+  const int64_t S = (int64_t)d.T * d.K;
+  L.bm = fp4_tile_rows(S, d.E);
+  L.mt = max_tiles(S, d.E, L.bm);
+  L.header = c.take<int32_t>(kHeaderInts);
+  L.ntiles = c.take<int32_t>(2);
+  L.tiles_gu = c.take<Tile>(L.mt);
+  L.tiles_dn = c.take<Tile>(L.mt);
+  L.route_scratch = c.take<uint8_t>(route_scratch_bytes(S, d.E));
+}
+
+struct Fp4Layout {
+  Fp4Stage st;
+  int32_t *counts, *offsets, *sorted_slot, *slot_row;
+  uint8_t *xq, *xb; float* xr;   // x quantized: codes, block scales, row scales
+  uint16_t* h;                   // bf16 [S][I]
+  uint8_t *hq, *hb; float* hr;   // h quantized
+  uint16_t* y;                   // bf16 [S][H]
+  size_t bytes;
+};
+
+Fp4Layout make_fp4_layout(const qre_desc& d, void* ws) {
+  Fp4Layout L;
+  const int64_t S = (int64_t)d.T * d.K;
+  Carver c(ws);
+  carve_fp4_stage(d, c, L.st);
+  L.counts = c.take<int32_t>(d.E);
+  L.offsets = c.take<int32_t>(d.E + 1);
+  L.sorted_slot = c.take<int32_t>(S);
+  L.slot_row = c.take<int32_t>(S);
+  L.xq = c.take<uint8_t>((size_t)d.T * d.H / 2);
+  L.xb = c.take<uint8_t>((size_t)d.T * d.H / QRE_NVFP4_BLOCK);
+  L.xr = c.take<float>((size_t)d.T);
+  L.h = c.take<uint16_t>((size_t)S * d.I);
+  L.hq = c.take<uint8_t>((size_t)S * d.I / 2);
+  L.hb = c.take<uint8_t>((size_t)S * d.I / QRE_NVFP4_BLOCK);
+  L.hr = c.take<float>((size_t)S);
+  L.y = c.take<uint16_t>((size_t)S * d.H);
+  L.bytes = c.off;
+  return L;
+}
+
+Fp4Problem fp4_gate_up_problem(const qre_desc& d, const void* xq, const void* xb, const float* xr,
+                               const int32_t* sorted_slot, const qre_nvfp4_weights& w, const Fp4Stage& st, void* h) {
+  Fp4Problem p;
+  p.aq = static_cast<const uint8_t*>(xq);
+  p.ab = static_cast<const uint8_t*>(xb);
+  p.ar = xr;
+  p.a_rows = d.T;
+  p.gather_k = d.K;
+  p.sorted_slot = sorted_slot;
+  p.w0q = static_cast<const uint8_t*>(w.gate.q); p.w0b = static_cast<const uint8_t*>(w.gate.s); p.w0o = w.gate.outer;
+  p.w1q = static_cast<const uint8_t*>(w.up.q);   p.w1b = static_cast<const uint8_t*>(w.up.s);   p.w1o = w.up.outer;
+  p.tiles = st.tiles_gu; p.ntiles = st.ntiles; p.max_tiles = st.mt; p.bm = st.bm;
+  p.out = static_cast<uint16_t*>(h);
+  p.n = d.I;
+  p.kdim = d.H;
+  return p;
+}
+
+Fp4Problem fp4_down_problem(const qre_desc& d, const void* hq, const void* hb, const float* hr,
+                            const qre_nvfp4_weights& w, const Fp4Stage& st, void* y) {
+  Fp4Problem p;
+  p.aq = static_cast<const uint8_t*>(hq);
+  p.ab = static_cast<const uint8_t*>(hb);
+  p.ar = hr;
+  p.a_rows = (int64_t)d.T * d.K;
+  p.gather_k = 0;
+  p.sorted_slot = nullptr;
+  p.w0q = static_cast<const uint8_t*>(w.down.q); p.w0b = static_cast<const uint8_t*>(w.down.s); p.w0o = w.down.outer;
+  p.w1q = nullptr; p.w1b = nullptr; p.w1o = nullptr;
+  p.tiles = st.tiles_dn; p.ntiles = st.ntiles + 1; p.max_tiles = st.mt; p.bm = st.bm;
+  p.out = static_cast<uint16_t*>(y);
   p.n = d.H;
   p.kdim = d.I;
   return p;
@@ -509,6 +628,140 @@ int qre_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, qre_stream
   if (!aligned16(buf) || !aligned16(sink)) return QRE_ERR_ALIGN;
   if (bytes == 0 || bytes % 16) return QRE_ERR_SHAPE;
   return hip_status(launch_hbm_read(buf, (int64_t)bytes, sink, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qre_nvfp4_quantize_weights(const float* w, int64_t mats, int64_t rows, int64_t cols, void* q, void* s,
+                               float* outer, qre_stream_t stream) {
+  if (mats < 0 || rows < 0 || cols <= 0 || cols % QRE_NVFP4_BLOCK) return QRE_ERR_SHAPE;
+  if (mats * rows * (cols / QRE_NVFP4_BLOCK) >= (1ll << 40)) return QRE_ERR_LIMIT;
+  if (mats == 0 || rows == 0) return QRE_OK;
+  if (!w || !q || !s || !outer) return QRE_ERR_NULL;
+  if (!aligned16(w) || !aligned16(q) || !aligned16(s) || !aligned4(outer)) return QRE_ERR_ALIGN;
+  return hip_status(launch_fp4_quantize_weights(w, mats, rows, cols, static_cast<uint8_t*>(q),
+                                                static_cast<uint8_t*>(s), outer, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qre_nvfp4_quantize_act(const void* v, int32_t rows, int32_t cols, void* q, void* s, float* row_scale,
+                           qre_stream_t stream) {
+  if (rows < 0 || cols <= 0 || cols % QRE_NVFP4_BLOCK) return QRE_ERR_SHAPE;
+  if ((int64_t)rows * cols >= (1ll << 40)) return QRE_ERR_LIMIT;
+  if (rows == 0) return QRE_OK;
+  if (!v || !q || !s || !row_scale) return QRE_ERR_NULL;
+  if (!aligned16(v) || !aligned16(q) || !aligned16(s) || !aligned16(row_scale)) return QRE_ERR_ALIGN;
+  return hip_status(launch_fp4_quantize_act(static_cast<const uint16_t*>(v), rows, cols, static_cast<uint8_t*>(q),
+                                            static_cast<uint8_t*>(s), row_scale,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qre_nvfp4_workspace_bytes(const qre_desc* desc, size_t* bytes) {
+  int rc = check_nvfp4_desc(desc);
+  if (rc) return rc;
+  if (!bytes) return QRE_ERR_NULL;
+  *bytes = make_fp4_layout(*desc, nullptr).bytes;
+  return QRE_OK;
+}
+
+int qre_nvfp4_stage_workspace_bytes(const qre_desc* desc, size_t* bytes) {
+  int rc = check_nvfp4_desc(desc);
+  if (rc) return rc;
+  if (!bytes) return QRE_ERR_NULL;
+  Carver c(nullptr);
+  Fp4Stage L;
+  carve_fp4_stage(*desc, c, L);
+  *bytes = c.off;
+  return QRE_OK;
+}
+
+int qre_nvfp4_moe_forward(const qre_desc* desc, const void* x, const int32_t* topk_ids, const float* topk_w,
+                          const qre_nvfp4_weights* weights, void* out, void* workspace, size_t workspace_bytes,
+                          qre_stream_t stream) {
+  int rc = check_nvfp4_desc(desc);
+  if (rc) return rc;
+  const qre_desc& d = *desc;
+  if (d.T == 0) return QRE_OK;
+  if (!x || !topk_ids || !topk_w || !out || !workspace) return QRE_ERR_NULL;
+  rc = check_nvfp4_weights(weights, true, true);
+  if (rc) return rc;
+  if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(out) || !aligned16(workspace))
+    return QRE_ERR_ALIGN;
+  const Fp4Layout L = make_fp4_layout(d, workspace);
+  if (workspace_bytes < L.bytes) return QRE_ERR_WORKSPACE;
+  const int64_t S = (int64_t)d.T * d.K;
+  const Fp4Stage& st = L.st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_route(topk_ids, d.T, d.K, d.E, L.counts, L.offsets, L.sorted_slot, L.slot_row, st.header,
+                              st.route_scratch, st.tiles_gu, st.ntiles, st.bm, st.tiles_dn, st.ntiles + 1, st.bm, s);
+  if (e == hipSuccess) e = launch_fp4_quantize_act(static_cast<const uint16_t*>(x), d.T, d.H, L.xq, L.xb, L.xr, s);
+  if (e == hipSuccess)
+    e = launch_fp4_gemm(fp4_gate_up_problem(d, L.xq, L.xb, L.xr, L.sorted_slot, *weights, st, L.h), s);
+  if (e == hipSuccess) e = launch_fp4_quantize_act(L.h, S, d.I, L.hq, L.hb, L.hr, s);
+  if (e == hipSuccess) e = launch_fp4_gemm(fp4_down_problem(d, L.hq, L.hb, L.hr, *weights, st, L.y), s);
+  if (e == hipSuccess) e = launch_combine(L.y, L.slot_row, topk_w, d.T, d.K, d.H, static_cast<uint16_t*>(out), s);
+  return hip_status(e);
+}
+
+int qre_nvfp4_workspace_permutation(const qre_desc* desc, void* workspace, int32_t** counts, int32_t** offsets,
+                                    int32_t** sorted_slot, int32_t** slot_row) {
+  int rc = check_nvfp4_desc(desc);
+  if (rc) return rc;
+  if (!workspace || !counts || !offsets || !sorted_slot || !slot_row) return QRE_ERR_NULL;
+  const Fp4Layout L = make_fp4_layout(*desc, workspace);
+  *counts = L.counts;
+  *offsets = L.offsets;
+  *sorted_slot = L.sorted_slot;
+  *slot_row = L.slot_row;
+  return QRE_OK;
+}
+
+static int check_fp4_stage_ws(const qre_desc& d, const void* workspace, size_t workspace_bytes, Fp4Stage& st) {
+  if (!workspace) return QRE_ERR_NULL;
+  if (!aligned16(workspace)) return QRE_ERR_ALIGN;
+  Carver c(const_cast<void*>(workspace));
+  carve_fp4_stage(d, c, st);
+  if (workspace_bytes < c.off) return QRE_ERR_WORKSPACE;
+  return QRE_OK;
+}
+
+int qre_nvfp4_gate_up(const qre_desc* desc, const void* xq, const void* xs, const float* xr, const int32_t* sorted_slot,
+                      const int32_t* offsets, const qre_nvfp4_weights* weights, void* h, void* workspace,
+                      size_t workspace_bytes, qre_stream_t stream) {
+  int rc = check_nvfp4_desc(desc);
+  if (rc) return rc;
+  const qre_desc& d = *desc;
+  if (d.T == 0) return QRE_OK;
+  Fp4Stage st;
+  rc = check_fp4_stage_ws(d, workspace, workspace_bytes, st);
+  if (rc) return rc;
+  if (!xq || !xs || !xr || !sorted_slot || !offsets || !h) return QRE_ERR_NULL;
+  rc = check_nvfp4_weights(weights, true, false);
+  if (rc) return rc;
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(xr) || !aligned16(sorted_slot) || !aligned16(offsets) ||
+      !aligned16(h))
+    return QRE_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_build_tiles(offsets, d.E, st.tiles_gu, st.ntiles, st.bm, nullptr, nullptr, 0, s);
+  if (e == hipSuccess) e = launch_fp4_gemm(fp4_gate_up_problem(d, xq, xs, xr, sorted_slot, *weights, st, h), s);
+  return hip_status(e);
+}
+
+int qre_nvfp4_down(const qre_desc* desc, const void* hq, const void* hs, const float* hr, const int32_t* offsets,
+                   const qre_nvfp4_weights* weights, void* y, void* workspace, size_t workspace_bytes,
+                   qre_stream_t stream) {
+  int rc = check_nvfp4_desc(desc);
+  if (rc) return rc;
+  const qre_desc& d = *desc;
+  if (d.T == 0) return QRE_OK;
+  Fp4Stage st;
+  rc = check_fp4_stage_ws(d, workspace, workspace_bytes, st);
+  if (rc) return rc;
+  if (!hq || !hs || !hr || !offsets || !y) return QRE_ERR_NULL;
+  rc = check_nvfp4_weights(weights, false, true);
+  if (rc) return rc;
+  if (!aligned16(hq) || !aligned16(hs) || !aligned16(hr) || !aligned16(offsets) || !aligned16(y)) return QRE_ERR_ALIGN;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_build_tiles(offsets, d.E, st.tiles_dn, st.ntiles + 1, st.bm, nullptr, nullptr, 0, s);
+  if (e == hipSuccess) e = launch_fp4_gemm(fp4_down_problem(d, hq, hs, hr, *weights, st, y), s);
+  return hip_status(e);
 }
 
 }  // extern "C"

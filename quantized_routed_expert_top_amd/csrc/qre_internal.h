@@ -128,6 +128,32 @@ hipError_t launch_down_routed(const GemmProblem& p, const RouteOut& ro, hipStrea
 
 
 
+// NVFP4 (W4A4): E2M1 codes, E4M3 scale per 16 values, FP32 outer scale per
+// expert matrix (weights) or per input row (activations).
+struct Fp4Problem {
+  const uint8_t* aq;      // activation codes [a_rows][kdim/2]
+  const uint8_t* ab;      // activation E4M3 block scales [a_rows][kdim/16]
+  const float* ar;        // activation outer scales [a_rows]
+  int64_t a_rows;
+  int gather_k;           // >0: A row of sorted row r is token sorted_slot[r] / gather_k; 0: A row = r
+  const int32_t* sorted_slot;
+  const uint8_t* w0q; const uint8_t* w0b; const float* w0o;   // [E][n][kdim/2], [E][n][kdim/16], [E]
+  const uint8_t* w1q; const uint8_t* w1b; const float* w1o;   // up (fused gate/up) or null
+  const Tile* tiles; const int32_t* ntiles; int64_t max_tiles; int bm;
+  uint16_t* out;          // bf16 [S][n]
+  int n, kdim;
+};
+constexpr size_t kFp4MaxLds = 160 * 1024;
+constexpr int64_t kMaxQuantBlocks = 1 << 16;   // grid cap of the grid-stride quantizers
+// Row-tile height of the NVFP4 GEMMs (8 or 16 rows).
+int fp4_tile_rows(int64_t S, int E);
+size_t fp4_gemm_lds_bytes(int bm, int kdim);
+hipError_t launch_fp4_gemm(const Fp4Problem& p, hipStream_t stream);
+hipError_t launch_fp4_quantize_act(const uint16_t* v, int64_t rows, int cols, uint8_t* q, uint8_t* b, float* rs,
+                                   hipStream_t stream);
+hipError_t launch_fp4_quantize_weights(const float* w, int64_t mats, int64_t rows, int64_t cols, uint8_t* q,
+                                       uint8_t* b, float* outer, hipStream_t stream);
+
 // Combine.
 hipError_t launch_combine(const uint16_t* y, const int32_t* slot_row, const float* topk_w, int T, int K,
                           int H, uint16_t* out, hipStream_t stream);

@@ -26,7 +26,6 @@ namespace {
 
 // Grid-stride over (row, group) pairs, one 16-lane segment each; the grid is
 // bounded, so any size the entry point accepts launches.
-constexpr int64_t kMaxQuantBlocks = 1 << 16;
 
 __global__ __launch_bounds__(256) void k_quantize_act(const uint16_t* __restrict__ v, int64_t ngroups, int G,
                                                       int8_t* __restrict__ q, float* __restrict__ s) {

@@ -127,3 +127,49 @@ def test_noalloc_rejects_oversized_problems_without_a_gpu():
                                      None) == -3
     n = C.c_size_t(0)
     assert L.qre_workspace_bytes(C.byref(_desc()), C.byref(n)) == 0 and n.value <= qre.NOALLOC_SCRATCH_BYTES
+
+
+def _fp4_desc(**kw):
+    return _desc(**{"group_size": 16, **kw})
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(weight_bits=8), -3), (dict(group_size=128), -4), (dict(act_int8=1), -8), (dict(H=2000), -2),
+    (dict(I=144), -2), (dict(K=300), -2), (dict(E=1024), -9),
+    (dict(T=64, H=8192, E=8), -9),                     # 16 staged rows of x exceed the LDS
+    (dict(T=4, H=8192, E=8, K=2), 0),                  # 8 rows fit
+])
+def test_nvfp4_descriptor_validation(kw, code):
+    n = C.c_size_t(0)
+    assert qre._lib().qre_nvfp4_workspace_bytes(C.byref(_fp4_desc(**kw)), C.byref(n)) == code
+
+
+def test_nvfp4_argument_errors_need_no_gpu():
+    L = qre._lib()
+    P = C.c_void_p
+    m = lambda o=16: qre._Fp4Mat(16, 16, o)
+    w = qre._Fp4Weights(m(), m(), m())
+    d = _fp4_desc()
+    ws = C.c_size_t(0)
+    assert L.qre_nvfp4_workspace_bytes(C.byref(d), C.byref(ws)) == 0
+    args = lambda **k: [C.byref(k.get("d", d)), k.get("x", P(16)), P(16), P(16), C.byref(k.get("w", w)),
+                        k.get("out", P(32)), P(16), k.get("n", ws.value), None]
+    assert L.qre_nvfp4_moe_forward(*args(x=None)) == -1
+    assert L.qre_nvfp4_moe_forward(*args(out=P(24))) == -5
+    assert L.qre_nvfp4_moe_forward(*args(n=ws.value - 1)) == -6
+    assert L.qre_nvfp4_moe_forward(*args(w=qre._Fp4Weights(m(), qre._Fp4Mat(16, None, 16), m()))) == -1
+    assert L.qre_nvfp4_moe_forward(*args(w=qre._Fp4Weights(m(), m(), m(o=18)))) == -5     # outer: 4-byte alignment
+    assert L.qre_nvfp4_moe_forward(*args(d=_desc())) == -4                              # an INT descriptor
+    assert L.qre_nvfp4_moe_forward(C.byref(_fp4_desc(T=0)), None, None, None, None, None, None, 0, None) == 0
+    # quantizers
+    assert L.qre_nvfp4_quantize_act(P(16), 4, 100, P(16), P(16), P(16), None) == -2
+    assert L.qre_nvfp4_quantize_act(P(16), 4, 64, P(16), P(16), None, None) == -1
+    assert L.qre_nvfp4_quantize_weights(P(16), 2, 4, 24, P(16), P(16), P(16), None) == -2
+    assert L.qre_nvfp4_quantize_weights(P(16), 2, 4, 32, P(16), P(16), P(18), None) == -5
+    assert L.qre_nvfp4_quantize_weights(None, 0, 4, 32, None, None, None, None) == 0
+    # stages: the workspace must hold the row tiles
+    sw = C.c_size_t(0)
+    assert L.qre_nvfp4_stage_workspace_bytes(C.byref(d), C.byref(sw)) == 0 and sw.value > 0
+    assert L.qre_nvfp4_gate_up(C.byref(d), P(16), P(16), P(16), P(16), P(16), C.byref(w), P(16), P(16), 16,
+                               None) == -6
+    assert L.qre_nvfp4_down(C.byref(d), P(16), P(16), None, P(16), C.byref(w), P(16), P(16), sw.value, None) == -1
