@@ -201,7 +201,10 @@ __device__ __forceinline__ f16x8_t rebuild8(uint32_t w, f16x2_t s2) {
 // loads 16 code bytes (reduction positions 32 kb .. 32 kb + 31 of the step)
 // and the two scale bytes of those two blocks, DEPTH steps ahead; MFMA step t
 // of the four takes code word t, matched by LDS chunk 4 kb + t of the row.
-template <bool DUAL, int FN, int BMR, int DEPTH>
+// NS > 0 is the number of 128-wide steps, known at compile time: the stream
+// is straight-line code and every wait covers exactly the step it needs;
+// NS = 0 takes the count at run time (other reduction lengths).
+template <bool DUAL, int FN, int BMR, int DEPTH, int NS>
 struct Fp4Gemm {
   static constexpr int NM = DUAL ? 2 : 1;
   static constexpr int BN = 4 * 16 * FN;                          // output columns per workgroup
@@ -220,7 +223,8 @@ struct Fp4Gemm {
   template <class RowSrc>
   __device__ static void run(const Fp4Problem& p, int e, int row0, int nrows, RowSrc src_row, uint8_t* lds, int cb) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, kb = lane >> 4;
-    const int K = p.kdim, NS = K / kGroup;                          // 128-wide steps
+    const int K = NS > 0 ? NS * kGroup : p.kdim;
+    const int nsteps = K / kGroup;
     const int col0 = min((cb * 4 + wave) * 16 * FN, p.n - 16 * FN);  // a surplus wave recomputes the last tile, stores nothing
     const int64_t cbytes = (int64_t)p.n * (K / 2), sbytes = (int64_t)p.n * (K / kBlk);
     rsrc_t rc[NM], rb[NM];
@@ -238,7 +242,7 @@ struct Fp4Gemm {
     }
     WBuf buf[DEPTH];
     auto load_step = [&](WBuf& bf, int g) {
-      const bool in = g < NS;
+      const bool in = NS > 0 || g < nsteps;
 #pragma unroll
       for (int f = 0; f < FN; ++f)
 #pragma unroll
@@ -249,7 +253,7 @@ struct Fp4Gemm {
     };
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) {
-      load_step(buf[j], j);
+      if (NS == 0 || j < NS) load_step(buf[j], j);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -269,43 +273,59 @@ struct Fp4Gemm {
     __syncthreads();
     if ((cb * 4 + wave) * 16 * FN >= p.n) return;                 // wave-uniform, after the barrier
 
+    // the lane's LDS row and the offsets of its four chunks in step 0 (the
+    // swizzle touches only the low 3 bits of a chunk index, and a step spans
+    // 16 chunks, so step g adds g * 256 bytes)
     const int arow = (BMR == 16) ? li : (li & (BMR - 1));         // LDS row feeding MFMA row li
+    uint32_t a_base[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) a_base[t] = lds_chunk(arow, kb * 4 + t, K);
     f32x4_t acc[FN][NM];
 #pragma unroll
     for (int f = 0; f < FN; ++f)
 #pragma unroll
       for (int m = 0; m < NM; ++m) acc[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int g0 = 0; g0 < NS; g0 += DEPTH) {
+    auto step = [&](WBuf& bf, int g) {
+      f16x2_t s_lo[FN][NM], s_hi[FN][NM];
 #pragma unroll
-      for (int j = 0; j < DEPTH; ++j) {
-        const int g = g0 + j;
-        if (g < NS) {                                              // uniform
-          WBuf& bf = buf[j];
-          f16x2_t s_lo[FN][NM], s_hi[FN][NM];
+      for (int f = 0; f < FN; ++f)
 #pragma unroll
-          for (int f = 0; f < FN; ++f)
-#pragma unroll
-            for (int m = 0; m < NM; ++m) {
-              const f16x2_t s = __builtin_bit_cast(f16x2_t,
-                                                   __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bf.s[f][m], 1.0f, false));
-              s_lo[f][m] = f16x2_t{s[0], s[0]};
-              s_hi[f][m] = f16x2_t{s[1], s[1]};
-            }
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const f16x8_t a = *reinterpret_cast<const f16x8_t*>(lds + lds_chunk(arow, g * 16 + kb * 4 + t, K));
-#pragma unroll
-            for (int f = 0; f < FN; ++f)
-#pragma unroll
-              for (int m = 0; m < NM; ++m) {
-                const f16x8_t bv = rebuild8(bf.c[f][m][t], t < 2 ? s_lo[f][m] : s_hi[f][m]);
-                acc[f][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bv, acc[f][m], 0, 0, 0);
-              }
-          }
-          load_step(bf, g + DEPTH);
+        for (int m = 0; m < NM; ++m) {
+          const f16x2_t s = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bf.s[f][m], 1.0f, false));
+          s_lo[f][m] = f16x2_t{s[0], s[0]};
+          s_hi[f][m] = f16x2_t{s[1], s[1]};
         }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f16x8_t a = *reinterpret_cast<const f16x8_t*>(lds + a_base[t] + g * 256);
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            const f16x8_t bv = rebuild8(bf.c[f][m][t], t < 2 ? s_lo[f][m] : s_hi[f][m]);
+            acc[f][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bv, acc[f][m], 0, 0, 0);
+          }
+      }
+    };
+    if constexpr (NS > 0) {
+#pragma unroll
+      for (int g = 0; g < NS; ++g) {
+        step(buf[g % DEPTH], g);
+        if (g + DEPTH < NS) load_step(buf[g % DEPTH], g + DEPTH);
         __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      for (int g0 = 0; g0 < nsteps; g0 += DEPTH) {
+#pragma unroll
+        for (int j = 0; j < DEPTH; ++j) {
+          const int g = g0 + j;
+          if (g < nsteps) {                                        // uniform
+            step(buf[j], g);
+            load_step(buf[j], g + DEPTH);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
 
@@ -329,9 +349,9 @@ struct Fp4Gemm {
   }
 };
 
-template <bool DUAL, int FN, int BMR, int DEPTH>
+template <bool DUAL, int FN, int BMR, int DEPTH, int NS>
 __global__ __launch_bounds__(256) void k_fp4_gemm(Fp4Problem p) {
-  using G = Fp4Gemm<DUAL, FN, BMR, DEPTH>;
+  using G = Fp4Gemm<DUAL, FN, BMR, DEPTH, NS>;
   extern __shared__ __attribute__((aligned(16))) uint8_t fp4_lds[];
   const int tile = blockIdx.y;
   if (tile >= *p.ntiles) return;
@@ -344,15 +364,28 @@ __global__ __launch_bounds__(256) void k_fp4_gemm(Fp4Problem p) {
     G::run(p, td.e, row0, td.nrows, [&](int r) { return (int64_t)(row0 + r); }, fp4_lds, blockIdx.x);
 }
 
-template <bool DUAL, int FN, int BMR>
-hipError_t launch_fp4_cfg(const Fp4Problem& p, hipStream_t s) {
-  using G = Fp4Gemm<DUAL, FN, BMR, 4>;
-  if (p.n % (16 * FN) != 0 || p.kdim % kGroup != 0) return hipErrorInvalidValue;
+template <bool DUAL, int FN, int BMR, int NS>
+hipError_t launch_fp4_ns(const Fp4Problem& p, hipStream_t s) {
+  constexpr int DEPTH = (NS > 0 && NS < 8) ? NS : 8;
+  using G = Fp4Gemm<DUAL, FN, BMR, DEPTH, NS>;
   const size_t lds = G::lds_bytes(p.kdim);
   if (lds > kFp4MaxLds) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((p.n + G::BN - 1) / G::BN), (unsigned)p.max_tiles);
-  hipLaunchKernelGGL((k_fp4_gemm<DUAL, FN, BMR, 4>), grid, dim3(256), lds, s, p);
+  hipLaunchKernelGGL((k_fp4_gemm<DUAL, FN, BMR, DEPTH, NS>), grid, dim3(256), lds, s, p);
   return hipGetLastError();
+}
+
+template <bool DUAL, int FN, int BMR>
+hipError_t launch_fp4_cfg(const Fp4Problem& p, hipStream_t s) {
+  if (p.n % (16 * FN) != 0 || p.kdim % kGroup != 0) return hipErrorInvalidValue;
+  switch (p.kdim / kGroup) {
+    case 4: return launch_fp4_ns<DUAL, FN, BMR, 4>(p, s);
+    case 8: return launch_fp4_ns<DUAL, FN, BMR, 8>(p, s);
+    case 12: return launch_fp4_ns<DUAL, FN, BMR, 12>(p, s);
+    case 16: return launch_fp4_ns<DUAL, FN, BMR, 16>(p, s);
+    case 32: return launch_fp4_ns<DUAL, FN, BMR, 32>(p, s);
+    default: return launch_fp4_ns<DUAL, FN, BMR, 0>(p, s);
+  }
 }
 
 }  // namespace
