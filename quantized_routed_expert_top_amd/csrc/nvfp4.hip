@@ -197,21 +197,26 @@ __device__ __forceinline__ f16x8_t rebuild8(uint32_t w, f16x2_t s2) {
 // tile of up to BMR sorted rows).  A workgroup's four waves each own 16 FN
 // weight rows (columns of the output) over the whole reduction; the tile's
 // activation rows are rebuilt into LDS once, as FP16 in natural order with
-// the 16-byte chunk index XOR-swizzled by row.  Per 128-wide step a lane
-// loads 16 code bytes (reduction positions 32 kb .. 32 kb + 31 of the step)
-// and the two scale bytes of those two blocks, DEPTH steps ahead; MFMA step t
-// of the four takes code word t, matched by LDS chunk 4 kb + t of the row.
-// NS > 0 is the number of 128-wide steps, known at compile time: the stream
-// is straight-line code and every wait covers exactly the step it needs;
-// NS = 0 takes the count at run time (other reduction lengths).
+// the 16-byte chunk index XOR-swizzled by row.  The reduction is walked in
+// steps of SW values (SW = 256 when its length is a known multiple of 256,
+// else 128): per step a lane loads the codes of SW / 4 consecutive values
+// (lanes kb = 0..3 of a row take consecutive quarters) and the SW / 64
+// scale bytes of those blocks, DEPTH steps ahead.  MFMA t of the step takes
+// code word t, matched by LDS chunk (SW / 32) kb + t of the row.  NS > 0 is
+// the reduction length in 128s, known at compile time: the stream is then
+// straight-line code and every wait covers exactly the step it needs; NS = 0
+// takes the length at run time.
 template <bool DUAL, int FN, int BMR, int DEPTH, int NS>
 struct Fp4Gemm {
   static constexpr int NM = DUAL ? 2 : 1;
   static constexpr int BN = 4 * 16 * FN;                          // output columns per workgroup
+  static constexpr int SW = (NS > 0 && NS % 2 == 0) ? 256 : 128;  // reduction values per step
+  static constexpr int CW = SW / 128;                             // 16-byte code loads per lane per step
+  static constexpr int NT = SW / 32;                              // MFMAs per fragment per step
 
   struct WBuf {
-    u32x4_t c[FN][NM];
-    uint32_t s[FN][NM];
+    u32x4_t c[FN][NM][CW];
+    uint32_t s[FN][NM];        // the lane's SW / 64 scale bytes (low bytes first)
   };
 
   __device__ static int swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
@@ -224,7 +229,7 @@ struct Fp4Gemm {
   __device__ static void run(const Fp4Problem& p, int e, int row0, int nrows, RowSrc src_row, uint8_t* lds, int cb) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, kb = lane >> 4;
     const int K = NS > 0 ? NS * kGroup : p.kdim;
-    const int nsteps = K / kGroup;
+    const int nsteps = K / SW;
     const int col0 = min((cb * 4 + wave) * 16 * FN, p.n - 16 * FN);  // a surplus wave recomputes the last tile, stores nothing
     const int64_t cbytes = (int64_t)p.n * (K / 2), sbytes = (int64_t)p.n * (K / kBlk);
     rsrc_t rc[NM], rb[NM];
@@ -237,8 +242,8 @@ struct Fp4Gemm {
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
       const int n = col0 + f * 16 + li;
-      c_off[f] = (uint32_t)(n * (K / 2) + kb * 16);
-      s_off[f] = (uint32_t)(n * (K / kBlk) + kb * 2);
+      c_off[f] = (uint32_t)(n * (K / 2) + kb * (SW / 8));
+      s_off[f] = (uint32_t)(n * (K / kBlk) + kb * (SW / 64));
     }
     WBuf buf[DEPTH];
     auto load_step = [&](WBuf& bf, int g) {
@@ -247,13 +252,16 @@ struct Fp4Gemm {
       for (int f = 0; f < FN; ++f)
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-          bf.c[f][m] = bload16(rc[m], in ? c_off[f] + (uint32_t)g * 64u : kOOB);
-          bf.s[f][m] = bload_u16(rb[m], in ? s_off[f] + (uint32_t)g * 8u : kOOB);
+#pragma unroll
+          for (int j = 0; j < CW; ++j)
+            bf.c[f][m][j] = bload16(rc[m], in ? c_off[f] + (uint32_t)(g * (SW / 2) + 16 * j) : kOOB);
+          const uint32_t so = in ? s_off[f] + (uint32_t)g * (SW / 16) : kOOB;
+          bf.s[f][m] = SW == 256 ? __builtin_amdgcn_raw_buffer_load_b32(rb[m], so, 0, 0) : bload_u16(rb[m], so);
         }
     };
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) {
-      if (NS == 0 || j < NS) load_step(buf[j], j);
+      if (NS == 0 || j < NS * 128 / SW) load_step(buf[j], j);
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -273,13 +281,13 @@ struct Fp4Gemm {
     __syncthreads();
     if ((cb * 4 + wave) * 16 * FN >= p.n) return;                 // wave-uniform, after the barrier
 
-    // the lane's LDS row and the offsets of its four chunks in step 0 (the
+    // the lane's LDS row and the offsets of its NT chunks in step 0 (the
     // swizzle touches only the low 3 bits of a chunk index, and a step spans
-    // 16 chunks, so step g adds g * 256 bytes)
+    // a multiple of 8 chunks, so step g adds g * SW * 2 bytes)
     const int arow = (BMR == 16) ? li : (li & (BMR - 1));         // LDS row feeding MFMA row li
-    uint32_t a_base[4];
+    uint32_t a_base[NT];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) a_base[t] = lds_chunk(arow, kb * 4 + t, K);
+    for (int t = 0; t < NT; ++t) a_base[t] = lds_chunk(arow, kb * NT + t, K);
     f32x4_t acc[FN][NM];
 #pragma unroll
     for (int f = 0; f < FN; ++f)
@@ -287,32 +295,35 @@ struct Fp4Gemm {
       for (int m = 0; m < NM; ++m) acc[f][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     auto step = [&](WBuf& bf, int g) {
-      f16x2_t s_lo[FN][NM], s_hi[FN][NM];
+      // the block scales as FP16 pairs: blocks 0, 1 (and 2, 3) of the lane's values
+      f16x2_t sc[FN][NM][SW / 128];
 #pragma unroll
       for (int f = 0; f < FN; ++f)
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-          const f16x2_t s = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bf.s[f][m], 1.0f, false));
-          s_lo[f][m] = f16x2_t{s[0], s[0]};
-          s_hi[f][m] = f16x2_t{s[1], s[1]};
+          sc[f][m][0] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bf.s[f][m], 1.0f, false));
+          if constexpr (SW == 256)
+            sc[f][m][1] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bf.s[f][m], 1.0f, true));
         }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const f16x8_t a = *reinterpret_cast<const f16x8_t*>(lds + a_base[t] + g * 256);
+      for (int t = 0; t < NT; ++t) {
+        const f16x8_t a = *reinterpret_cast<const f16x8_t*>(lds + a_base[t] + g * SW * 2);
 #pragma unroll
         for (int f = 0; f < FN; ++f)
 #pragma unroll
           for (int m = 0; m < NM; ++m) {
-            const f16x8_t bv = rebuild8(bf.c[f][m][t], t < 2 ? s_lo[f][m] : s_hi[f][m]);
+            const _Float16 s1 = sc[f][m][t / 4][(t / 2) % 2];       // block t / 2 of the lane's values
+            const f16x8_t bv = rebuild8(bf.c[f][m][t / 4][t % 4], f16x2_t{s1, s1});
             acc[f][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bv, acc[f][m], 0, 0, 0);
           }
       }
     };
     if constexpr (NS > 0) {
+      constexpr int NST = NS * 128 / SW;
 #pragma unroll
-      for (int g = 0; g < NS; ++g) {
+      for (int g = 0; g < NST; ++g) {
         step(buf[g % DEPTH], g);
-        if (g + DEPTH < NS) load_step(buf[g % DEPTH], g + DEPTH);
+        if (g + DEPTH < NST) load_step(buf[g % DEPTH], g + DEPTH);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
@@ -366,7 +377,12 @@ __global__ __launch_bounds__(256) void k_fp4_gemm(Fp4Problem p) {
 
 template <bool DUAL, int FN, int BMR, int NS>
 hipError_t launch_fp4_ns(const Fp4Problem& p, hipStream_t s) {
-  constexpr int DEPTH = (NS > 0 && NS < 8) ? NS : 8;
+  // 1024 reduction values of weights in flight per lane (8 steps of 128 or 4
+  // of 256), fewer when the reduction is shorter
+  constexpr int SW = (NS > 0 && NS % 2 == 0) ? 256 : 128;
+  constexpr int STEPS = NS > 0 ? NS * 128 / SW : 1 << 30;
+  constexpr int DMAX = 1024 / SW;
+  constexpr int DEPTH = STEPS < DMAX ? STEPS : DMAX;
   using G = Fp4Gemm<DUAL, FN, BMR, DEPTH, NS>;
   const size_t lds = G::lds_bytes(p.kdim);
   if (lds > kFp4MaxLds) return hipErrorInvalidValue;
