@@ -12,9 +12,10 @@ weight copy) and rotate over enough copies of the packed weights that the
 The headline is the 32-token W4A16 block (decode_w4a16): `value` is its
 tokens/s over exactly K timed steps.  By default the same process then times
 the 8192-token W8A8 prefill (`prefill` object: its own timed steps, the
-gate/up MFMA fraction and the whole step's INT8 MFMA fraction) and a plain
-streaming read of device memory (`hbm_read_probe`: the measured read ceiling
-next to the published 8 TB/s).
+gate/up MFMA fraction and the whole step's INT8 MFMA fraction), the same
+32-token block with NVFP4 (W4A4) experts (`nvfp4` object: timed steps, the
+gate/up kernel's HBM fraction) and a plain streaming read of device memory
+(`hbm_read_probe`: the measured read ceiling next to the published 8 TB/s).
 
 The roofline object is for the dominant kernel (the fused gate/up GEMM): its
 algorithmic bytes per launch (packed weights + scales of the touched experts)
@@ -51,9 +52,11 @@ def is_big(wl) -> bool:
 
 
 def gemm_sources(wl) -> list:
-    """Source files of the dominant kernel a workload runs: the 128-row tile
-    kernels at 64 or more slots per expert, else the per-expert kernels."""
-    return [os.path.join(CSRC, f) for f in (("gemm_big.hip" if is_big(wl) else "gemm.hip"), "gemm_common.h")]
+    """Source files of the dominant kernel a workload runs: the NVFP4 kernels,
+    the 128-row tile kernels at 64 or more slots per expert, else the
+    per-expert kernels."""
+    main = "nvfp4.hip" if wl.fmt == "nvfp4" else "gemm_big.hip" if is_big(wl) else "gemm.hip"
+    return [os.path.join(CSRC, f) for f in (main, "gemm_common.h")]
 
 
 def source_digest(wl) -> str:
@@ -199,12 +202,17 @@ def time_workload(wl, steps, warmup, eager, copies_arg, dev, hip):
     R = copies_arg or max(1, math.ceil((1 << 30) / max(alg["gate_up_weights"] + alg["down_weights"], 1)))
     copies = [W0] + [W0.clone() for _ in range(R - 1)]
     x, ids_t, w_t = P["x"], P["topk_ids"], P["topk_w"]
-    ws = torch.empty(qre.workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.K, wl.weight_bits, wl.act_int8),
-                     dtype=torch.uint8, device=dev)
+    fp4 = wl.fmt == "nvfp4"
+    nb = (qre.nvfp4_workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.K) if fp4 else
+          qre.workspace_bytes(wl.T, wl.H, wl.I, wl.E, wl.K, wl.weight_bits, wl.act_int8))
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
 
     def step(i):
-        qre.moe_forward(x, ids_t, w_t, copies[i % R], act_int8=wl.act_int8, out=out, workspace=ws)
+        if fp4:
+            qre.nvfp4_moe_forward(x, ids_t, w_t, copies[i % R], out=out, workspace=ws)
+        else:
+            qre.moe_forward(x, ids_t, w_t, copies[i % R], act_int8=wl.act_int8, out=out, workspace=ws)
 
     stream = torch.cuda.Stream()
     graphs = []
@@ -263,13 +271,17 @@ def time_workload(wl, steps, warmup, eager, copies_arg, dev, hip):
         nk = max(20, min(steps, 200))
         evs = [[hip.create() for _ in range(6)] for _ in range(nk)]
         for i in range(nk):
-            qre.moe_forward_timed(x, ids_t, w_t, copies[i % R], evs[i], act_int8=wl.act_int8, out=out, workspace=ws)
+            if fp4:
+                qre.nvfp4_moe_forward_timed(x, ids_t, w_t, copies[i % R], evs[i], out=out, workspace=ws)
+            else:
+                qre.moe_forward_timed(x, ids_t, w_t, copies[i % R], evs[i], act_int8=wl.act_int8, out=out,
+                                      workspace=ws)
         torch.cuda.synchronize()
         if not torch.equal(out, eager_out):
             raise RuntimeError("timed forward differs from qre_moe_forward")
     dur = np.array([[hip.elapsed_ms(e[j], e[j + 1]) for j in range(5)] for e in evs[2:]]).mean(axis=0) * 1e3
     dur = np.maximum(dur - pair_us, 0.0)
-    plan = qre.forward_plan(wl.T, wl.H, wl.I, wl.E, wl.K, wl.weight_bits, wl.act_int8)
+    plan = 0 if fp4 else qre.forward_plan(wl.T, wl.H, wl.I, wl.E, wl.K, wl.weight_bits, wl.act_int8)
     return {
         "wl": wl, "P": P, "alg": alg, "R": R, "steps": steps, "wall": wall, "gpu_ms": gpu_ms, "plan": plan,
         "median_loop_ms": float(np.median(loop_ms)), "loops_ms": [round(v, 5) for v in loop_ms],
@@ -422,6 +434,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill_w8a8 object of the default run")
     ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read probe")
+    ap.add_argument("--no-nvfp4", action="store_true", help="skip the decode_nvfp4 object of the default run")
     ap.add_argument("--stage", choices=["ffn", "router"], default="ffn",
                     help="ffn: the whole feed-forward (default); router: the top-K + softmax router alone")
     ap.add_argument("--copy-probe", action="store_true",
@@ -449,6 +462,9 @@ def main():
     if not args.no_prefill and wl.name != "prefill_w8a8":
         pw = WORKLOADS["prefill_w8a8"]
         pre = time_workload(pw, min(args.steps, 100), min(args.warmup, 10), args.eager, 0, dev, hip)
+    f4 = None
+    if not args.no_nvfp4 and wl.name != "decode_nvfp4":
+        f4 = time_workload(WORKLOADS["decode_nvfp4"], args.steps, args.warmup, args.eager, 0, dev, hip)
     hip.destroy_all()
 
     ms_per_step = res["wall"] * 1e3 / args.steps
@@ -490,6 +506,17 @@ def main():
             "gate_up_us": pr["avg_us"], "gate_up_mfma_frac": pr["frac"], "gate_up_tops": pr["achieved"],
             "step_i8_mfma_frac": ps["mfma_frac_whole_step"], "step": ps, "kernels_us": pre["kernels_us"],
             "gate_up_traffic": pr["traffic"],
+        }
+    if f4 is not None:
+        fw = f4["wl"]
+        fr = roofline(f4, probe["gbs"] if probe else None)
+        result["nvfp4"] = {
+            "workload": fw.name, "T": fw.T, "H": fw.H, "I": fw.I, "E": fw.E, "K": fw.K,
+            "format": "E2M1 weights and inputs, E4M3 scale per 16, FP32 outer scale per matrix / input row",
+            "dtype": "f16 MFMA on exactly rebuilt FP4 operands, FP32 accumulation", "weight_copies": f4["R"],
+            "steps": f4["steps"], "ms_per_step": round(f4["wall"] * 1e3 / f4["steps"], 5),
+            "tokens_per_s": round(fw.T * f4["steps"] / f4["wall"], 1), "touched_experts": f4["alg"]["touched"],
+            "roofline": fr, "step": step_summary(f4), "kernels_us": f4["kernels_us"],
         }
     if args.copy_probe:
         n = 256 << 20

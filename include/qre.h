@@ -349,6 +349,14 @@ int qre_nvfp4_moe_forward(const qre_desc* desc, const void* x, const int32_t* to
                           const qre_nvfp4_weights* weights, void* out, void* workspace, size_t workspace_bytes,
                           qre_stream_t stream);
 
+/* Measurement aid: qre_nvfp4_moe_forward that also records six caller-created
+ * hipEvent_t (events[0..5], host array; NULL entries skipped) on `stream`:
+ * before the routing, after the routing and the quantization of x, after
+ * gate/up, after the quantization of h, after down, after the combine. */
+int qre_nvfp4_moe_forward_timed(const qre_desc* desc, const void* x, const int32_t* topk_ids, const float* topk_w,
+                                const qre_nvfp4_weights* weights, void* out, void* workspace, size_t workspace_bytes,
+                                void* const* events, qre_stream_t stream);
+
 /* Device pointers into an NVFP4 forward workspace (host out): the
  * permutation of the last qre_nvfp4_moe_forward that used it. */
 int qre_nvfp4_workspace_permutation(const qre_desc* desc, void* workspace, int32_t** counts, int32_t** offsets,

@@ -79,6 +79,7 @@ def _lib():
         L.qre_nvfp4_workspace_bytes.argtypes = [P, P]
         L.qre_nvfp4_stage_workspace_bytes.argtypes = [P, P]
         L.qre_nvfp4_moe_forward.argtypes = [P, P, P, P, P, P, P, sz, P]
+        L.qre_nvfp4_moe_forward_timed.argtypes = [P, P, P, P, P, P, P, sz, P, P]
         L.qre_nvfp4_workspace_permutation.argtypes = [P, P, P, P, P, P]
         L.qre_nvfp4_gate_up.argtypes = [P, P, P, P, P, P, P, P, P, sz, P]
         L.qre_nvfp4_down.argtypes = [P, P, P, P, P, P, P, P, sz, P]
@@ -607,6 +608,28 @@ def nvfp4_moe_forward(x, topk_ids, topk_w, W: Nvfp4Experts, out=None, workspace=
     _check("qre_nvfp4_moe_forward", _lib().qre_nvfp4_moe_forward(
         C.byref(d), _ptr(x), _ptr(topk_ids), _ptr(topk_w), C.byref(ws_struct), _ptr(out), _ptr(workspace),
         workspace.numel(), _stream()))
+    return out
+
+
+def nvfp4_moe_forward_timed(x, topk_ids, topk_w, W: Nvfp4Experts, events, out=None, workspace=None):
+    """nvfp4_moe_forward that records six caller-created hipEvent_t handles
+    (ints, or None) between its steps; see qre_nvfp4_moe_forward_timed."""
+    T, H = x.shape
+    K = topk_ids.shape[1]
+    _need(x, "x", torch.bfloat16, (T, H))
+    _need(topk_ids, "topk_ids", torch.int32, (T, K))
+    _need(topk_w, "topk_w", torch.float32, (T, K))
+    if len(events) != 6:
+        raise ValueError("six events")
+    if workspace is None:
+        workspace = _workspace(nvfp4_workspace_bytes(T, H, W.I, W.E, K), x.device)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    ev = (C.c_void_p * 6)(*[e if e else None for e in events])
+    ws_struct = W._struct()
+    _check("qre_nvfp4_moe_forward_timed", _lib().qre_nvfp4_moe_forward_timed(
+        C.byref(_fp4_desc(T, H, W.I, W.E, K)), _ptr(x), _ptr(topk_ids), _ptr(topk_w), C.byref(ws_struct), _ptr(out),
+        _ptr(workspace), workspace.numel(), ev, _stream()))
     return out
 
 

@@ -672,9 +672,9 @@ int qre_nvfp4_stage_workspace_bytes(const qre_desc* desc, size_t* bytes) {
   return QRE_OK;
 }
 
-int qre_nvfp4_moe_forward(const qre_desc* desc, const void* x, const int32_t* topk_ids, const float* topk_w,
-                          const qre_nvfp4_weights* weights, void* out, void* workspace, size_t workspace_bytes,
-                          qre_stream_t stream) {
+static int nvfp4_forward_impl(const qre_desc* desc, const void* x, const int32_t* topk_ids, const float* topk_w,
+                              const qre_nvfp4_weights* weights, void* out, void* workspace, size_t workspace_bytes,
+                              hipEvent_t const* ev, hipStream_t s) {
   int rc = check_nvfp4_desc(desc);
   if (rc) return rc;
   const qre_desc& d = *desc;
@@ -688,16 +688,38 @@ int qre_nvfp4_moe_forward(const qre_desc* desc, const void* x, const int32_t* to
   if (workspace_bytes < L.bytes) return QRE_ERR_WORKSPACE;
   const int64_t S = (int64_t)d.T * d.K;
   const Fp4Stage& st = L.st;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = launch_route(topk_ids, d.T, d.K, d.E, L.counts, L.offsets, L.sorted_slot, L.slot_row, st.header,
-                              st.route_scratch, st.tiles_gu, st.ntiles, st.bm, st.tiles_dn, st.ntiles + 1, st.bm, s);
+  auto mark = [&](int i) -> hipError_t { return (ev && ev[i]) ? hipEventRecord(ev[i], s) : hipSuccess; };
+  hipError_t e = mark(0);
+  if (e == hipSuccess)
+    e = launch_route(topk_ids, d.T, d.K, d.E, L.counts, L.offsets, L.sorted_slot, L.slot_row, st.header,
+                     st.route_scratch, st.tiles_gu, st.ntiles, st.bm, st.tiles_dn, st.ntiles + 1, st.bm, s);
   if (e == hipSuccess) e = launch_fp4_quantize_act(static_cast<const uint16_t*>(x), d.T, d.H, L.xq, L.xb, L.xr, s);
+  if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess)
     e = launch_fp4_gemm(fp4_gate_up_problem(d, L.xq, L.xb, L.xr, L.sorted_slot, *weights, st, L.h), s);
+  if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = launch_fp4_quantize_act(L.h, S, d.I, L.hq, L.hb, L.hr, s);
+  if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = launch_fp4_gemm(fp4_down_problem(d, L.hq, L.hb, L.hr, *weights, st, L.y), s);
+  if (e == hipSuccess) e = mark(4);
   if (e == hipSuccess) e = launch_combine(L.y, L.slot_row, topk_w, d.T, d.K, d.H, static_cast<uint16_t*>(out), s);
+  if (e == hipSuccess) e = mark(5);
   return hip_status(e);
+}
+
+int qre_nvfp4_moe_forward(const qre_desc* desc, const void* x, const int32_t* topk_ids, const float* topk_w,
+                          const qre_nvfp4_weights* weights, void* out, void* workspace, size_t workspace_bytes,
+                          qre_stream_t stream) {
+  return nvfp4_forward_impl(desc, x, topk_ids, topk_w, weights, out, workspace, workspace_bytes, nullptr,
+                            reinterpret_cast<hipStream_t>(stream));
+}
+
+int qre_nvfp4_moe_forward_timed(const qre_desc* desc, const void* x, const int32_t* topk_ids, const float* topk_w,
+                                const qre_nvfp4_weights* weights, void* out, void* workspace, size_t workspace_bytes,
+                                void* const* events, qre_stream_t stream) {
+  if (!events) return QRE_ERR_NULL;
+  return nvfp4_forward_impl(desc, x, topk_ids, topk_w, weights, out, workspace, workspace_bytes,
+                            reinterpret_cast<hipEvent_t const*>(events), reinterpret_cast<hipStream_t>(stream));
 }
 
 int qre_nvfp4_workspace_permutation(const qre_desc* desc, void* workspace, int32_t** counts, int32_t** offsets,

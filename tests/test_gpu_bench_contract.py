@@ -49,6 +49,11 @@ def test_default_workload_line():
     assert 0 < pf["step_i8_mfma_frac"] < 1 and pf["steps"] == 20
     pr = j["hbm_read_probe"]
     assert 0 < pr["frac_of_peak"] < 1 and 0 < j["roofline"]["frac_of_measured_read"] < 1.2
+    # the NVFP4 (W4A4) decode block
+    f4 = j["nvfp4"]
+    assert f4["workload"] == "decode_nvfp4" and f4["tokens_per_s"] > 0 and f4["steps"] == 20
+    assert f4["roofline"]["bound"] == "hbm" and 0 < f4["roofline"]["frac"] < 1
+    assert set(f4["kernels_us"]) == {"route_and_quantize_x", "gate_up", "quantize_h", "down", "combine"}
 
 
 def test_router_stage_line_with_cpu_baseline():
