@@ -1,12 +1,14 @@
 """Text summaries of rocprofv3 output (the SQLite database it writes).
 
     python -m harness.rocprof_summary kernels DIR [--top N]
-    python -m harness.rocprof_summary counters DIR [--kernel SUBSTR]
+    python -m harness.rocprof_summary counters DIR [--kernel SUBSTR] [--dispatches]
 
 `kernels` prints, per kernel name, the number of dispatches and the average,
 minimum, maximum and total duration (from a --kernel-trace run); `counters`
 prints, per kernel and counter, the mean value per dispatch (from a --pmc
-run).  DIR is the directory given to rocprofv3 with -d; every *.db below it is
+run), and with --dispatches every dispatch's value in dispatch order (to tell
+apart launches of one kernel with different sizes, such as the copies of a
+calibration run).  DIR is the directory given to rocprofv3 with -d; every *.db below it is
 read.
 """
 from __future__ import annotations
@@ -55,17 +57,33 @@ def counter_means(d: str, kernel_substr: str = "") -> dict[str, dict[str, tuple[
     return out
 
 
+def counter_dispatches(d: str, kernel_substr: str = "") -> list[tuple[str, str, int, float]]:
+    """(kernel, counter, dispatch id, value summed over instances), in dispatch order."""
+    rows = []
+    for path in _dbs(d):
+        con = sqlite3.connect(path)
+        q = ("select kernel_name, counter_name, dispatch_id, sum(value) from counters_collection "
+             "where kernel_name like ? group by kernel_name, counter_name, dispatch_id order by dispatch_id")
+        rows += [(k, c, int(i), float(v)) for k, c, i, v in con.execute(q, (f"%{kernel_substr}%",))]
+        con.close()
+    return rows
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("what", choices=["kernels", "counters"])
     ap.add_argument("dir")
     ap.add_argument("--top", type=int, default=12)
     ap.add_argument("--kernel", default="")
+    ap.add_argument("--dispatches", action="store_true")
     a = ap.parse_args(argv)
     if a.what == "kernels":
         print(f"{'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'total_us':>11}  kernel")
         for n, c, avg, mn, mx, tot in kernel_stats(a.dir)[: a.top]:
             print(f"{c:6d} {avg:9.2f} {mn:9.2f} {mx:9.2f} {tot:11.1f}  {n}")
+    elif a.dispatches:
+        for k, c, i, v in counter_dispatches(a.dir, a.kernel):
+            print(f"{i:8d} {c:16s} {v:16.1f}  {k}")
     else:
         for k, cs in counter_means(a.dir, a.kernel).items():
             print(k)
