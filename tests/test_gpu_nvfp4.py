@@ -192,3 +192,52 @@ def test_argument_errors():
         qre.nvfp4_workspace_bytes(wl.T, 100, wl.I, wl.E, wl.K)                # H not a multiple of 128
     with pytest.raises(qre.QreError):
         qre.nvfp4_workspace_bytes(64, 8192, 512, 8, 8)                          # x rows do not fit LDS
+
+
+# ---- the forward against its own stages -----------------------------------------------
+
+def stage_sequence(wl, x, ids, w, Wg):
+    """The forward as separate launches: routing, quantization of x, gate/up,
+    quantization of h, down, combine."""
+    xt = x_tensor(x, DEV)
+    counts, offsets, sorted_slot, slot_row, _ = qre.route(i32(ids), wl.E)
+    xq, xs, xr = qre.nvfp4_quantize_act(xt)
+    h = qre.nvfp4_gate_up(xq, xs, xr, sorted_slot, offsets, Wg, wl.K)
+    hq, hs, hr = qre.nvfp4_quantize_act(h)
+    y = qre.nvfp4_down(hq, hs, hr, offsets, Wg, wl.T, wl.K)
+    return bf16_np(qre.combine(y, slot_row, f32(w)))
+
+
+@pytest.mark.parametrize("name", ["decode_nvfp4", "f4_st_c"])
+def test_forward_is_bit_identical_to_its_stages(name):
+    wl = WORKLOADS[name] if name in WORKLOADS else next(w for w in STAGE if w.name == name)
+    x = gen_x(wl)
+    ids, w = gen_routing(wl)
+    Wg = gpu_experts(wl, DEV)
+    out = run_forward(wl, x, ids, w, Wg)
+    np.testing.assert_array_equal(out, stage_sequence(wl, x, ids, w, Wg))
+
+
+def test_forward_edges_8_row_tiles():
+    """Decode-sized shapes with 8-row tiles and a 256-value step (reductions
+    of 512): out-of-range and duplicate ids, one token, an expert with more
+    rows than one tile; the forward equals its stages bit for bit."""
+    base = Workload("f4_edge_fold", T=6, H=512, I=512, E=4, K=2, weight_bits=4, act_int8=False, fmt="nvfp4",
+                    seed=27)
+    x = gen_x(base)
+    ids = np.array([[0, 1], [1, 7], [-1, 2], [3, 3], [2, 0], [1, 1]], np.int32)
+    w = np.full((6, 2), 0.5, np.float32)
+    Wo = oracle.fp4_workload_experts(base, range(4))
+    Wg = to_gpu(Wo)
+    check_forward(base, x=x, ids=ids, w=w, Wo=Wo, Wg=Wg)
+    np.testing.assert_array_equal(run_forward(base, x, ids, w, Wg), stage_sequence(base, x, ids, w, Wg))
+    check_forward(base.with_(T=1, name="f4_one_fold"), x=x[:1], ids=ids[:1], w=w[:1], Wo=Wo, Wg=Wg)
+    # 32 slots over 16 experts (8-row tiles), expert 0 seeing 16 rows: two tiles
+    many = base.with_(T=16, E=16, name="f4_many_rows", seed=28)
+    xm = gen_x(many)
+    idm = np.stack([np.zeros(16, np.int32), np.arange(16, dtype=np.int32) % 3 + 1], axis=1)
+    wm = np.full((16, 2), 0.5, np.float32)
+    Wm = oracle.fp4_workload_experts(many, range(4))
+    Wmg = to_gpu(Wm)
+    check_forward(many, x=xm, ids=idm, w=wm, Wo=Wm, Wg=Wmg)
+    np.testing.assert_array_equal(run_forward(many, xm, idm, wm, Wmg), stage_sequence(many, xm, idm, wm, Wmg))
