@@ -5,9 +5,11 @@
 
 A step is one whole qre_moe_forward (permutation, gate/up+SiLU GEMM, down GEMM,
 combine; plus the INT8 quantizers in INT8-activation mode) over one synthetic
-batch already resident in HBM.  Steps are replayed from HIP graphs (one per
-weight copy) and rotate over enough copies of the packed weights that the
-256 MB last-level cache cannot serve them.  Prints one JSON line.
+batch already resident in HBM.  Steps rotate over R copies of the packed
+weights, enough that the 256 MB last-level cache cannot serve them, and are
+replayed from one HIP graph holding R consecutive forwards (as a decode graph
+holds the feed-forward of many layers); `step.one_graph_per_forward_ms` gives
+the same loop with one graph launch per forward.  Prints one JSON line.
 
 The headline is the 32-token W4A16 block (decode_w4a16): `value` is its
 tokens/s over exactly K timed steps.  By default the same process then times
@@ -40,6 +42,8 @@ I8_PEAK_TOPS = 5000.0
 METRIC = "routed-expert FFN tokens/s; % HBM peak (32-tok block) & % MFMA peak (prefill)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_{}.txt")
 CSRC = os.path.join(ROOT, "quantized_routed_expert_top_amd", "csrc")
+LAUNCH = ("hipGraph of {R} consecutive forwards over the {R} weight copies, replayed "
+          "(one-forward graphs for a remainder)")
 STAGES = ("route_and_quantize_x", "gate_up", "quantize_h", "down", "combine")
 
 
@@ -221,31 +225,52 @@ def time_workload(wl, steps, warmup, eager, copies_arg, dev, hip):
             step(i)
         torch.cuda.synchronize()
         eager_out = out.clone()
+        chain = None
         if not eager:
             for r in range(R):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=stream):
                     step(r)
                 graphs.append(g)
+            # R consecutive forwards over the R weight sets in one graph, as a
+            # decode graph holds the feed-forward of many layers
+            chain = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(chain, stream=stream):
+                for r in range(R):
+                    step(r)
             for i in range(max(2 * R, min(warmup, 4 * R))):
                 graphs[i % R].replay()
             torch.cuda.synchronize()
             if not torch.equal(out, eager_out):
                 raise RuntimeError("graph replay differs from eager output")
+            chain.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(out, eager_out):
+                raise RuntimeError("chained graph replay differs from eager output")
 
-        def run(i):
+        def run_steps(n, single=False):
+            """n whole forwards, in order over the weight sets: eager launches,
+            else the chained graph for each full round of R forwards and the
+            one-forward graphs for the rest (or one-forward graphs only)."""
+            i = 0
             if eager:
-                step(i)
-            else:
+                for i in range(n):
+                    step(i)
+                return
+            if not single:
+                while i + R <= n:
+                    chain.replay()
+                    i += R
+            while i < n:
                 graphs[i % R].replay()
+                i += 1
 
         # ---- timed region: K whole steps ----
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         ev0.record(stream)
-        for i in range(steps):
-            run(i)
+        run_steps(steps)
         ev1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -259,11 +284,21 @@ def time_workload(wl, steps, warmup, eager, copies_arg, dev, hip):
         for _ in range(5):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            for i in range(nl):
-                run(i)
+            run_steps(nl)
             b.record(stream)
             torch.cuda.synchronize()
             loop_ms.append(a.elapsed_time(b) / nl)
+        # the same loops with one graph launch per forward (the graph-to-graph
+        # gap paid on every step)
+        single_ms = []
+        if not eager:
+            for _ in range(3):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                run_steps(nl, single=True)
+                b.record(stream)
+                torch.cuda.synchronize()
+                single_ms.append(a.elapsed_time(b) / nl)
 
         # ---- per-kernel durations: the same kernels, with HIP events between steps ----
         sh = stream.cuda_stream
@@ -285,6 +320,7 @@ def time_workload(wl, steps, warmup, eager, copies_arg, dev, hip):
     return {
         "wl": wl, "P": P, "alg": alg, "R": R, "steps": steps, "wall": wall, "gpu_ms": gpu_ms, "plan": plan,
         "median_loop_ms": float(np.median(loop_ms)), "loops_ms": [round(v, 5) for v in loop_ms],
+        "one_graph_per_forward_ms": round(float(np.median(single_ms)), 5) if single_ms else None,
         "kernels_us": {k: round(float(v), 2) for k, v in zip(STAGES, dur)}, "event_pair_us": round(pair_us, 2),
     }
 
@@ -346,6 +382,7 @@ def step_summary(res):
     peak = I8_PEAK_TOPS if wl.act_int8 else BF16_PEAK_TFLOPS
     return {"gpu_ms_per_step": round(res["gpu_ms"] / res["steps"], 5),
             "median_of_5_loops_ms": round(res["median_loop_ms"], 5),
+            "one_graph_per_forward_ms": res["one_graph_per_forward_ms"],
             "alg_bytes": int(alg["total"]),
             "hbm_frac_whole_step": round(alg["total"] / s / 1e9 / HBM_PEAK_GBS, 4),
             "mfma_frac_whole_step": round(alg["flops"] / s / 1e12 / peak, 5)}
@@ -483,7 +520,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "K": wl.K,
                    "weight_bits": wl.weight_bits, "act_int8": wl.act_int8, "weight_copies": res["R"],
-                   "launch": "eager" if args.eager else "hipGraph replay", "touched_experts": res["alg"]["touched"]},
+                   "launch": "eager" if args.eager else LAUNCH.format(R=res["R"]),
+                   "touched_experts": res["alg"]["touched"]},
         "roofline": roofline(res, probe["gbs"] if probe else None),
         "step": step_summary(res),
         "kernels_us": res["kernels_us"],

@@ -41,6 +41,10 @@ def test_default_workload_line():
     _check_common(j, 20, 3)
     assert j["config"]["workload"] == "decode_w4a16" and j["dtype"] == "bf16"
     assert j["roofline"]["bound"] == "hbm" and j["roofline"]["unit"] == "GB/s"
+    # steps replay a graph of R consecutive forwards; the one-forward-per-graph
+    # loop is reported beside it
+    assert j["step"]["one_graph_per_forward_ms"] > 0
+    assert str(j["config"]["weight_copies"]) in j["config"]["launch"]
     # tokens/s and ms/step describe the same timed region
     assert abs(j["value"] * j["ms_per_step"] / 1e3 - j["config"]["T"]) / j["config"]["T"] < 1e-3
     # the prefill half of the metric and the measured read ceiling ride on the same line
