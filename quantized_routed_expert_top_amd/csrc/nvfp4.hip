@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "gemm_common.h"
+#include "route_small.h"
 
 namespace qre {
 namespace {
@@ -94,12 +95,13 @@ __device__ __forceinline__ void quantize_block(const float (&v)[kBlk], float S, 
 
 // Activations: one wave per row (grid-stride over rows).  Pass 1: the row's
 // max; pass 2: each lane quantizes whole blocks (16 BF16 values, 32 bytes).
-__global__ __launch_bounds__(256) void k_fp4_quantize_act(const uint16_t* __restrict__ v, int64_t rows, int cols,
-                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ b,
-                                                          float* __restrict__ rs) {
+// Rows r = 4 blk0 + wave, stepping by 4 nblk (blk0 < nblk: this workgroup's
+// index among the nblk that quantize).
+__device__ void fp4_quantize_rows(const uint16_t* __restrict__ v, int64_t rows, int cols, uint8_t* __restrict__ q,
+                                  uint8_t* __restrict__ b, float* __restrict__ rs, int blk0, int nblk) {
   const int lane = threadIdx.x & 63;
   const int nb = cols / kBlk;
-  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows; r += (int64_t)gridDim.x * 4) {
+  for (int64_t r = (int64_t)blk0 * 4 + (threadIdx.x >> 6); r < rows; r += (int64_t)nblk * 4) {
     const uint16_t* vr = v + r * cols;
     float amax = 0.f;
     for (int k = lane * 8; k < cols; k += 64 * 8) {
@@ -130,6 +132,27 @@ __global__ __launch_bounds__(256) void k_fp4_quantize_act(const uint16_t* __rest
       b[r * nb + blk] = (uint8_t)sb;
     }
   }
+}
+
+__global__ __launch_bounds__(256) void k_fp4_quantize_act(const uint16_t* __restrict__ v, int64_t rows, int cols,
+                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ b,
+                                                          float* __restrict__ rs) {
+  fp4_quantize_rows(v, rows, cols, q, b, rs, blockIdx.x, gridDim.x);
+}
+
+// Decode blocks: the routing (workgroup 0, four waves) and the quantization
+// of x (the other workgroups, one row per wave) in one launch, since neither
+// reads what the other writes.
+__global__ __launch_bounds__(256) void k_fp4_route_quantize_x(RouteArgs ra, const uint16_t* __restrict__ v,
+                                                              int64_t rows, int cols, uint8_t* __restrict__ q,
+                                                              uint8_t* __restrict__ b, float* __restrict__ rs) {
+  extern __shared__ int route_lds[];
+  if (blockIdx.x == 0) {
+    route_small<4>(route_lds, ra.ids, ra.S, ra.E, ra.nbits, ra.counts, ra.offsets, ra.sorted_slot, ra.slot_row,
+                   ra.dropped, ra.tiles_a, ra.ntiles_a, ra.bm_a, ra.tiles_b, ra.ntiles_b, ra.bm_b);
+    return;
+  }
+  fp4_quantize_rows(v, rows, cols, q, b, rs, blockIdx.x - 1, gridDim.x - 1);
 }
 
 // Weights, pass 1: the largest magnitude of each matrix, as FP32 bits (the
@@ -424,6 +447,17 @@ hipError_t launch_fp4_quantize_act(const uint16_t* v, int64_t rows, int cols, ui
   const int64_t wgs = (rows + 3) / 4;
   const unsigned grid = (unsigned)(wgs < kMaxQuantBlocks ? wgs : kMaxQuantBlocks);
   hipLaunchKernelGGL(k_fp4_quantize_act, dim3(grid), dim3(256), 0, s, v, rows, cols, q, b, rs);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp4_route_quantize_x(RouteArgs ra, const uint16_t* v, int64_t rows, int cols, uint8_t* q,
+                                       uint8_t* b, float* rs, hipStream_t s) {
+  if ((int64_t)ra.S > kRouteQuantMaxSlots || rows == 0) return hipErrorInvalidValue;
+  ra.nbits = bits_for(ra.E);
+  const int64_t wgs = (rows + 3) / 4;
+  const unsigned grid = 1 + (unsigned)(wgs < kMaxQuantBlocks ? wgs : kMaxQuantBlocks);
+  hipLaunchKernelGGL(k_fp4_route_quantize_x, dim3(grid), dim3(256), sizeof(int) * route_small_lds_ints(4, ra.E), s,
+                     ra, v, rows, cols, q, b, rs);
   return hipGetLastError();
 }
 

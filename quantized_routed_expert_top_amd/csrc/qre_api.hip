@@ -690,10 +690,17 @@ static int nvfp4_forward_impl(const qre_desc* desc, const void* x, const int32_t
   const Fp4Stage& st = L.st;
   auto mark = [&](int i) -> hipError_t { return (ev && ev[i]) ? hipEventRecord(ev[i], s) : hipSuccess; };
   hipError_t e = mark(0);
-  if (e == hipSuccess)
-    e = launch_route(topk_ids, d.T, d.K, d.E, L.counts, L.offsets, L.sorted_slot, L.slot_row, st.header,
-                     st.route_scratch, st.tiles_gu, st.ntiles, st.bm, st.tiles_dn, st.ntiles + 1, st.bm, s);
-  if (e == hipSuccess) e = launch_fp4_quantize_act(static_cast<const uint16_t*>(x), d.T, d.H, L.xq, L.xb, L.xr, s);
+  if (S <= kRouteQuantMaxSlots) {   // decode blocks: routing and the quantization of x in one launch
+    const RouteArgs ra = {topk_ids, (int)S, d.E, 0, L.counts, L.offsets, L.sorted_slot, L.slot_row, st.header,
+                          st.tiles_gu, st.ntiles, st.bm, st.tiles_dn, st.ntiles + 1, st.bm};
+    if (e == hipSuccess)
+      e = launch_fp4_route_quantize_x(ra, static_cast<const uint16_t*>(x), d.T, d.H, L.xq, L.xb, L.xr, s);
+  } else {
+    if (e == hipSuccess)
+      e = launch_route(topk_ids, d.T, d.K, d.E, L.counts, L.offsets, L.sorted_slot, L.slot_row, st.header,
+                       st.route_scratch, st.tiles_gu, st.ntiles, st.bm, st.tiles_dn, st.ntiles + 1, st.bm, s);
+    if (e == hipSuccess) e = launch_fp4_quantize_act(static_cast<const uint16_t*>(x), d.T, d.H, L.xq, L.xb, L.xr, s);
+  }
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess)
     e = launch_fp4_gemm(fp4_gate_up_problem(d, L.xq, L.xb, L.xr, L.sorted_slot, *weights, st, L.h), s);

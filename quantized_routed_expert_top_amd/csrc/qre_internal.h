@@ -80,6 +80,18 @@ hipError_t launch_route(const int32_t* ids, int T, int K, int E, int32_t* counts
 // Tile list from offsets alone (used by the stage entry points); tiles_b may be null.
 hipError_t launch_build_tiles(const int32_t* offsets, int E, Tile* tiles_a, int32_t* ntiles_a, int bm_a,
                               Tile* tiles_b, int32_t* ntiles_b, int bm_b, hipStream_t stream);
+// Arguments of the one-workgroup routing when another kernel runs it.
+struct RouteArgs {
+  const int32_t* ids;
+  int S, E, nbits;
+  int32_t *counts, *offsets, *sorted_slot, *slot_row, *dropped;
+  Tile* tiles_a;
+  int32_t* ntiles_a;
+  int bm_a;
+  Tile* tiles_b;
+  int32_t* ntiles_b;
+  int bm_b;
+};
 // Upper bound on the number of row tiles of height bm over S sorted rows and E experts.
 int64_t max_tiles(int64_t S, int E, int bm);
 
@@ -153,6 +165,12 @@ hipError_t launch_fp4_quantize_act(const uint16_t* v, int64_t rows, int cols, ui
                                    hipStream_t stream);
 hipError_t launch_fp4_quantize_weights(const float* w, int64_t mats, int64_t rows, int64_t cols, uint8_t* q,
                                        uint8_t* b, float* outer, hipStream_t stream);
+// The routing (one workgroup of four waves; ra.nbits is filled in) and the
+// NVFP4 quantization of x [rows][cols] in one launch, for ra.S <=
+// kRouteQuantMaxSlots.
+constexpr int64_t kRouteQuantMaxSlots = 512;
+hipError_t launch_fp4_route_quantize_x(RouteArgs ra, const uint16_t* v, int64_t rows, int cols, uint8_t* q,
+                                       uint8_t* b, float* rs, hipStream_t stream);
 
 // Combine.
 hipError_t launch_combine(const uint16_t* y, const int32_t* slot_row, const float* topk_w, int T, int K,

@@ -18,35 +18,12 @@
 //    ascending slot order.
 // Small problems (S <= kSmallMax) do all of it in one workgroup with the
 // tables in LDS; larger ones use three kernels with the per-wave table in HBM.
-#include "qre_internal.h"
+#include "route_small.h"
 
 namespace qre {
 namespace {
 
-constexpr int kSmallMax = 8192;   // slots handled by the one-workgroup kernel
 constexpr int kLargeChunk = 256;  // slots per wave in the three-kernel path
-constexpr int kBatch = 4;         // 64-slot rows whose id loads are issued together
-
-__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
-
-
-// Mask of the lanes whose key equals this lane's key (keys < 2^nbits).
-// Must be called by all 64 lanes.
-__device__ __forceinline__ uint64_t match_any(uint32_t key, int nbits) {
-  uint64_t m = ~0ull;
-  for (int b = 0; b < nbits; ++b) {
-    const bool bit = (key >> b) & 1u;
-    const uint64_t bal = __ballot(bit);
-    m &= bit ? bal : ~bal;
-  }
-  return m;
-}
-
-__device__ __forceinline__ uint32_t slot_key(const int32_t* ids, int64_t s, int64_t c1, int E) {
-  if (s >= c1) return (uint32_t)E;
-  const int32_t id = ids[s];
-  return (id >= 0 && id < E) ? (uint32_t)id : (uint32_t)E;
-}
 
 // Count this wave's chunk [c0, c1) into hist_row[E] (LDS, zeroed by the caller).
 // The ids of kBatch rows of 64 slots are loaded before the first is counted.
@@ -94,112 +71,6 @@ __device__ void wave_scatter(const int32_t* ids, int64_t c0, int64_t c1, int E, 
   }
 }
 
-// The one-workgroup kernel keeps its wave's chunk (at most kSmallRows rows of
-// 64 slots) in registers between the count and the scatter: the keys and, per
-// row, each lane's mask of equal keys.  Same order of work as wave_count and
-// wave_scatter, so the same result.
-constexpr int kSmallRows = kSmallMax / 16 / kWave;   // 16 waves cover kSmallMax slots
-struct SmallChunk {
-  uint32_t key[kSmallRows];
-  uint64_t m[kSmallRows];
-};
-
-__device__ void small_load(const int32_t* ids, int64_t c0, int64_t c1, int E, int nbits, SmallChunk& ch) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int r = 0; r < kSmallRows; ++r) ch.key[r] = slot_key(ids, c0 + r * kWave + lane, c1, E);
-#pragma unroll
-  for (int r = 0; r < kSmallRows; ++r) ch.m[r] = (c0 + r * kWave < c1) ? match_any(ch.key[r], nbits) : 0ull;   // uniform
-}
-
-__device__ void small_count(const SmallChunk& ch, int64_t c0, int64_t c1, int E, int* hist_row) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int r = 0; r < kSmallRows; ++r)
-    if (c0 + r * kWave < c1 && ch.key[r] < (uint32_t)E && lane == __builtin_ctzll(ch.m[r]))
-      hist_row[ch.key[r]] += __popcll(ch.m[r]);
-}
-
-__device__ void small_scatter(const SmallChunk& ch, int64_t c0, int64_t c1, int E, int* base_row,
-                              int32_t* sorted_slot, int32_t* slot_row) {
-  const int lane = lane_id();
-  const uint64_t below = (1ull << lane) - 1ull;
-#pragma unroll
-  for (int r = 0; r < kSmallRows; ++r) {
-    if (c0 + r * kWave >= c1) continue;                     // uniform
-    const int64_t s = c0 + r * kWave + lane;
-    const uint32_t key = ch.key[r];
-    if (s < c1) {
-      if (key < (uint32_t)E) {
-        const int pos = base_row[key] + __popcll(ch.m[r] & below);
-        sorted_slot[pos] = (int32_t)s;
-        slot_row[s] = pos;
-      } else {
-        slot_row[s] = -1;
-      }
-    }
-    // every lane has read base_row[key] above; LDS ops of one wave stay in order
-    if (key < (uint32_t)E && lane == __builtin_ctzll(ch.m[r])) base_row[key] += __popcll(ch.m[r]);
-  }
-}
-
-// Exclusive scan of data[0, n) (LDS) by the whole workgroup; returns the total.
-__device__ int block_exclusive_scan(int* data, int n, int* wave_tmp) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  const int per = ceil_div(n, nt);
-  const int lo = min(n, tid * per), hi = min(n, lo + per);
-  int local = 0;
-  for (int i = lo; i < hi; ++i) local += data[i];
-  int v = local;
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(v, d);
-    if (lane_id() >= d) v += o;
-  }
-  if (lane_id() == kWave - 1) wave_tmp[tid / kWave] = v;
-  __syncthreads();
-  int before = 0, total = 0;
-  for (int w = 0; w < nt / kWave; ++w) {
-    if (w < tid / kWave) before += wave_tmp[w];
-    total += wave_tmp[w];
-  }
-  int run = before + v - local;
-  for (int i = lo; i < hi; ++i) {
-    const int c = data[i];
-    data[i] = run;
-    run += c;
-  }
-  __syncthreads();
-  return total;
-}
-
-// Write the row-tile list of height bm from cnt[e] and offs[e] (LDS), into
-// tiles (and into tiles2 too, when given: two lists of the same height).
-// scratch (LDS, E entries) is clobbered.  All threads must call.
-__device__ void build_tiles(const int* cnt, const int* offs, int E, int bm, int* scratch, int* wave_tmp,
-                            Tile* tiles, int32_t* ntiles, Tile* tiles2 = nullptr, int32_t* ntiles2 = nullptr) {
-  for (int e = threadIdx.x; e < E; e += blockDim.x) scratch[e] = ceil_div(cnt[e], bm);
-  __syncthreads();
-  const int total = block_exclusive_scan(scratch, E, wave_tmp);
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    const int nt = ceil_div(cnt[e], bm);
-    for (int j = 0; j < nt; ++j) {
-      Tile t;
-      t.e = e;
-      t.row0 = offs[e] + j * bm;
-      t.nrows = min(bm, cnt[e] - j * bm);
-      t.pad = 0;
-      tiles[scratch[e] + j] = t;
-      if (tiles2) tiles2[scratch[e] + j] = t;
-    }
-  }
-  if (threadIdx.x == 0) {
-    *ntiles = total;
-    if (ntiles2) *ntiles2 = total;
-  }
-  __syncthreads();
-}
-
-// One workgroup of NW waves.  LDS: hist[NW][E], cnt[E], offs[E+1], scratch[E], wave_tmp[NW].
 template <int NW>
 __global__ __launch_bounds__(NW * kWave) void k_route_small(const int32_t* __restrict__ ids, int S, int E,
                                                             int nbits, int32_t* counts, int32_t* offsets,
@@ -207,52 +78,8 @@ __global__ __launch_bounds__(NW * kWave) void k_route_small(const int32_t* __res
                                                             int32_t* dropped, Tile* tiles_a, int32_t* ntiles_a, int bm_a,
                                                             Tile* tiles_b, int32_t* ntiles_b, int bm_b) {
   extern __shared__ int lds[];
-  int* hist = lds;                 // [NW][E]
-  int* cnt = hist + NW * E;        // [E]
-  int* offs = cnt + E;             // [E+1]
-  int* scratch = offs + E + 1;     // [E]
-  int* wave_tmp = scratch + E;     // [NW]
-  const int tid = threadIdx.x, w = tid / kWave;
-  for (int i = tid; i < NW * E; i += blockDim.x) hist[i] = 0;
-  __syncthreads();
-  const int64_t L = (int64_t)ceil_div(ceil_div(S, NW), kWave) * kWave;
-  const int64_t c0 = min((int64_t)S, w * L), c1 = min((int64_t)S, c0 + L);
-  SmallChunk ch;
-  small_load(ids, c0, c1, E, nbits, ch);
-  small_count(ch, c0, c1, E, hist + w * E);
-  __syncthreads();
-  // per expert: prefix over waves, total count
-  for (int e = tid; e < E; e += blockDim.x) {
-    int run = 0;
-    for (int v = 0; v < NW; ++v) {
-      const int c = hist[v * E + e];
-      hist[v * E + e] = run;
-      run += c;
-    }
-    cnt[e] = run;
-    offs[e] = run;
-  }
-  __syncthreads();
-  const int total = block_exclusive_scan(offs, E, wave_tmp);
-  if (tid == 0) {
-    offs[E] = total;
-    if (dropped) *dropped = S - total;
-  }
-  __syncthreads();
-  for (int e = tid; e <= E; e += blockDim.x) {
-    offsets[e] = offs[e];
-    if (e < E) counts[e] = cnt[e];
-  }
-  for (int i = tid; i < NW * E; i += blockDim.x) hist[i] += offs[i % E];
-  __syncthreads();
-  small_scatter(ch, c0, c1, E, hist + w * E, sorted_slot, slot_row);
-  for (int i = total + tid; i < S; i += blockDim.x) sorted_slot[i] = -1;
-  if (tiles_a && tiles_b && bm_a == bm_b) {
-    build_tiles(cnt, offs, E, bm_a, scratch, wave_tmp, tiles_a, ntiles_a, tiles_b, ntiles_b);
-  } else {
-    if (tiles_a) build_tiles(cnt, offs, E, bm_a, scratch, wave_tmp, tiles_a, ntiles_a);
-    if (tiles_b) build_tiles(cnt, offs, E, bm_b, scratch, wave_tmp, tiles_b, ntiles_b);
-  }
+  route_small<NW>(lds, ids, S, E, nbits, counts, offsets, sorted_slot, slot_row, dropped, tiles_a, ntiles_a, bm_a,
+                  tiles_b, ntiles_b, bm_b);
 }
 
 // Three-kernel path.  ghist[gw][E]: per-wave counts, then per-wave bases.
@@ -382,12 +209,6 @@ __global__ __launch_bounds__(256) void k_build_tiles(const int32_t* offsets, int
   if (tiles_b) build_tiles(cnt, offs, E, bm_b, scratch, wave_tmp, tiles_b, ntiles_b);
 }
 
-int bits_for(int E) {
-  int b = 0;
-  while ((1 << b) <= E) ++b;   // keys 0..E (E is the drop sentinel)
-  return b;
-}
-
 }  // namespace
 
 size_t route_scratch_bytes(int64_t S, int E) {
@@ -410,7 +231,7 @@ hipError_t launch_route(const int32_t* ids, int T, int K, int E, int32_t* counts
   const int nbits = bits_for(E);
   if (S <= 512) {
     constexpr int NW = 4;
-    const size_t lds = sizeof(int) * (size_t)(NW * E + 3 * E + 1 + NW);
+    const size_t lds = sizeof(int) * route_small_lds_ints(NW, E);
     hipLaunchKernelGGL(k_route_small<NW>, dim3(1), dim3(NW * kWave), lds, stream, ids, (int)S, E, nbits, counts,
                        offsets, sorted_slot, slot_row, dropped, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b);
     return hipGetLastError();
@@ -420,7 +241,7 @@ hipError_t launch_route(const int32_t* ids, int T, int K, int E, int32_t* counts
   static_assert(512 / 4 <= kSmallRows * kWave && kSmallMax / 16 <= kSmallRows * kWave, "chunk exceeds registers");
   if (S <= kSmallMax) {
     constexpr int NW = 16;
-    const size_t lds = sizeof(int) * (size_t)(NW * E + 3 * E + 1 + NW);
+    const size_t lds = sizeof(int) * route_small_lds_ints(NW, E);
     hipLaunchKernelGGL(k_route_small<NW>, dim3(1), dim3(NW * kWave), lds, stream, ids, (int)S, E, nbits, counts,
                        offsets, sorted_slot, slot_row, dropped, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b);
     return hipGetLastError();

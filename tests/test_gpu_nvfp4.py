@@ -146,6 +146,10 @@ SMALL = STAGE + [
     Workload("f4_sm_d", T=45, H=384, I=384, E=5, K=3, weight_bits=4, act_int8=False, fmt="nvfp4", seed=24),
     Workload("f4_sm_e", T=200, H=256, I=128, E=16, K=8, weight_bits=4, act_int8=False, fmt="nvfp4", seed=25,
              outlier_frac=0.02),
+    # 512 slots: routing and the quantization of x share one launch; 513:
+    # the routing kernel and the quantizer run as two launches
+    Workload("f4_sm_f", T=64, H=256, I=128, E=32, K=8, weight_bits=4, act_int8=False, fmt="nvfp4", seed=29),
+    Workload("f4_sm_g", T=57, H=256, I=128, E=32, K=9, weight_bits=4, act_int8=False, fmt="nvfp4", seed=30),
 ]
 
 
