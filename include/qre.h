@@ -196,7 +196,9 @@ int qre_quantize_act(const void* v, int32_t rows, int32_t cols, int8_t* q, float
  * (fp32 [T][H/128]), combines INT32 group sums in FP32, and, when hq and hs
  * are given, also writes h quantized per 128 values (the input of the INT8
  * down projection): hq int8 [T*K][I], hs fp32 [T*K][I/128], exactly what
- * qre_quantize_act gives for h.  h: bf16 [T*K][I], optional in INT8 mode
+ * qre_quantize_act gives for h (with INT8 weights and 64 or more rows per
+ * expert the gate/up kernel quantizes h in its epilogue; otherwise the
+ * quantizer runs on h after it).  h: bf16 [T*K][I], optional in INT8 mode
  * when hq/hs are given.  Rows past offsets[E] are not written.  sorted_slot
  * and offsets are qre_route's outputs (or any stable permutation in the same
  * form).  `workspace` (>= qre_stage_workspace_bytes) receives the row-tile

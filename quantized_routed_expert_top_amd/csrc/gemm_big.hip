@@ -337,20 +337,28 @@ struct Big {
 // direct loads as [group][row] FP32; the weight scales, stored [row][group]
 // FP16, are first copied into the LDS of the fourth stage (not loaded before
 // the first round) and converted there into [group][row] FP32.
-template <bool DUAL>
+// WN: waves along the weight rows (two along the activation rows), so the
+// workgroup has 2 WN waves and 64 WN weight rows.  WN = 2: 128 weight rows,
+// two workgroups per CU; WN = 4: 256 weight rows, one workgroup per CU, which
+// loads 24 KB per stage where two narrow workgroups load 32 KB for the same
+// MFMA work.
+template <bool DUAL, int WN>
 struct BigW8A8 {
-  static constexpr int BM = 128, BNW = 128;
-  static constexpr int BNO = DUAL ? 64 : 128;      // output columns per workgroup
+  static constexpr int NWAVE = 2 * WN, NT = 64 * NWAVE;
+  static constexpr int BM = 128, BNW = 64 * WN;
+  static constexpr int HW = BNW / 2;               // DUAL: gate rows, then as many up rows
+  static constexpr int BNO = DUAL ? HW : BNW;      // output columns per workgroup
   static constexpr int TM = 4, TN = 4;             // 16x16 tiles per wave (64 rows x 64 weight rows)
   static constexpr int HB = kGroup / 2;            // reduction bytes per stage (half a group)
-  static constexpr int QA = BM * HB / 16 / 256;    // direct A loads per thread per stage (2)
-  static constexpr int QB = BNW * HB / 16 / 256;   // direct B loads per thread per stage (2)
+  static constexpr int QA = BM * HB / 16 / NT;     // direct A loads per thread per stage
+  static constexpr int QB = BNW * HB / 16 / NT;    // direct B loads per thread per stage (2)
+  static_assert(QA >= 1 && QB == 2 && QA * NT * 16 == BM * HB, "stage split");
   static constexpr int B_OFF = BM * HB;
   static constexpr int STAGE = B_OFF + BNW * HB;
   static constexpr int NS = 4;                     // stages; loads run NS - 1 stages ahead
   static constexpr int VM = QA + QB;               // direct loads per thread per stage
   static constexpr int NHALF = DUAL ? 2 : 1;       // weight-scale sources (gate, up) or one
-  static constexpr int kMaxGroups = 64;            // the FP16 weight-scale copy fits one stage
+  static constexpr int kMaxGroups = 64;            // every group's scales sit in LDS
   // FP16 weight-scale copy in the fourth stage: NHALF parts of BNW / NHALF
   // rows, each padded to whole KB (the direct loads move 1 KB per wave)
   __host__ __device__ static int ws16_part(int ng) { return (BNW / NHALF) * ng * 2; }
@@ -362,9 +370,14 @@ struct BigW8A8 {
   __device__ static uint32_t chunk_pos(int row, int chunk) {
     return (uint32_t)(row * HB + ((chunk ^ ((row >> 1) & 3)) << 4));
   }
+  // the FP16 weight-scale copy of ng groups fits the fourth stage and every
+  // group's FP32 scales fit beside the stages
+  __host__ __device__ static bool fits(int ng) {
+    return ng <= kMaxGroups && NHALF * ws16_pad(ng) <= STAGE && lds_bytes(ng) <= 160 * 1024;
+  }
   // first tile row of the wave's weight tile j (DUAL: j < 2 gate rows, j >= 2
-  // the same columns' up rows, 64 further on)
-  __device__ static int wrow0(int wn, int j) { return DUAL ? (j >> 1) * 64 + wn * 32 + (j & 1) * 16 : wn * 64 + j * 16; }
+  // the same columns' up rows, HW further on)
+  __device__ static int wrow0(int wn, int j) { return DUAL ? (j >> 1) * HW + wn * 32 + (j & 1) * 16 : wn * 64 + j * 16; }
 
   template <class RowSrc>
   __device__ static void run(const GemmProblem& p, int cb, int e, int row0, int nrows, RowSrc src, uint8_t* lds) {
@@ -389,13 +402,13 @@ struct BigW8A8 {
     uint32_t a_off[QA], b_off[QB];
 #pragma unroll
     for (int q = 0; q < QA; ++q) {
-      const int P = (q * 4 + wave) * 64 + lane, row = P >> 2, c = (P & 3) ^ ((row >> 1) & 3);
+      const int P = (q * NWAVE + wave) * 64 + lane, row = P >> 2, c = (P & 3) ^ ((row >> 1) & 3);
       a_off[q] = row < nrows ? (uint32_t)(src(row) * NG * kGroup) + (uint32_t)(c * 32) : kOOB;
     }
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
-      const int P = (q * 4 + wave) * 64 + lane, n = P >> 2, c = (P & 3) ^ ((n >> 1) & 3);
-      const int wrow = DUAL ? n0 + (n & 63) : n0 + n;  // DUAL: n < 64 gate (q = 0), else up (q = 1)
+      const int P = (q * NWAVE + wave) * 64 + lane, n = P >> 2, c = (P & 3) ^ ((n >> 1) & 3);
+      const int wrow = DUAL ? n0 + (n & (HW - 1)) : n0 + n;   // DUAL: n < HW gate (q = 0), else up (q = 1)
       b_off[q] = (uint32_t)(wrow * NG * kGroup) + (uint32_t)(c * 32);
     }
     auto lds3 = [&](int off) { return (__attribute__((address_space(3))) void*)(lds + off); };
@@ -408,12 +421,12 @@ struct BigW8A8 {
     // bytes [1 KB q, 1 KB q + 1 KB), lanes past the part reading zeros into
     // the padding.  The waves share the loads; a wave's count varies, which
     // the static waits below tolerate (they only bound the newer loads).
-    for (int q = wave; q < 2 * NG; q += 4) {       // uniform
+    for (int q = wave; q < 2 * NG; q += NWAVE) {   // uniform
       const int r = (q & 1) * 64 + lane;
       const uint32_t off = r < nrows ? (uint32_t)((src(r) * NG + (q >> 1)) * 4) : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lds3(XS_OFF + ((q >> 1) * BM + (q & 1) * 64) * 4), 4, off, 0, 0, 0);
     }
-    for (int q = wave; q < NHALF * nkb; q += 4) {  // uniform
+    for (int q = wave; q < NHALF * nkb; q += NWAVE) {   // uniform
       const int part = q / nkb, b = (q - part * nkb) * 1024 + 16 * lane;
       const uint32_t off = b < wpart ? (uint32_t)(n0 * NG * 2 + b) : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(DUAL && part == 1 ? rs1 : rs0, lds3(WS16_OFF + part * wpad + (q - part * nkb) * 1024),
@@ -429,18 +442,18 @@ struct BigW8A8 {
         const uint32_t koff = (uint32_t)((h >> 1) * kGroup + (h & 1) * 16);
 #pragma unroll
         for (int q = 0; q < QA; ++q)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds3(base + (q * 4 + wave) * 1024), 16, a_off[q], koff, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds3(base + (q * NWAVE + wave) * 1024), 16, a_off[q], koff, 0, 0);
 #pragma unroll
         for (int q = 0; q < QB; ++q)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(DUAL && q == 1 ? rw1 : rw0, lds3(base + B_OFF + (q * 4 + wave) * 1024),
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(DUAL && q == 1 ? rw1 : rw0, lds3(base + B_OFF + (q * NWAVE + wave) * 1024),
                                                    16, b_off[q], koff, 0, 0);
       } else {
 #pragma unroll
         for (int q = 0; q < QA; ++q)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds3(base + (q * 4 + wave) * 1024), 16, kOOB, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds3(base + (q * NWAVE + wave) * 1024), 16, kOOB, 0, 0, 0);
 #pragma unroll
         for (int q = 0; q < QB; ++q)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(DUAL && q == 1 ? rw1 : rw0, lds3(base + B_OFF + (q * 4 + wave) * 1024),
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(DUAL && q == 1 ? rw1 : rw0, lds3(base + B_OFF + (q * NWAVE + wave) * 1024),
                                                    16, kOOB, 0, 0, 0);
       }
     };
@@ -454,9 +467,9 @@ struct BigW8A8 {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();                            // and every thread's
     asm volatile("" ::: "memory");
-    for (int idx = tid; idx < BNW * NG; idx += 256) {
+    for (int idx = tid; idx < BNW * NG; idx += NT) {
       const int g = idx / BNW, n = idx - g * BNW;
-      const int part = DUAL ? n >> 6 : 0, nr = DUAL ? n & 63 : n;
+      const int part = DUAL ? n / HW : 0, nr = DUAL ? n % HW : n;
       const uint16_t w = *reinterpret_cast<const uint16_t*>(lds + WS16_OFF + part * wpad + (nr * NG + g) * 2);
       *reinterpret_cast<float*>(lds + WS_OFF + idx * 4) = half_bits_to_f32(w);
     }
@@ -499,7 +512,7 @@ struct BigW8A8 {
       u32x4_t bv[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int nj = DUAL ? ((j >> 1) * 64 + (j & 1) * 16) : j * 16;   // DUAL: up rows start at 64
+        const int nj = DUAL ? ((j >> 1) * HW + (j & 1) * 16) : j * 16;   // DUAL: up rows start at HW
         bv[j] = *reinterpret_cast<const u32x4_t*>(base + B_OFF + b_rd + nj * HB);
       }
 #pragma unroll
@@ -535,6 +548,12 @@ struct BigW8A8 {
     // lane: activation row wm*64 + 16 i + li, output columns 4 kb .. 4 kb + 3
     // of each 16-column tile
     uint16_t* out = static_cast<uint16_t*>(p.out);
+    if constexpr (DUAL && BNO == kGroup) {
+      if (p.hq) {
+        quantize_h_epilogue(p, cb, row0, nrows, acc, lds);
+        if (!out) return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int m = wm * 64 + i * 16 + li;
@@ -557,11 +576,77 @@ struct BigW8A8 {
       }
     }
   }
+
+  // h quantized per 128 values, as the INT8 quantizer does it for the BF16 h
+  // (the workgroup's 128 outputs are one group of each of its rows): the
+  // group maximum of |h| over the lane's eight values, the four 16-lane
+  // segments (xor 16, 32) and the four waves along the columns (LDS), then
+  // s = max / 127 and the codes of the BF16 values.  hq int8 [rows][n],
+  // hs fp32 [rows][n / 128].
+  __device__ static void quantize_h_epilogue(const GemmProblem& p, int cb, int row0, int nrows,
+                                             const f32x4_t (&acc)[TM][TN], uint8_t* lds) {
+    const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, kb = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    float* red = reinterpret_cast<float*>(lds);            // [BM][WN]: every wave is past its last stage
+    float hb[TM][2][4];
+    float mx[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      float m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t lo = pack2_bf16(silu(acc[i][j][0]) * acc[i][j + 2][0], silu(acc[i][j][1]) * acc[i][j + 2][1]);
+        const uint32_t hi = pack2_bf16(silu(acc[i][j][2]) * acc[i][j + 2][2], silu(acc[i][j][3]) * acc[i][j + 2][3]);
+        hb[i][j][0] = bf16_bits_to_f32(lo & 0xffffu);
+        hb[i][j][1] = bf16_bits_to_f32(lo >> 16);
+        hb[i][j][2] = bf16_bits_to_f32(hi & 0xffffu);
+        hb[i][j][3] = bf16_bits_to_f32(hi >> 16);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) m = fmaxf(m, fabsf(hb[i][j][v]));
+      }
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      mx[i] = m;
+    }
+    __syncthreads();                                       // every wave's last stage reads are done
+    if (kb == 0) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) red[(wm * 64 + i * 16 + li) * WN + wn] = mx[i];
+    }
+    __syncthreads();
+    const int ng = p.n / kGroup;
+    int8_t* hq = p.hq;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = wm * 64 + i * 16 + li;
+      float M = red[m * WN];
+#pragma unroll
+      for (int w = 1; w < WN; ++w) M = fmaxf(M, red[m * WN + w]);
+      const float sc = M / 127.0f;
+      const bool zero = !(sc != 0.0f);
+      const float r = 1.0f / (zero ? 1.0f : sc);
+      if (m < nrows) {
+        const int64_t row = row0 + m;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          uint32_t packed = 0u;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int qv = zero ? 0 : (int)act_code(hb[i][j][v], sc, r);
+            packed |= (uint32_t)(qv & 0xff) << (8 * v);
+          }
+          *reinterpret_cast<uint32_t*>(hq + row * p.n + cb * BNO + wn * 32 + j * 16 + 4 * kb) = packed;
+        }
+        if (wn == 0 && kb == 0) p.hs[row * ng + cb] = sc;
+      }
+    }
+  }
 };
 
-template <bool DUAL>
-__global__ __launch_bounds__(256, 2) void k_gemm_w8a8(GemmProblem p) {
-  using K = BigW8A8<DUAL>;
+template <bool DUAL, int WN>
+__global__ __launch_bounds__(128 * WN, (WN == 2) ? 2 : 1) void k_gemm_w8a8(GemmProblem p) {
+  using K = BigW8A8<DUAL, WN>;
   extern __shared__ __attribute__((aligned(16))) uint8_t big_lds[];
   int tile, cb;
   if (!xcd_tile(p, tile, cb)) return;
@@ -589,13 +674,28 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmProblem p) {
     K::run(p, cb, td.e, row0, td.nrows, [&](int r) { return (int64_t)(row0 + r); }, big_lds);
 }
 
+template <bool DUAL, int WN>
+hipError_t launch_w8a8_wn(const GemmProblem& p, hipStream_t stream) {
+  using K = BigW8A8<DUAL, WN>;
+  const dim3 grid(p.n / K::BNO, (unsigned)((p.max_tiles + 7) / 8 * 8));
+  hipLaunchKernelGGL((k_gemm_w8a8<DUAL, WN>), grid, dim3(K::NT), K::lds_bytes(p.kdim / kGroup), stream, p);
+  return hipGetLastError();
+}
+
+// Gate/up: the wide workgroup (128 outputs, one quantization group of h)
+// when the output width and the reduction allow it; it alone can quantize h
+// in its epilogue.  Down: the narrow one (two workgroups per CU keep more
+// loads in flight, which the down GEMM needs).
 template <bool DUAL>
 hipError_t launch_w8a8_cfg(const GemmProblem& p, hipStream_t stream) {
-  using K = BigW8A8<DUAL>;
-  if (p.n % K::BNO != 0 || p.kdim / kGroup > K::kMaxGroups) return hipErrorInvalidValue;
-  const dim3 grid(p.n / K::BNO, (unsigned)((p.max_tiles + 7) / 8 * 8));
-  hipLaunchKernelGGL((k_gemm_w8a8<DUAL>), grid, dim3(256), K::lds_bytes(p.kdim / kGroup), stream, p);
-  return hipGetLastError();
+  using Nw = BigW8A8<DUAL, 2>;
+  const int ng = p.kdim / kGroup;
+  if constexpr (DUAL) {
+    using Wd = BigW8A8<true, 4>;
+    if (p.n % Wd::BNO == 0 && Wd::fits(ng)) return launch_w8a8_wn<true, 4>(p, stream);
+  }
+  if (p.hq || p.n % Nw::BNO != 0 || !Nw::fits(ng)) return hipErrorInvalidValue;
+  return launch_w8a8_wn<DUAL, 2>(p, stream);
 }
 
 template <int WB, bool A8, bool DUAL>
@@ -609,10 +709,16 @@ hipError_t launch_big_cfg(const GemmProblem& p, hipStream_t stream) {
 
 }  // namespace
 
+bool gate_up_quantizes_h(const GemmProblem& p) {
+  using Wd = BigW8A8<true, 4>;
+  return p.bm == 128 && p.act_int8 && p.bits == 8 && p.w1q != nullptr && p.n % Wd::BNO == 0 &&
+         Wd::fits(p.kdim / kGroup);
+}
+
 bool big_applicable(int64_t S, int E, int kdim) {
   // many rows per expert: at least 64 on average; a reduction of at most 64
   // groups (the INT8-activation kernel keeps every group's scales in LDS)
-  return S >= 64 * (int64_t)E && kdim <= BigW8A8<true>::kMaxGroups * kGroup;
+  return S >= 64 * (int64_t)E && kdim <= BigW8A8<true, 2>::kMaxGroups * kGroup;
 }
 
 hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t stream) {

@@ -387,8 +387,16 @@ static int moe_forward_impl(const qre_desc* desc, const void* x, const int32_t* 
   const StageLayout& st = L.st;
   auto mark = [&](int i) -> hipError_t { return (ev && ev[i]) ? hipEventRecord(ev[i], s) : hipSuccess; };
 
-  const GemmProblem gu = gate_up_problem(d, x, L.xq, L.xs, L.sorted_slot, *weights, st.tiles_gu, st.ntiles,
-                                         st.mt_gu, st.bm_gu, L.h);
+  GemmProblem gu = gate_up_problem(d, x, L.xq, L.xs, L.sorted_slot, *weights, st.tiles_gu, st.ntiles, st.mt_gu,
+                                   st.bm_gu, L.h);
+  // INT8 mode with 128-output gate/up workgroups: h leaves the gate/up kernel
+  // already quantized (no BF16 h, no quantizer launch)
+  const bool fused_hq = d.act_int8 && gate_up_quantizes_h(gu);
+  if (fused_hq) {
+    gu.hq = L.hq;
+    gu.hs = L.hs;
+    gu.out = nullptr;
+  }
   const GemmProblem dn = down_problem(d, L.h, L.hq, L.hs, *weights, st.tiles_dn, st.ntiles + 1, st.mt_dn, st.bm_dn,
                                       L.y);
   // Decode-sized problems: the permutation is folded into the gate/up kernel;
@@ -403,7 +411,7 @@ static int moe_forward_impl(const qre_desc* desc, const void* x, const int32_t* 
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = routed ? launch_gate_up_routed(gu, ro, s) : launch_gemm(gu, s);
   if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess && d.act_int8) e = launch_quantize_act(L.h, (int)S, d.I, L.hq, L.hs, s);
+  if (e == hipSuccess && d.act_int8 && !fused_hq) e = launch_quantize_act(L.h, (int)S, d.I, L.hq, L.hs, s);
   if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess) e = routed ? launch_down_routed(dn, ro, s) : launch_gemm(dn, s);
   if (e == hipSuccess) e = mark(4);
@@ -555,14 +563,18 @@ int qre_gate_up(const qre_desc* desc, const void* x, const int8_t* xq, const flo
     return QRE_ERR_ALIGN;
   const StageLayout st = stage_layout(d, workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  void* hout = h ? h : st.h_tmp;
+  GemmProblem p = gate_up_problem(d, x, xq, xs, sorted_slot, *weights, st.tiles_gu, st.ntiles, st.mt_gu, st.bm_gu,
+                                  h ? h : st.h_tmp);
+  const bool fused_hq = hq && gate_up_quantizes_h(p);   // h quantized in the gate/up epilogue
+  if (fused_hq) {
+    p.hq = hq;
+    p.hs = hs;
+    p.out = h;
+  }
   hipError_t e = launch_build_tiles(offsets, d.E, st.tiles_gu, st.ntiles, st.bm_gu, nullptr, nullptr, 0, s);
-  if (e == hipSuccess)
-    e = launch_gemm(gate_up_problem(d, x, xq, xs, sorted_slot, *weights, st.tiles_gu, st.ntiles, st.mt_gu, st.bm_gu,
-                                    hout),
-                    s);
-  if (e == hipSuccess && hq)
-    e = launch_quantize_act(static_cast<const uint16_t*>(hout), (int)((int64_t)d.T * d.K), d.I, hq, hs, s);
+  if (e == hipSuccess) e = launch_gemm(p, s);
+  if (e == hipSuccess && hq && !fused_hq)
+    e = launch_quantize_act(static_cast<const uint16_t*>(p.out), (int)((int64_t)d.T * d.K), d.I, hq, hs, s);
   return hip_status(e);
 }
 

@@ -112,8 +112,10 @@ struct GemmProblem {
   const uint8_t* w0q; const uint16_t* w0s;   // [E][n][kdim*bits/8], [E][n][kdim/128]
   const uint8_t* w1q; const uint16_t* w1s;   // second matrix (gate/up: up), or null
   const Tile* tiles; const int32_t* ntiles; int64_t max_tiles; int bm;
-  void* out;              // bf16 [S][n]
+  void* out;              // bf16 [S][n] (may be null when hq is given)
   int n, kdim;
+  int8_t* hq = nullptr;   // fused gate/up, INT8 mode: h quantized per 128 values,
+  float* hs = nullptr;    // int8 [S][n] and fp32 [S][n/128] (gate_up_quantizes_h)
 };
 // Fused gate/up + SiLU*mul (w1 = up) or plain projection (w1 = null).
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
@@ -122,6 +124,9 @@ int gemm_tile_rows(int64_t S, int E, int n, int kdim);
 // Many rows per expert: 128-row tiles on the MFMA-bound kernel (gemm_big.hip),
 // used by launch_gemm for problems whose tile height is 128.
 bool big_applicable(int64_t S, int E, int kdim);
+// Whether the 128-row gate/up kernel for p quantizes h itself (p.hq, p.hs):
+// INT8 weights and activations, 128 outputs per workgroup.
+bool gate_up_quantizes_h(const GemmProblem& p);
 hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t stream);
 
 // Decode-sized problems (up to kRoutedMaxSlots slots): the gate/up kernel
