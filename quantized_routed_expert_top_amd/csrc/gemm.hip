@@ -567,15 +567,16 @@ template <int WB, bool A8, bool DUAL, int FN, int NG, int DEPTH, int BMR>
 __global__ __launch_bounds__(256) void k_gemm_dec(GemmProblem p) {
   using K = Dec16<WB, A8, DUAL, FN, NG, DEPTH, BMR>;
   extern __shared__ __attribute__((aligned(16))) uint8_t dec_lds[];
-  if ((int)blockIdx.y >= *p.ntiles) return;
-  const Tile td = p.tiles[blockIdx.y];
+  int tile, cb;
+  if (!xcd_tile(p, tile, cb)) return;   // an expert's tiles and a tile's column blocks share one L2
+  const Tile td = p.tiles[tile];
   const int row0 = td.row0;
   const GlobalRowStore st{static_cast<uint16_t*>(p.out), row0, p.n};
   if (p.gather_k) {
     K::run(p, td.e, row0, td.nrows, [&](int r) { return (int64_t)(p.sorted_slot[row0 + r] / p.gather_k); }, st,
-           dec_lds, blockIdx.x);
+           dec_lds, cb);
   } else {
-    K::run(p, td.e, row0, td.nrows, [&](int r) { return (int64_t)(row0 + r); }, st, dec_lds, blockIdx.x);
+    K::run(p, td.e, row0, td.nrows, [&](int r) { return (int64_t)(row0 + r); }, st, dec_lds, cb);
   }
 }
 
@@ -627,7 +628,7 @@ __global__ __launch_bounds__(256) void k_down_routed(GemmProblem p, const int32_
 template <int WB, bool A8, bool DUAL, int FN, int NG, int DEPTH, int BMR>
 hipError_t launch_dec(const GemmProblem& p, hipStream_t stream) {
   using K = Dec16<WB, A8, DUAL, FN, NG, DEPTH, BMR>;
-  const dim3 grid((p.n + K::BN - 1) / K::BN, (unsigned)p.max_tiles);
+  const dim3 grid((p.n + K::BN - 1) / K::BN, (unsigned)((p.max_tiles + 7) / 8 * 8));
   hipLaunchKernelGGL((k_gemm_dec<WB, A8, DUAL, FN, NG, DEPTH, BMR>), grid, dim3(256), K::lds_bytes(), stream, p);
   return hipGetLastError();
 }

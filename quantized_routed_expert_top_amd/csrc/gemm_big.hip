@@ -48,25 +48,6 @@ constexpr int kVmcntEnc[17] = {vmcnt_enc(0),  vmcnt_enc(1),  vmcnt_enc(2),  vmcn
 // tiles 16 apart share read offsets up to a constant.
 __device__ __forceinline__ int swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
 
-// Workgroup -> (row tile, column block).  Workgroups are dispatched to the
-// eight XCDs round-robin (linear id mod 8), and each XCD has its own L2.  The
-// tile list is cut into eight contiguous ranges, one per XCD, walked tile by
-// tile with all column blocks of a tile adjacent: the column blocks of a tile
-// share its activation rows, and the consecutive tiles of an expert share its
-// weights, in one L2.  Returns false for workgroups past the device-side tile
-// count.
-__device__ __forceinline__ bool xcd_tile(const GemmProblem& p, int& tile, int& cb) {
-  const int ncb = gridDim.x;
-  const int lin = blockIdx.y * ncb + blockIdx.x;
-  const int xcd = lin & 7, k = lin >> 3;
-  const int nt = *p.ntiles;
-  const int per = (nt + 7) >> 3;
-  const int local = k / ncb;
-  cb = k - local * ncb;
-  tile = xcd * per + local;
-  return local < per && tile < nt;
-}
-
 template <int WB, bool A8, bool DUAL>
 struct Big {
   static constexpr int BM = 128;                   // sorted rows per tile

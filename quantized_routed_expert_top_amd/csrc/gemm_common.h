@@ -122,6 +122,26 @@ __device__ __forceinline__ u32x4_t b_operand_i8(const u32x4_t* b, int t) {
   return u32x4_t{w0 & 0x0f0f0f0fu, (w0 >> 4) & 0x0f0f0f0fu, w1 & 0x0f0f0f0fu, (w1 >> 4) & 0x0f0f0f0fu};
 }
 
+// Workgroup -> (row tile, column block).  Workgroups are dispatched to the
+// eight XCDs round-robin (linear id mod 8), and each XCD has its own L2.  The
+// tile list is cut into eight contiguous ranges, one per XCD, walked tile by
+// tile with all column blocks of a tile adjacent: the column blocks of a tile
+// share its activation rows, and the consecutive tiles of an expert share its
+// weights, in one L2.  Returns false for workgroups past the device-side tile
+// count.  The grid's second dimension must be a multiple of 8 and at least
+// the tile count.
+__device__ __forceinline__ bool xcd_tile(const GemmProblem& p, int& tile, int& cb) {
+  const int ncb = gridDim.x;
+  const int lin = blockIdx.y * ncb + blockIdx.x;
+  const int xcd = lin & 7, k = lin >> 3;
+  const int nt = *p.ntiles;
+  const int per = (nt + 7) >> 3;
+  const int local = k / ncb;
+  cb = k - local * ncb;
+  tile = xcd * per + local;
+  return local < per && tile < nt;
+}
+
 // One expert's share of the stable counting sort of the routed slots, computed
 // by a workgroup of 256 threads from the ids alone (at most kRoutedMaxSlots
 // slots).  Each wave takes a contiguous quarter of the slots and ballots, per
