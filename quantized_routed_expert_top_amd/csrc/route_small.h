@@ -91,6 +91,18 @@ __device__ void small_scatter(const SmallChunk& ch, int64_t c0, int64_t c1, int 
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then the
+// row broadcasts of lanes 15 and 31).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // Exclusive scan of data[0, n) (LDS) by the whole workgroup; returns the total.
 __device__ int block_exclusive_scan(int* data, int n, int* wave_tmp) {
   const int tid = threadIdx.x, nt = blockDim.x;
@@ -98,11 +110,7 @@ __device__ int block_exclusive_scan(int* data, int n, int* wave_tmp) {
   const int lo = min(n, tid * per), hi = min(n, lo + per);
   int local = 0;
   for (int i = lo; i < hi; ++i) local += data[i];
-  int v = local;
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(v, d);
-    if (lane_id() >= d) v += o;
-  }
+  const int v = wave_incl_scan(local);
   if (lane_id() == kWave - 1) wave_tmp[tid / kWave] = v;
   __syncthreads();
   int before = 0, total = 0;
