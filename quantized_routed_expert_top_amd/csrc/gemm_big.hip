@@ -67,6 +67,7 @@ struct Big {
   static constexpr int NH = A8 ? 1 : 2;            // staging halves (BF16: half a group in flight at a time)
   static constexpr int QH = CPT / NH;              // staged chunks per thread per half
   static constexpr size_t lds_bytes() { return 2 * (size_t)STAGE; }
+  static_assert(A8 || CPG == 16, "BF16 row-groups span one 16-lane DPP row");
 
   __device__ static uint32_t lds_chunk(int row, int chunk) { return (uint32_t)(row * GB + ((chunk ^ swz(row)) << 4)); }
 
@@ -146,8 +147,7 @@ struct Big {
 #pragma unroll
           for (int w = 0; w < 4; ++w)
             t += bf16_bits_to_f32(v[k][w] & 0xffffu) + bf16_bits_to_f32(v[k][w] >> 16);
-#pragma unroll
-          for (int d = 1; d < CPG; d <<= 1) t += __shfl_xor(t, d);
+          t = row16_sum(t);                          // the 16 lanes of the row-group are one DPP row
           if (sc == 0) aux[r] = t;
         }
       }
@@ -178,8 +178,12 @@ struct Big {
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // prologue: group 0 staged, its weights in flight
-    WB_ wcur;
+    // prologue: group 0 staged, its weights in flight.  BF16 activations
+    // with INT4 weights (registers to spare): the next group's weights are requested at the
+    // start of each group, a whole group ahead; INT8 activations: after the
+    // group's last MFMA.
+    constexpr bool kWAhead = !A8 && WB == 4;
+    WB_ wcur, wnxt;
     load_w(wcur, 0);
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -197,6 +201,7 @@ struct Big {
       u32x4_t vn[QH];
       float xsn[QH];
       if (more) load_a(vn, xsn, g + 1, 0);
+      if (kWAhead && more) load_w(wnxt, g + 1);
       const uint8_t* base = lds + b * STAGE;
       const float* aux = reinterpret_cast<const float*>(base + A_STAGE);
       float ws[TN];
@@ -224,8 +229,9 @@ struct Big {
             load_a(vn, xsn, g + 1, NH - 1);
           }
         }
-        // the weight registers are free once the last MFMA has read them
-        if (more) load_w(wcur, g + 1);
+        // without look-ahead the weight registers are refilled once the last
+        // MFMA has read them
+        if (!kWAhead && more) load_w(wcur, g + 1);
         constexpr float kOff = (WB == 4) ? 136.0f : 128.0f;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -271,6 +277,7 @@ struct Big {
         }
       }
       if (more) store_a(vn, xsn, b ^ 1, NH - 1);
+      if (kWAhead && more) wcur = wnxt;
       __syncthreads();
     }
 

@@ -54,6 +54,25 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
+// v of lane + N within its row of 16 lanes (DPP row_shl; lanes whose source
+// leaves the row read 0)
+template <int N>
+__device__ __forceinline__ float row_shl(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x100 + N, 0xf, 0xf,
+                                                               true));
+}
+
+// Sum of t over the 16 lanes of each DPP row, in lane 16r: the pairwise tree
+// ((t0 + t1) + (t2 + t3)) + ... that an xor butterfly over 16 lanes leaves in
+// its lane 0 (the same additions in the same order).
+__device__ __forceinline__ float row16_sum(float t) {
+  t += row_shl<1>(t);
+  t += row_shl<2>(t);
+  t += row_shl<4>(t);
+  t += row_shl<8>(t);
+  return t;
+}
+
 __device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
   return __half2float(__ushort_as_half((unsigned short)h));
 }
