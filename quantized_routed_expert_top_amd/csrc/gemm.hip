@@ -298,8 +298,13 @@ struct Dec16 {
 
   static constexpr int NC = (NG + 3) / 4;                   // 4-group steps of the offset correction
   // LDS: rows [BMR][ROWB], then [NG][16] FP32: activation scales (INT8) or
-  // row sums of each 128-group (BF16, for the 136 + q / 128 + q offset)
-  static constexpr size_t lds_bytes() { return (size_t)BMR * ROWB + (size_t)NG * 16 * 4; }
+  // row sums of each 128-group (BF16, for the 136 + q / 128 + q offset), then
+  // the A-source row of each tile row [BMR]
+  static constexpr size_t lds_bytes() { return (size_t)BMR * ROWB + (size_t)NG * 16 * 4 + (size_t)BMR * 4; }
+  static constexpr int NCH = (BMR * CPR + 255) / 256;       // staged chunks per thread at most
+  // chunk loads in flight together (8-row tiles: decode blocks, one or two
+  // rows per tile, where registers go to the weight look-ahead)
+  static constexpr int SBATCH = (BMR == 8) ? 1 : (NCH < 8 ? NCH : 8);
 
   struct WBuf {
     u32x4_t b[FN][NM][NB];
@@ -321,6 +326,10 @@ struct Dec16 {
   __device__ static void run(const GemmProblem& p, int e, int row0, int nrows, RowSrc src_row, Store store,
                              uint8_t* lds, int cb, bool stage = true) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, kb = lane >> 4;
+    int* s_src = reinterpret_cast<int*>(lds + (size_t)BMR * ROWB + (size_t)NG * 16 * 4);   // [BMR]
+    // 0. the A-source rows of the tile, requested before the weights so that
+    //    waiting for them does not wait for the weight stream
+    if (stage && tid < BMR) s_src[tid] = tid < nrows ? (int)src_row(tid) : 0;
     // 1. per-wave descriptors, weight offsets, all scales of its columns and
     //    the first DEPTH groups of weights: issued before the activation rows
     //    are staged, so the weight stream starts at once
@@ -408,36 +417,51 @@ struct Dec16 {
       load_group(buf[j], j);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // 2. stage the tile's activation rows (and INT8 scales) into LDS
-    const uint8_t* a = static_cast<const uint8_t*>(p.a);
+    // 2. stage the tile's activation rows (and INT8 scales) into LDS.  The
+    //    chunk loads go out SBATCH at a time, so staging waits for memory
+    //    NCH / SBATCH times; the first wait also covers the weights in flight.
     float* xs_lds = reinterpret_cast<float*>(lds + (size_t)BMR * ROWB);   // [NG][16]
     if (stage) {
-    for (int idx = tid; idx < nrows * CPR; idx += blockDim.x) {
-      const int r = idx / CPR, c = idx % CPR;
-      const int64_t src = src_row(r);
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(a + src * ROWB + c * 16);
-      *reinterpret_cast<u32x4_t*>(lds + lds_chunk(r, c)) = a_operand<WB, A8>(v);
-      if constexpr (!A8) {
-        // row sum of the 128-group: 8 values per lane, 16 consecutive lanes
-        float t = 0.f;
+      __syncthreads();                                      // s_src
+      const rsrc_t ra = make_rsrc(p.a, p.a_rows * (int64_t)ROWB);
+      const int nch = nrows * CPR;
+#pragma unroll 1
+      for (int k0 = 0; k0 < NCH && k0 * 256 < nch; k0 += SBATCH) {   // uniform; only the batches holding rows
+        u32x4_t v[SBATCH];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) t += bf16_bits_to_f32(v[w] & 0xffffu) + bf16_bits_to_f32(v[w] >> 16);
+        for (int k = 0; k < SBATCH; ++k) {
+          const int idx = tid + (k0 + k) * 256;
+          const int r = idx / CPR, c = idx - r * CPR;
+          const bool in = k0 + k < NCH && idx < nch;
+          v[k] = bload16(ra, in ? (uint32_t)(s_src[in ? r : 0] * ROWB + c * 16) : kOOB);
+        }
 #pragma unroll
-        for (int d = 1; d < 16; d <<= 1) t += __shfl_xor(t, d);
-        if ((c & 15) == 0) {
-          xs_lds[(c >> 4) * 16 + r] = t;
-          if (BMR == 8) xs_lds[(c >> 4) * 16 + r + 8] = t;   // MFMA rows 8..15 repeat rows 0..7
+        for (int k = 0; k < SBATCH; ++k) {
+          const int idx = tid + (k0 + k) * 256;
+          const int r = idx / CPR, c = idx - r * CPR;
+          const bool in = k0 + k < NCH && idx < nch;
+          if constexpr (!A8) {
+            // row sum of the 128-group: 8 values per lane, 16 consecutive
+            // lanes (one DPP row; the xor-butterfly order)
+            float t = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) t += bf16_bits_to_f32(v[k][w] & 0xffffu) + bf16_bits_to_f32(v[k][w] >> 16);
+            t = row16_sum(t);
+            if (in && (c & 15) == 0) {
+              xs_lds[(c >> 4) * 16 + r] = t;
+              if (BMR == 8) xs_lds[(c >> 4) * 16 + r + 8] = t;   // MFMA rows 8..15 repeat rows 0..7
+            }
+          }
+          if (in) *reinterpret_cast<u32x4_t*>(lds + lds_chunk(r, c)) = a_operand<WB, A8>(v[k]);
         }
       }
-    }
-    if constexpr (A8) {
-      for (int idx = tid; idx < nrows * NG; idx += blockDim.x) {
-        const int r = idx / NG, g = idx % NG;
-        const int64_t src = src_row(r);
-        xs_lds[g * 16 + r] = p.a_scale[src * NG + g];
+      if constexpr (A8) {
+        for (int idx = tid; idx < nrows * NG; idx += blockDim.x) {
+          const int r = idx / NG, g = idx % NG;
+          xs_lds[g * 16 + r] = p.a_scale[(int64_t)s_src[r] * NG + g];
+        }
       }
-    }
-    __syncthreads();
+      __syncthreads();
     }
     if ((cb * 4 + wave) * 16 * FN >= p.n) return;   // wave-uniform, after the barrier
 
