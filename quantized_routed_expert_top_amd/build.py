@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqre.so")
 SOURCES = ["qre_api.hip", "route.hip", "quant.hip", "gemm.hip", "gemm_big.hip", "combine.hip", "router.hip", "probe.hip", "nvfp4.hip"]
-HEADERS = [os.path.join(CSRC, "qre_internal.h"), os.path.join(CSRC, "gemm_common.h"), os.path.join(CSRC, "route_small.h"), os.path.join(INCLUDE, "qre.h")]
+HEADERS = [os.path.join(CSRC, "qre_internal.h"), os.path.join(CSRC, "gemm_common.h"), os.path.join(CSRC, "route_small.h"), os.path.join(CSRC, "quant_act.h"), os.path.join(INCLUDE, "qre.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -404,10 +404,14 @@ static int moe_forward_impl(const qre_desc* desc, const void* x, const int32_t* 
   const bool routed = routed_applicable(S, d.E, d.H, d.I, d.act_int8);
   const RouteOut ro = {topk_ids, (int)S, d.E, L.counts, L.offsets, L.sorted_slot, L.slot_row, st.header};
   hipError_t e = mark(0);
+  // INT8 mode: the quantization of x rides on the routing launches when there
+  // are any (it shares the last of the three large-problem kernels)
+  const QuantX qx = {static_cast<const uint16_t*>(x), d.T, d.H, L.xq, L.xs};
   if (e == hipSuccess && !routed)
     e = launch_route(topk_ids, d.T, d.K, d.E, L.counts, L.offsets, L.sorted_slot, L.slot_row, st.header,
-                     st.route_scratch, st.tiles_gu, st.ntiles, st.bm_gu, st.tiles_dn, st.ntiles + 1, st.bm_dn, s);
-  if (e == hipSuccess && d.act_int8) e = launch_quantize_act(static_cast<const uint16_t*>(x), d.T, d.H, L.xq, L.xs, s);
+                     st.route_scratch, st.tiles_gu, st.ntiles, st.bm_gu, st.tiles_dn, st.ntiles + 1, st.bm_dn, s,
+                     d.act_int8 ? &qx : nullptr);
+  if (e == hipSuccess && d.act_int8 && routed) e = launch_quantize_act(qx.v, qx.rows, qx.cols, qx.q, qx.s, s);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) e = routed ? launch_gate_up_routed(gu, ro, s) : launch_gemm(gu, s);
   if (e == hipSuccess) e = mark(2);

@@ -73,10 +73,19 @@ __device__ __forceinline__ float act_code(float x, float sc, float r) {
 // `ws` (route scratch) must hold route_scratch_bytes(S, E) bytes.
 size_t route_scratch_bytes(int64_t S, int E);
 // `dropped` (may be null) receives S - offsets[E], the slots whose id was
-// outside [0, E).  Either tile list may be null.
+// outside [0, E).  Either tile list may be null.  With qx, the INT8
+// quantization of x [rows][cols] is enqueued too (in the three-kernel path
+// it shares the last routing launch).
+struct QuantX {
+  const uint16_t* v;
+  int rows, cols;
+  int8_t* q;
+  float* s;
+};
 hipError_t launch_route(const int32_t* ids, int T, int K, int E, int32_t* counts, int32_t* offsets,
                         int32_t* sorted_slot, int32_t* slot_row, int32_t* dropped, void* ws, Tile* tiles_a,
-                        int32_t* ntiles_a, int bm_a, Tile* tiles_b, int32_t* ntiles_b, int bm_b, hipStream_t stream);
+                        int32_t* ntiles_a, int bm_a, Tile* tiles_b, int32_t* ntiles_b, int bm_b, hipStream_t stream,
+                        const QuantX* qx = nullptr);
 // Tile list from offsets alone (used by the stage entry points); tiles_b may be null.
 hipError_t launch_build_tiles(const int32_t* offsets, int E, Tile* tiles_a, int32_t* ntiles_a, int bm_a,
                               Tile* tiles_b, int32_t* ntiles_b, int bm_b, hipStream_t stream);

@@ -19,7 +19,7 @@
 
 #include <algorithm>
 
-#include "qre_internal.h"
+#include "quant_act.h"
 
 namespace qre {
 namespace {
@@ -29,35 +29,7 @@ namespace {
 
 __global__ __launch_bounds__(256) void k_quantize_act(const uint16_t* __restrict__ v, int64_t ngroups, int G,
                                                       int8_t* __restrict__ q, float* __restrict__ s) {
-  const int sub = threadIdx.x & 15;
-  for (int64_t gid = (int64_t)blockIdx.x * 16 + threadIdx.x / 16; gid < ngroups; gid += (int64_t)gridDim.x * 16) {
-    // whole 16-lane segments take the same trips
-    const int64_t row = gid / G, g = gid % G;
-    const int64_t off = row * (int64_t)G * kGroup + g * kGroup + sub * 8;
-    const uint4 raw = *reinterpret_cast<const uint4*>(v + off);
-    float x[8];
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[2 * j] = bf16_bits_to_f32(w[j] & 0xffffu);
-      x[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
-    }
-    float m = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(x[j]));
-    m = seg16_max(m);
-    const float sc = m / 127.0f;
-    const bool zero = !(sc != 0.0f);
-    const float r = 1.0f / (zero ? 1.0f : sc);
-    uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int qv = zero ? 0 : (int)act_code(x[j], sc, r);
-      packed[j / 4] |= (uint32_t)(qv & 0xff) << (8 * (j % 4));
-    }
-    *reinterpret_cast<uint2*>(q + off) = make_uint2(packed[0], packed[1]);
-    if (sub == 0) s[gid] = sc;
-  }
+  quantize_act_groups(v, ngroups, G, q, s, blockIdx.x, gridDim.x);
 }
 
 __global__ __launch_bounds__(256) void k_quantize_weights(const float* __restrict__ w, int64_t ngroups, int G,

@@ -18,6 +18,9 @@
 //    ascending slot order.
 // Small problems (S <= kSmallMax) do all of it in one workgroup with the
 // tables in LDS; larger ones use three kernels with the per-wave table in HBM.
+#include <algorithm>
+
+#include "quant_act.h"
 #include "route_small.h"
 
 namespace qre {
@@ -151,12 +154,11 @@ __global__ __launch_bounds__(256) void k_route_prefix(int32_t* ghist, int nwaves
 // also writes offsets and the row-tile lists.  Then every wave scatters its
 // chunk from its bases.  LDS: rows[4][E], cnt[E], offs[E+1], scratch[E],
 // wave_tmp[4].
-__global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict__ ids, int S, int E, int nbits,
-                                                       const int32_t* ghist, const int32_t* counts, int32_t* offsets,
-                                                       int32_t* dropped, Tile* tiles_a, int32_t* ntiles_a, int bm_a, Tile* tiles_b,
-                                                       int32_t* ntiles_b, int bm_b, int32_t* sorted_slot,
-                                                       int32_t* slot_row) {
-  extern __shared__ int lds[];
+// Scatter pass of workgroup blk of nblk (LDS: 7E + 5 ints).
+__device__ void route_scatter(int* lds, const int32_t* __restrict__ ids, int S, int E, int nbits, const int32_t* ghist,
+                              const int32_t* counts, int32_t* offsets, int32_t* dropped, Tile* tiles_a,
+                              int32_t* ntiles_a, int bm_a, Tile* tiles_b, int32_t* ntiles_b, int bm_b,
+                              int32_t* sorted_slot, int32_t* slot_row, int blk, int nblk) {
   int* rows = lds;                 // [4][E]
   int* cnt = rows + 4 * E;         // [E]
   int* offs = cnt + E;             // [E+1]
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict
   const int total = block_exclusive_scan(offs, E, wave_tmp);
   if (tid == 0) offs[E] = total;
   __syncthreads();
-  if (blockIdx.x == 0) {           // uniform over the workgroup
+  if (blk == 0) {                  // uniform over the workgroup
     for (int e = tid; e <= E; e += blockDim.x) offsets[e] = offs[e];
     if (tid == 0 && dropped) *dropped = S - total;
     if (tiles_a && tiles_b && bm_a == bm_b) {
@@ -183,13 +185,41 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict
     }
   }
   int* row = rows + w * E;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + w;
+  const int64_t gw = (int64_t)blk * 4 + w;
   for (int e = lane_id(); e < E; e += kWave) row[e] = ghist[gw * E + e] + offs[e];
   const int64_t c0 = min((int64_t)S, gw * kLargeChunk), c1 = min((int64_t)S, c0 + kLargeChunk);
   wave_scatter(ids, c0, c1, E, nbits, row, sorted_slot, slot_row);
-  for (int64_t i = total + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < S;
-       i += (int64_t)gridDim.x * blockDim.x)
+  for (int64_t i = total + (int64_t)blk * blockDim.x + threadIdx.x; i < S; i += (int64_t)nblk * blockDim.x)
     sorted_slot[i] = -1;
+}
+
+__global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict__ ids, int S, int E, int nbits,
+                                                       const int32_t* ghist, const int32_t* counts, int32_t* offsets,
+                                                       int32_t* dropped, Tile* tiles_a, int32_t* ntiles_a, int bm_a,
+                                                       Tile* tiles_b, int32_t* ntiles_b, int bm_b, int32_t* sorted_slot,
+                                                       int32_t* slot_row) {
+  extern __shared__ int lds[];
+  route_scatter(lds, ids, S, E, nbits, ghist, counts, offsets, dropped, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b,
+                bm_b, sorted_slot, slot_row, blockIdx.x, gridDim.x);
+}
+
+// The scatter (the first nscatter workgroups) and the INT8 quantization of x
+// (the others) in one launch: neither reads what the other writes.
+__global__ __launch_bounds__(256) void k_route_scatter_qx(const int32_t* __restrict__ ids, int S, int E, int nbits,
+                                                          const int32_t* ghist, const int32_t* counts,
+                                                          int32_t* offsets, int32_t* dropped, Tile* tiles_a,
+                                                          int32_t* ntiles_a, int bm_a, Tile* tiles_b,
+                                                          int32_t* ntiles_b, int bm_b, int32_t* sorted_slot,
+                                                          int32_t* slot_row, int nscatter, QuantX qx) {
+  extern __shared__ int lds[];
+  if ((int)blockIdx.x < nscatter) {
+    route_scatter(lds, ids, S, E, nbits, ghist, counts, offsets, dropped, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b,
+                  bm_b, sorted_slot, slot_row, blockIdx.x, nscatter);
+    return;
+  }
+  const int G = qx.cols / kGroup;
+  quantize_act_groups(qx.v, (int64_t)qx.rows * G, G, qx.q, qx.s, (int)blockIdx.x - nscatter,
+                      (int)gridDim.x - nscatter);
 }
 
 __global__ __launch_bounds__(256) void k_build_tiles(const int32_t* offsets, int E, Tile* tiles_a,
@@ -226,7 +256,8 @@ int64_t max_tiles(int64_t S, int E, int bm) {
 
 hipError_t launch_route(const int32_t* ids, int T, int K, int E, int32_t* counts, int32_t* offsets,
                         int32_t* sorted_slot, int32_t* slot_row, int32_t* dropped, void* ws, Tile* tiles_a,
-                        int32_t* ntiles_a, int bm_a, Tile* tiles_b, int32_t* ntiles_b, int bm_b, hipStream_t stream) {
+                        int32_t* ntiles_a, int bm_a, Tile* tiles_b, int32_t* ntiles_b, int bm_b, hipStream_t stream,
+                        const QuantX* qx) {
   const int64_t S = (int64_t)T * K;
   const int nbits = bits_for(E);
   if (S <= 512) {
@@ -234,7 +265,8 @@ hipError_t launch_route(const int32_t* ids, int T, int K, int E, int32_t* counts
     const size_t lds = sizeof(int) * route_small_lds_ints(NW, E);
     hipLaunchKernelGGL(k_route_small<NW>, dim3(1), dim3(NW * kWave), lds, stream, ids, (int)S, E, nbits, counts,
                        offsets, sorted_slot, slot_row, dropped, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b);
-    return hipGetLastError();
+    const hipError_t err = hipGetLastError();
+    return (err == hipSuccess && qx) ? launch_quantize_act(qx->v, qx->rows, qx->cols, qx->q, qx->s, stream) : err;
   }
   // the one-workgroup kernel holds at most kSmallRows rows of 64 slots per
   // wave in registers: 4 waves up to 512 slots, 16 waves up to kSmallMax
@@ -244,7 +276,8 @@ hipError_t launch_route(const int32_t* ids, int T, int K, int E, int32_t* counts
     const size_t lds = sizeof(int) * route_small_lds_ints(NW, E);
     hipLaunchKernelGGL(k_route_small<NW>, dim3(1), dim3(NW * kWave), lds, stream, ids, (int)S, E, nbits, counts,
                        offsets, sorted_slot, slot_row, dropped, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b);
-    return hipGetLastError();
+    const hipError_t err = hipGetLastError();
+    return (err == hipSuccess && qx) ? launch_quantize_act(qx->v, qx->rows, qx->cols, qx->q, qx->s, stream) : err;
   }
   int32_t* ghist = static_cast<int32_t*>(ws);
   const int64_t nwaves = (S + kLargeChunk - 1) / kLargeChunk;
@@ -257,9 +290,17 @@ hipError_t launch_route(const int32_t* ids, int T, int K, int E, int32_t* counts
                      counts);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_route_scatter, dim3(nblocks), dim3(256), sizeof(int) * (size_t)(7 * E + 5), stream, ids,
-                     (int)S, E, nbits, ghist, counts, offsets, dropped, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b,
-                     sorted_slot, slot_row);
+  const size_t slds = sizeof(int) * (size_t)(7 * E + 5);
+  if (qx && qx->rows > 0) {
+    const int64_t ngroups = (int64_t)qx->rows * (qx->cols / kGroup);
+    const int64_t qblocks = std::min((ngroups + 15) / 16, kMaxQuantBlocks);
+    hipLaunchKernelGGL(k_route_scatter_qx, dim3((unsigned)(nblocks + qblocks)), dim3(256), slds, stream, ids, (int)S, E,
+                       nbits, ghist, counts, offsets, dropped, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b,
+                       sorted_slot, slot_row, nblocks, *qx);
+  } else {
+    hipLaunchKernelGGL(k_route_scatter, dim3(nblocks), dim3(256), slds, stream, ids, (int)S, E, nbits, ghist, counts,
+                       offsets, dropped, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b, sorted_slot, slot_row);
+  }
   return hipGetLastError();
 }
 
