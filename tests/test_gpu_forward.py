@@ -88,6 +88,11 @@ SMALL = [
     Workload("big_b", T=700, H=384, I=256, E=6, K=3, weight_bits=8, act_int8=True, seed=23),
     Workload("big_c", T=500, H=512, I=384, E=5, K=2, weight_bits=4, act_int8=True, seed=24),
     Workload("big_d", T=400, H=640, I=256, E=3, K=2, weight_bits=8, act_int8=False, seed=25),
+    # more than 8192 slots with INT8 activations: the three routing kernels,
+    # the last of which also quantizes x; 128-row tiles (INT8 weights: gate/up
+    # quantizes h in its epilogue) and 8-row tiles (INT4 weights)
+    Workload("big_e", T=1100, H=256, I=128, E=16, K=8, weight_bits=8, act_int8=True, seed=35),
+    Workload("big_f", T=1040, H=256, I=128, E=160, K=8, weight_bits=4, act_int8=True, seed=36),
 ]
 
 
