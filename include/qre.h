@@ -262,8 +262,9 @@ int qre_quantize_weights(const float* w, int64_t rows, int64_t cols, int32_t bit
  * mask).  QRE_PLAN_ROUTE_IN_GATE_UP: the permutation is computed inside the
  * gate/up kernel (no routing launch).  QRE_PLAN_COMBINE_IN_DOWN: the combine
  * runs inside the down kernel (no combine launch).  QRE_PLAN_BIG_TILES:
- * 128-row MFMA tiles for the gate/up GEMM (64 or more slots per expert and
- * a hidden size of at most 8192). */
+ * the big-tile MFMA kernels for the gate/up GEMM (64 or more slots per expert
+ * and a hidden size of at most 8192: 64-row tiles with BF16 activations,
+ * 128-row tiles with INT8 activations). */
 #define QRE_PLAN_ROUTE_IN_GATE_UP 1
 #define QRE_PLAN_COMBINE_IN_DOWN 2
 #define QRE_PLAN_BIG_TILES 4

@@ -777,12 +777,15 @@ hipError_t launch_routed_mode(const GemmProblem& gu, const GemmProblem& dn, cons
 
 // Row-tile height: 8 when experts see only a few rows each (decode blocks: the
 // weights stream once per tile either way, and a smaller activation tile leaves
-// LDS for more workgroups), 16 otherwise.
-int gemm_tile_rows(int64_t S, int E, int, int kdim) { return big_applicable(S, E, kdim) ? 128 : (S <= 4 * (int64_t)E) ? 8 : 16; }
+// LDS for more workgroups), 16 otherwise; the big-tile kernels' height (64 or
+// 128) when experts average 64 rows or more.
+int gemm_tile_rows(int64_t S, int E, int, int kdim, int act_int8) {
+  return big_applicable(S, E, kdim) ? big_tile_rows(act_int8) : (S <= 4 * (int64_t)E) ? 8 : 16;
+}
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream) {
   if (p.max_tiles == 0 || p.n == 0) return hipSuccess;
-  if (p.bm == 128) return launch_gemm_big(p, stream);
+  if (p.bm >= 64) return launch_gemm_big(p, stream);
   const bool dual = p.w1q != nullptr;
   if (p.bits == 4) {
     if (p.act_int8) return dual ? launch_shape<4, true, true>(p, stream) : launch_shape<4, true, false>(p, stream);

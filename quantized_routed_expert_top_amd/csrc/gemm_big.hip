@@ -7,10 +7,13 @@
 // on INT8 MFMAs (exact INT32 sums per 128-group), each group's sum scaled in
 // FP32 and the groups added in FP32.  The tiling is this kernel's own, made
 // for tiles that the matrix cores, not HBM, bound:
-//  * workgroup tile: 128 sorted rows of one expert x 128 weight rows (the
-//    fused gate/up kernel takes 64 gate and the same 64 up rows, so the tile
-//    is 64 output columns of h); four waves in 2 x 2, each 64 x 64
-//    (sixteen 16x16 MFMA tiles);
+//  * workgroup tile: four waves, each 64 sorted rows x 64 weight rows
+//    (sixteen 16x16 MFMA tiles).  BF16 activations: the waves side by side
+//    along the weight rows (64 sorted rows of one expert x 256 weight rows),
+//    so each weight column is loaded and dequantized by one wave only and a
+//    staged activation row serves 256 weight rows; INT8 activations: 2 x 2
+//    (128 rows x 128 weight rows).  The fused gate/up kernel takes half its
+//    weight rows from gate and the same columns from up;
 //  * the reduction is walked one 128-group at a time: the group's activation
 //    rows are staged into LDS (double-buffered, XOR-swizzled 16-byte chunks,
 //    already permuted into the operand order), together with one FP32 per row
@@ -19,8 +22,9 @@
 //    weight columns straight into registers (16-byte buffer loads, next group
 //    in flight while the current one computes);
 //  * per group: MFMAs into a per-group accumulator, then one FP32 update of
-//    the running sums (INT8: acc += float(isum) * (xs * ws); BF16: acc +=
-//    ws * (gsum - offset * rowsum)), one barrier per group;
+//    the running sums (INT8: acc += float(isum) * (xs * ws); BF16: the
+//    group's MFMAs start from -offset * rowsum, then acc += ws * gsum), one
+//    barrier per group;
 //  * epilogue: SiLU(gate) * up (fused kernel) or the plain sum, rounded to
 //    BF16, rows past the tile's end masked.
 #include <type_traits>
@@ -48,10 +52,11 @@ constexpr int kVmcntEnc[17] = {vmcnt_enc(0),  vmcnt_enc(1),  vmcnt_enc(2),  vmcn
 // tiles 16 apart share read offsets up to a constant.
 __device__ __forceinline__ int swz(int r) { return (r ^ ((r >> 3) & 1)) & 7; }
 
-template <int WB, bool A8, bool DUAL>
+template <int WB, bool A8, bool DUAL, int WM = 2>
 struct Big {
-  static constexpr int BM = 128;                   // sorted rows per tile
-  static constexpr int BNO = DUAL ? 64 : 128;      // output columns per workgroup
+  static constexpr int WN = 4 / WM;                // waves along the weight rows (WM along the sorted rows)
+  static constexpr int BM = 64 * WM;               // sorted rows per tile
+  static constexpr int BNO = (DUAL ? 32 : 64) * WN;   // output columns per workgroup
   static constexpr int TM = 4, TN = 4;             // 16x16 tiles per wave (64 x 64)
   static constexpr int ELEM = A8 ? 1 : 2;
   static constexpr int GB = kGroup * ELEM;         // bytes of one row's 128-group
@@ -75,10 +80,14 @@ struct Big {
   template <class RowSrc>
   __device__ static void run(const GemmProblem& p, int cb, int e, int row0, int nrows, RowSrc src, uint8_t* lds) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, kb = lane >> 4;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave % WM, wn = wave / WM;
     const int live = min(TM, max(0, (nrows - wm * 64 + 15) >> 4));   // 16-row blocks holding rows (uniform)
     const int NG = p.kdim / kGroup;
     const int n0 = cb * BNO;
+    // a wave whose columns lie past n (the last column block of a width that
+    // is not a multiple of BNO) reads zeros through the buffer bound and
+    // stores nothing
+    const bool wcols = n0 + wn * (DUAL ? 32 : 64) < p.n;
 
     // weights: column of each 16-wide tile this lane feeds
     const int64_t mat_bytes = (int64_t)p.n * NG * WGB;
@@ -208,6 +217,17 @@ struct Big {
 #pragma unroll
       for (int j = 0; j < TN; ++j) ws[j] = half_bits_to_f32(wcur.s[j]);
       if constexpr (!A8) {
+        // the group's sums start from -offset * (row sum), so they leave the
+        // MFMAs without the 136 + q / 128 + q offset
+        constexpr float kOff = (WB == 4) ? 136.0f : 128.0f;
+        f32x4_t cinit[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          if (i >= live) continue;
+          const f32x4_t rsum = *reinterpret_cast<const f32x4_t*>(aux + wm * 64 + i * 16 + 4 * kb);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) cinit[i][v] = -kOff * rsum[v];
+        }
         f32x4_t part[TM][TN];
 #pragma unroll
         for (int t = 0; t < STEPS; ++t) {
@@ -221,8 +241,8 @@ struct Big {
                 __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(base + a_base[t] + i * 16 * GB));
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-              part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  av, __builtin_bit_cast(bf16x8_t, bv[j]), t == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : part[i][j], 0, 0, 0);
+              part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bv[j]),
+                                                                   t == 0 ? cinit[i] : part[i][j], 0, 0, 0);
           }
           if (NH == 2 && t == STEPS / 2 - 1 && more) {   // first half staged, second half in flight
             store_a(vn, xsn, b ^ 1, 0);
@@ -232,16 +252,13 @@ struct Big {
         // without look-ahead the weight registers are refilled once the last
         // MFMA has read them
         if (!kWAhead && more) load_w(wcur, g + 1);
-        constexpr float kOff = (WB == 4) ? 136.0f : 128.0f;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           if (i >= live) continue;
-          const f32x4_t rsum = *reinterpret_cast<const f32x4_t*>(aux + wm * 64 + i * 16 + 4 * kb);
 #pragma unroll
           for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-              acc[i][j][v] = __builtin_fmaf(ws[j], __builtin_fmaf(-kOff, rsum[v], part[i][j][v]), acc[i][j][v]);
+            for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf(ws[j], part[i][j][v], acc[i][j][v]);
         }
       } else {
         i32x4_t part[TM][TN];
@@ -288,7 +305,7 @@ struct Big {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int r = wm * 64 + i * 16 + 4 * kb + v;
-        if (r < nrows) {
+        if (r < nrows && wcols) {
           uint16_t* orow = out + (int64_t)(row0 + r) * p.n;
           if constexpr (DUAL) {
 #pragma unroll
@@ -647,9 +664,9 @@ __global__ __launch_bounds__(128 * WN, (WN == 2) ? 2 : 1) void k_gemm_w8a8(GemmP
     K::run(p, cb, td.e, row0, td.nrows, [&](int r) { return (int64_t)(row0 + r); }, big_lds);
 }
 
-template <int WB, bool A8, bool DUAL>
+template <int WB, bool A8, bool DUAL, int WM>
 __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmProblem p) {
-  using K = Big<WB, A8, DUAL>;
+  using K = Big<WB, A8, DUAL, WM>;
   extern __shared__ __attribute__((aligned(16))) uint8_t big_lds[];
   int tile, cb;
   if (!xcd_tile(p, tile, cb)) return;
@@ -686,12 +703,12 @@ hipError_t launch_w8a8_cfg(const GemmProblem& p, hipStream_t stream) {
   return launch_w8a8_wn<DUAL, 2>(p, stream);
 }
 
-template <int WB, bool A8, bool DUAL>
+template <int WB, bool A8, bool DUAL, int WM>
 hipError_t launch_big_cfg(const GemmProblem& p, hipStream_t stream) {
-  using K = Big<WB, A8, DUAL>;
-  if (p.n % K::BNO != 0) return hipErrorInvalidValue;
-  const dim3 grid(p.n / K::BNO, (unsigned)((p.max_tiles + 7) / 8 * 8));
-  hipLaunchKernelGGL((k_gemm_big<WB, A8, DUAL>), grid, dim3(256), K::lds_bytes(), stream, p);
+  using K = Big<WB, A8, DUAL, WM>;
+  if (p.n % (DUAL ? 32 : 64) != 0 || p.bm != K::BM) return hipErrorInvalidValue;
+  const dim3 grid((p.n + K::BNO - 1) / K::BNO, (unsigned)((p.max_tiles + 7) / 8 * 8));
+  hipLaunchKernelGGL((k_gemm_big<WB, A8, DUAL, WM>), grid, dim3(256), K::lds_bytes(), stream, p);
   return hipGetLastError();
 }
 
@@ -709,15 +726,18 @@ bool big_applicable(int64_t S, int E, int kdim) {
   return S >= 64 * (int64_t)E && kdim <= BigW8A8<true, 2>::kMaxGroups * kGroup;
 }
 
+int big_tile_rows(int act_int8) { return act_int8 ? 128 : 64; }
+
 hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t stream) {
   const bool dual = p.w1q != nullptr;
-  if (p.bm != 128) return hipErrorInvalidValue;
+  if (p.bm != big_tile_rows(p.act_int8)) return hipErrorInvalidValue;
   if (p.bits == 4) {
-    if (p.act_int8) return dual ? launch_big_cfg<4, true, true>(p, stream) : launch_big_cfg<4, true, false>(p, stream);
-    return dual ? launch_big_cfg<4, false, true>(p, stream) : launch_big_cfg<4, false, false>(p, stream);
+    if (p.act_int8)
+      return dual ? launch_big_cfg<4, true, true, 2>(p, stream) : launch_big_cfg<4, true, false, 2>(p, stream);
+    return dual ? launch_big_cfg<4, false, true, 1>(p, stream) : launch_big_cfg<4, false, false, 1>(p, stream);
   }
   if (p.act_int8) return dual ? launch_w8a8_cfg<true>(p, stream) : launch_w8a8_cfg<false>(p, stream);
-  return dual ? launch_big_cfg<8, false, true>(p, stream) : launch_big_cfg<8, false, false>(p, stream);
+  return dual ? launch_big_cfg<8, false, true, 1>(p, stream) : launch_big_cfg<8, false, false, 1>(p, stream);
 }
 
 }  // namespace qre

@@ -72,8 +72,8 @@ struct StageLayout {
 
 void carve_stage(const qre_desc& d, Carver& c, StageLayout& L, bool stage) {
   const int64_t S = (int64_t)d.T * d.K;
-  L.bm_gu = gemm_tile_rows(S, d.E, 2 * d.I, d.H);
-  L.bm_dn = gemm_tile_rows(S, d.E, d.H, d.I);
+  L.bm_gu = gemm_tile_rows(S, d.E, 2 * d.I, d.H, d.act_int8);
+  L.bm_dn = gemm_tile_rows(S, d.E, d.H, d.I, d.act_int8);
   L.mt_gu = max_tiles(S, d.E, L.bm_gu);
   L.mt_dn = max_tiles(S, d.E, L.bm_dn);
   L.header = c.take<int32_t>(kHeaderInts);
@@ -149,8 +149,8 @@ int check_desc(const qre_desc* d) {
   if ((int64_t)d->H * d->I * 2 >= (1ll << 31)) return QRE_ERR_LIMIT;
   if (max_tiles(S, d->E, 1) >= (1ll << 31)) return QRE_ERR_LIMIT;
   // grid limit of the GEMM launch (row tiles along grid.y, rounded up to a multiple of 8)
-  if (max_tiles(S, d->E, gemm_tile_rows(S, d->E, 2 * d->I, d->H)) > 65528) return QRE_ERR_LIMIT;
-  if (max_tiles(S, d->E, gemm_tile_rows(S, d->E, d->H, d->I)) > 65528) return QRE_ERR_LIMIT;
+  if (max_tiles(S, d->E, gemm_tile_rows(S, d->E, 2 * d->I, d->H, d->act_int8)) > 65528) return QRE_ERR_LIMIT;
+  if (max_tiles(S, d->E, gemm_tile_rows(S, d->E, d->H, d->I, d->act_int8)) > 65528) return QRE_ERR_LIMIT;
   return QRE_OK;
 }
 

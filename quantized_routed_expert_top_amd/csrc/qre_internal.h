@@ -129,10 +129,12 @@ struct GemmProblem {
 // Fused gate/up + SiLU*mul (w1 = up) or plain projection (w1 = null).
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 // Row-tile height the GEMM wants for a problem with S sorted rows over E experts.
-int gemm_tile_rows(int64_t S, int E, int n, int kdim);
-// Many rows per expert: 128-row tiles on the MFMA-bound kernel (gemm_big.hip),
-// used by launch_gemm for problems whose tile height is 128.
+int gemm_tile_rows(int64_t S, int E, int n, int kdim, int act_int8);
+// Many rows per expert: the MFMA-bound kernels of gemm_big.hip, with tiles of
+// big_tile_rows(act_int8) rows (64 with BF16 activations, 128 with INT8
+// ones), used by launch_gemm for problems whose tile height is 64 or more.
 bool big_applicable(int64_t S, int E, int kdim);
+int big_tile_rows(int act_int8);
 // Whether the 128-row gate/up kernel for p quantizes h itself (p.hq, p.hs):
 // INT8 weights and activations, 128 outputs per workgroup.
 bool gate_up_quantizes_h(const GemmProblem& p);

@@ -82,8 +82,10 @@ SMALL = [
     Workload("st_b", T=30, H=1024, I=256, E=40, K=6, weight_bits=8, act_int8=False, seed=32),
     Workload("st_c", T=33, H=512, I=128, E=1, K=1, weight_bits=8, act_int8=False, seed=33),
     Workload("st_d", T=7, H=2048, I=512, E=64, K=8, weight_bits=4, act_int8=False, seed=34, router="zipf"),
-    # at least 64 rows per expert on average: the 128-row MFMA tiles (several
-    # tiles per expert with ragged tails; a reduction of one group)
+    # at least 64 rows per expert on average: the big-tile MFMA kernels
+    # (64-row tiles with BF16 activations, 128-row with INT8; several tiles
+    # per expert with ragged tails; a reduction of one group; H = 640: a
+    # down column block of 256 that is half past the width)
     Workload("big_a", T=600, H=256, I=128, E=4, K=2, weight_bits=4, act_int8=False, seed=22),
     Workload("big_b", T=700, H=384, I=256, E=6, K=3, weight_bits=8, act_int8=True, seed=23),
     Workload("big_c", T=500, H=512, I=384, E=5, K=2, weight_bits=4, act_int8=True, seed=24),

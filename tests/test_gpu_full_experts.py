@@ -1,6 +1,7 @@
 """Whole experts at full size: the prefill (W8A8) and skewed (Zipf, W4A16)
 workloads run through the stage entry points (the same kernels and launch
-configuration as the whole feed-forward at these sizes: 128-row MFMA tiles),
+configuration as the whole feed-forward at these sizes: the big-tile MFMA
+kernels),
 and every row of three experts -- the hottest, one of median load and the
 least loaded -- is compared with the oracle, which computes only those rows
 (its row mask).  h must be at rounding level (one BF16 ulp, or 2^-10 of the

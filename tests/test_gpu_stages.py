@@ -117,9 +117,10 @@ STAGE_SHAPES = [
     (40, 768, 896, 8, 2),
     (12, 896, 768, 8, 2),
     (48, 4096, 256, 6, 2),
-    # 64 or more rows per expert: the 128-row tile kernels (INT8 weights with
-    # INT8 activations: 128-output gate/up workgroups that quantize h in their
-    # epilogue)
+    # 64 or more rows per expert: the big-tile kernels (BF16 activations:
+    # 64-row tiles, down in 256-column blocks, the last one half past H = 384;
+    # INT8 weights with INT8 activations: 128-output gate/up workgroups that
+    # quantize h in their epilogue)
     (260, 384, 256, 20, 8),
 ]
 
