@@ -445,7 +445,7 @@ struct Dec16 {
             // lanes (one DPP row; the xor-butterfly order)
             float t = 0.f;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) t += bf16_bits_to_f32(v[k][w] & 0xffffu) + bf16_bits_to_f32(v[k][w] >> 16);
+            for (int w = 0; w < 4; ++w) t = add_bf16x2(v[k][w], t);
             t = row16_sum(t);
             if (in && (c & 15) == 0) {
               xs_lds[(c >> 4) * 16 + r] = t;

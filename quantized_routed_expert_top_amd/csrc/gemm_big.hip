@@ -154,8 +154,7 @@ struct Big {
           // row sum of the group's 128 BF16 values: 8 per lane, 16 lanes per row
           float t = 0.f;
 #pragma unroll
-          for (int w = 0; w < 4; ++w)
-            t += bf16_bits_to_f32(v[k][w] & 0xffffu) + bf16_bits_to_f32(v[k][w] >> 16);
+          for (int w = 0; w < 4; ++w) t = add_bf16x2(v[k][w], t);
           t = row16_sum(t);                          // the 16 lanes of the row-group are one DPP row
           if (sc == 0) aux[r] = t;
         }

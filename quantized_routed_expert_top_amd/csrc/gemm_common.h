@@ -73,6 +73,13 @@ __device__ __forceinline__ float row16_sum(float t) {
   return t;
 }
 
+// t plus the two BF16 values packed in w: one v_dot2c_f32_bf16 against (1, 1).
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float t) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), __builtin_bit_cast(bf16x2_t, 0x3f803f80u), t,
+                                         false);
+}
+
 __device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
   return __half2float(__ushort_as_half((unsigned short)h));
 }
