@@ -189,8 +189,10 @@ struct Big {
     // prologue: group 0 staged, its weights in flight.  BF16 activations
     // with INT4 weights (registers to spare): the next group's weights are requested at the
     // start of each group, a whole group ahead; INT8 activations: after the
-    // group's last MFMA.
+    // group's last MFMA.  The next group's activation rows are requested at
+    // the start of each group too (BF16: both halves, 16 registers).
     constexpr bool kWAhead = !A8 && WB == 4;
+    constexpr bool kAEarly = NH == 2;
     WB_ wcur, wnxt;
     load_w(wcur, 0);
 #pragma unroll
@@ -206,9 +208,11 @@ struct Big {
       const int b = g & 1;
       const bool more = g + 1 < NG;
       // the next group's activations are in flight during this whole group
-      u32x4_t vn[QH];
-      float xsn[QH];
+      // (BF16: both halves requested here and staged after the last MFMA)
+      u32x4_t vn[QH], vn2[QH];
+      float xsn[QH], xsn2[QH];
       if (more) load_a(vn, xsn, g + 1, 0);
+      if (kAEarly && more) load_a(vn2, xsn2, g + 1, 1);
       if (kWAhead && more) load_w(wnxt, g + 1);
       const uint8_t* base = lds + b * STAGE;
       const float* aux = reinterpret_cast<const float*>(base + A_STAGE);
@@ -243,7 +247,7 @@ struct Big {
               part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bv[j]),
                                                                    t == 0 ? cinit[i] : part[i][j], 0, 0, 0);
           }
-          if (NH == 2 && t == STEPS / 2 - 1 && more) {   // first half staged, second half in flight
+          if (NH == 2 && !kAEarly && t == STEPS / 2 - 1 && more) {   // first half staged, second half in flight
             store_a(vn, xsn, b ^ 1, 0);
             load_a(vn, xsn, g + 1, NH - 1);
           }
@@ -292,7 +296,12 @@ struct Big {
             }
         }
       }
-      if (more) store_a(vn, xsn, b ^ 1, NH - 1);
+      if (kAEarly && more) {
+        store_a(vn, xsn, b ^ 1, 0);
+        store_a(vn2, xsn2, b ^ 1, 1);
+      } else if (more) {
+        store_a(vn, xsn, b ^ 1, NH - 1);
+      }
       if (kWAhead && more) wcur = wnxt;
       __syncthreads();
     }
