@@ -354,8 +354,11 @@ struct Big {
 // workgroup has 2 WN waves and 64 WN weight rows.  WN = 2: 128 weight rows,
 // two workgroups per CU; WN = 4: 256 weight rows, one workgroup per CU, which
 // loads 24 KB per stage where two narrow workgroups load 32 KB for the same
-// MFMA work.
-template <bool DUAL, int WN>
+// MFMA work.  CBW: consecutive column blocks of one row tile per workgroup,
+// walked with one stage ring (the activation rows, their scales and the
+// expert stay; the weight loads move by one column block), so the ring fills
+// once per CBW blocks; each block ends with its own epilogue.
+template <bool DUAL, int WN, int CBW = 1>
 struct BigW8A8 {
   static constexpr int NWAVE = 2 * WN, NT = 64 * NWAVE;
   static constexpr int BM = 128, BNW = 64 * WN;
@@ -377,8 +380,12 @@ struct BigW8A8 {
   __host__ __device__ static int ws16_part(int ng) { return (BNW / NHALF) * ng * 2; }
   __host__ __device__ static int ws16_pad(int ng) { return (ws16_part(ng) + 1023) / 1024 * 1024; }
   // the stages, then the scales of every group: activations [group][row] and
-  // weights [group][weight row], both FP32
-  __host__ __device__ static size_t lds_bytes(int ng) { return NS * (size_t)STAGE + (size_t)ng * (BM + BNW) * 4; }
+  // weights [column block][group][weight row], both FP32; then the row maxima
+  // of the h quantizer
+  static constexpr int RED_BYTES = BM * WN * 4;
+  __host__ __device__ static size_t lds_bytes(int ng) {
+    return NS * (size_t)STAGE + (size_t)ng * (BM + CBW * BNW) * 4 + RED_BYTES;
+  }
 
   __device__ static uint32_t chunk_pos(int row, int chunk) {
     return (uint32_t)(row * HB + ((chunk ^ ((row >> 1) & 3)) << 4));
@@ -386,7 +393,7 @@ struct BigW8A8 {
   // the FP16 weight-scale copy of ng groups fits the fourth stage and every
   // group's FP32 scales fit beside the stages
   __host__ __device__ static bool fits(int ng) {
-    return ng <= kMaxGroups && NHALF * ws16_pad(ng) <= STAGE && lds_bytes(ng) <= 160 * 1024;
+    return ng <= kMaxGroups && CBW * NHALF * ws16_pad(ng) <= STAGE && lds_bytes(ng) <= 160 * 1024;
   }
   // first tile row of the wave's weight tile j (DUAL: j < 2 gate rows, j >= 2
   // the same columns' up rows, HW further on)
@@ -398,8 +405,9 @@ struct BigW8A8 {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     const int NG = p.kdim / kGroup;
-    const int NH = 2 * NG;                          // stages of this tile
-    const int n0 = cb * BNO;
+    const int NH = 2 * NG;                          // stages of one column block
+    const int NHP = (NH + 3) & ~3;                  // ... in whole rounds of four
+    const int n0 = cb * CBW * BNO;                  // first column block of the workgroup
     const int64_t mat_bytes = (int64_t)p.n * NG * kGroup;
     const rsrc_t rw0 = make_rsrc(p.w0q + e * mat_bytes, mat_bytes);
     const rsrc_t rw1 = DUAL ? make_rsrc(p.w1q + e * mat_bytes, mat_bytes) : rw0;
@@ -427,6 +435,7 @@ struct BigW8A8 {
     auto lds3 = [&](int off) { return (__attribute__((address_space(3))) void*)(lds + off); };
 
     const int XS_OFF = NS * STAGE, WS_OFF = XS_OFF + NG * BM * 4, WS16_OFF = (NS - 1) * STAGE;
+    const int RED_OFF = WS_OFF + NG * CBW * BNW * 4;
     const int wpart = ws16_part(NG), wpad = ws16_pad(NG), nkb = wpad / 1024;
     // the tile's scales of every group, before the first stage's loads.
     // Activation scales: load q (of 2 NG, four bytes a lane) is group q / 2,
@@ -439,27 +448,32 @@ struct BigW8A8 {
       const uint32_t off = r < nrows ? (uint32_t)((src(r) * NG + (q >> 1)) * 4) : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lds3(XS_OFF + ((q >> 1) * BM + (q & 1) * 64) * 4), 4, off, 0, 0, 0);
     }
-    for (int q = wave; q < NHALF * nkb; q += NWAVE) {   // uniform
-      const int part = q / nkb, b = (q - part * nkb) * 1024 + 16 * lane;
-      const uint32_t off = b < wpart ? (uint32_t)(n0 * NG * 2 + b) : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(DUAL && part == 1 ? rs1 : rs0, lds3(WS16_OFF + part * wpad + (q - part * nkb) * 1024),
+    for (int q = wave; q < CBW * NHALF * nkb; q += NWAVE) {   // uniform
+      const int cp = q / nkb, c = cp / NHALF, part = cp - c * NHALF, b = (q - cp * nkb) * 1024 + 16 * lane;
+      const uint32_t off = b < wpart ? (uint32_t)((n0 + c * BNO) * NG * 2 + b) : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(DUAL && part == 1 ? rs1 : rs0, lds3(WS16_OFF + cp * wpad + (q - cp * nkb) * 1024),
                                                16, off, 0, 0, 0);
     }
-    // stage loads of half-group h into stage st; past the reduction's end
-    // (the last round) the same loads with an out-of-range offset, so that
-    // every stage keeps the same count
-    auto issue = [&](int h, auto stc) {
+    // stage loads of ring stage hg (column block hg / NHP, half-group
+    // hg % NHP) into stage st; past the reduction's end (the last round of a
+    // block, or past the last block) the same loads with an out-of-range
+    // offset, so that every stage keeps the same count.  The weights of
+    // column block c sit c * BNO rows further on: a scalar offset, every
+    // block's rows lying inside the matrix.
+    auto issue = [&](int hg, auto stc) {
       constexpr int st = decltype(stc)::value;
       const int base = st * STAGE;
-      if (h < NH) {                                  // uniform
+      const int c = CBW == 1 ? 0 : hg / NHP, h = hg - c * NHP;
+      if (c < CBW && h < NH) {                       // uniform
         const uint32_t koff = (uint32_t)((h >> 1) * kGroup + (h & 1) * 16);
+        const uint32_t kwoff = koff + (uint32_t)(c * BNO * NG * kGroup);
 #pragma unroll
         for (int q = 0; q < QA; ++q)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds3(base + (q * NWAVE + wave) * 1024), 16, a_off[q], koff, 0, 0);
 #pragma unroll
         for (int q = 0; q < QB; ++q)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(DUAL && q == 1 ? rw1 : rw0, lds3(base + B_OFF + (q * NWAVE + wave) * 1024),
-                                                   16, b_off[q], koff, 0, 0);
+                                                   16, b_off[q], kwoff, 0, 0);
       } else {
 #pragma unroll
         for (int q = 0; q < QA; ++q)
@@ -480,10 +494,12 @@ struct BigW8A8 {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();                            // and every thread's
     asm volatile("" ::: "memory");
-    for (int idx = tid; idx < BNW * NG; idx += NT) {
-      const int g = idx / BNW, n = idx - g * BNW;
+    for (int idx = tid; idx < CBW * BNW * NG; idx += NT) {
+      const int c = idx / (BNW * NG), rem = idx - c * (BNW * NG);
+      const int g = rem / BNW, n = rem - g * BNW;
       const int part = DUAL ? n / HW : 0, nr = DUAL ? n % HW : n;
-      const uint16_t w = *reinterpret_cast<const uint16_t*>(lds + WS16_OFF + part * wpad + (nr * NG + g) * 2);
+      const uint16_t w =
+          *reinterpret_cast<const uint16_t*>(lds + WS16_OFF + (c * NHALF + part) * wpad + (nr * NG + g) * 2);
       *reinterpret_cast<float*>(lds + WS_OFF + idx * 4) = half_bits_to_f32(w);
     }
 
@@ -501,22 +517,23 @@ struct BigW8A8 {
     f32x4_t wsv[TN];
 
     // one stage: wait for it, refill the stage read last time, compute
-    auto body = [&](int h, auto stc) {
+    auto body = [&](int hg, auto stc) {
       constexpr int st = decltype(stc)::value;
+      const int c = CBW == 1 ? 0 : hg / NHP, h = hg - c * NHP;
       constexpr int t = st & 1;                      // stage index and half agree (NS even)
       __builtin_amdgcn_s_waitcnt(vmcnt_enc((NS - 2) * VM));   // this thread's loads of stage h landed
       __builtin_amdgcn_s_waitcnt(kLgkmcnt0);                   // and its LDS reads of stage h - 1 completed
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();                  // every thread's; stage h - 1 may be refilled
       asm volatile("" ::: "memory");
-      issue(h + NS - 1, std::integral_constant<int, (st + NS - 1) % NS>{});
+      issue(hg + NS - 1, std::integral_constant<int, (st + NS - 1) % NS>{});
       const uint8_t* base = lds + st * STAGE;
       if constexpr (t == 0) {
         // a group past the reduction (the last round's): zero operands, zero scales
         const bool gin = (h >> 1) < NG;
         const int g = gin ? h >> 1 : NG - 1;
         const float* xsl = reinterpret_cast<const float*>(lds + XS_OFF) + g * BM + wm * 64 + li;
-        const float* wsl = reinterpret_cast<const float*>(lds + WS_OFF) + g * BNW + 4 * kb;
+        const float* wsl = reinterpret_cast<const float*>(lds + WS_OFF) + (c * NG + g) * BNW + 4 * kb;
 #pragma unroll
         for (int i = 0; i < TM; ++i) xsv[i] = gin ? xsl[i * 16] : 0.f;
 #pragma unroll
@@ -549,45 +566,60 @@ struct BigW8A8 {
 
     // whole rounds of four stages: with an odd group count the last group is
     // a no-op one (zero operands, zero scales), which keeps every round the
-    // same straight-line code and every wait count static
-    for (int h = 0; h < NH; h += 4) {
-      body(h, std::integral_constant<int, 0>{});
-      body(h + 1, std::integral_constant<int, 1>{});
-      body(h + 2, std::integral_constant<int, 2>{});
-      body(h + 3, std::integral_constant<int, 3>{});
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));        // no load into LDS outlives the workgroup
-
-    // lane: activation row wm*64 + 16 i + li, output columns 4 kb .. 4 kb + 3
-    // of each 16-column tile
+    // same straight-line code and every wait count static.  A column block's
+    // epilogue runs between its last round and the next block's first, with
+    // the next block's first stages already in flight.
     uint16_t* out = static_cast<uint16_t*>(p.out);
-    if constexpr (DUAL && BNO == kGroup) {
-      if (p.hq) {
-        quantize_h_epilogue(p, cb, row0, nrows, acc, lds);
-        if (!out) return;
+    for (int c = 0; c < CBW; ++c) {
+      for (int h = 0; h < NHP; h += 4) {
+        const int hg = c * NHP + h;
+        body(hg, std::integral_constant<int, 0>{});
+        body(hg + 1, std::integral_constant<int, 1>{});
+        body(hg + 2, std::integral_constant<int, 2>{});
+        body(hg + 3, std::integral_constant<int, 3>{});
       }
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int m = wm * 64 + i * 16 + li;
-      if (m < nrows) {
-        uint16_t* orow = out + (int64_t)(row0 + m) * p.n + n0 + 4 * kb;
-        if constexpr (DUAL) {
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            float hv[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) hv[v] = silu(acc[i][j][v]) * acc[i][j + 2][v];
-            *reinterpret_cast<uint2*>(orow + wn * 32 + j * 16) = uint2{pack2_bf16(hv[0], hv[1]), pack2_bf16(hv[2], hv[3])};
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            *reinterpret_cast<uint2*>(orow + wn * 64 + j * 16) =
-                uint2{pack2_bf16(acc[i][j][0], acc[i][j][1]), pack2_bf16(acc[i][j][2], acc[i][j][3])};
+      // lane: activation row wm*64 + 16 i + li, output columns 4 kb .. 4 kb + 3
+      // of each 16-column tile
+      const int cbc = cb * CBW + c, n0c = cbc * BNO;
+      bool h_out = true;
+      if constexpr (DUAL && BNO == kGroup) {
+        if (p.hq) {
+          quantize_h_epilogue(p, cbc, row0, nrows, acc, reinterpret_cast<float*>(lds + RED_OFF));
+          h_out = out != nullptr;
         }
       }
+      if (h_out) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int m = wm * 64 + i * 16 + li;
+          if (m < nrows) {
+            uint16_t* orow = out + (int64_t)(row0 + m) * p.n + n0c + 4 * kb;
+            if constexpr (DUAL) {
+#pragma unroll
+              for (int j = 0; j < 2; ++j) {
+                float hv[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) hv[v] = silu(acc[i][j][v]) * acc[i][j + 2][v];
+                *reinterpret_cast<uint2*>(orow + wn * 32 + j * 16) =
+                    uint2{pack2_bf16(hv[0], hv[1]), pack2_bf16(hv[2], hv[3])};
+              }
+            } else {
+#pragma unroll
+              for (int j = 0; j < TN; ++j)
+                *reinterpret_cast<uint2*>(orow + wn * 64 + j * 16) =
+                    uint2{pack2_bf16(acc[i][j][0], acc[i][j][1]), pack2_bf16(acc[i][j][2], acc[i][j][3])};
+            }
+          }
+        }
+      }
+      if (c + 1 < CBW) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));        // no load into LDS outlives the workgroup
   }
 
   // h quantized per 128 values, as the INT8 quantizer does it for the BF16 h
@@ -595,13 +627,13 @@ struct BigW8A8 {
   // group maximum of |h| over the lane's eight values, the four 16-lane
   // segments (xor 16, 32) and the four waves along the columns (LDS), then
   // s = max / 127 and the codes of the BF16 values.  hq int8 [rows][n],
-  // hs fp32 [rows][n / 128].
+  // hs fp32 [rows][n / 128].  red: LDS of BM * WN floats apart from the
+  // stages (the ring may be filling them).
   __device__ static void quantize_h_epilogue(const GemmProblem& p, int cb, int row0, int nrows,
-                                             const f32x4_t (&acc)[TM][TN], uint8_t* lds) {
+                                             const f32x4_t (&acc)[TM][TN], float* red) {
     const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, kb = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
-    float* red = reinterpret_cast<float*>(lds);            // [BM][WN]: every wave is past its last stage
     float hb[TM][2][4];
     float mx[TM];
 #pragma unroll
@@ -622,7 +654,7 @@ struct BigW8A8 {
       m = fmaxf(m, __shfl_xor(m, 32));
       mx[i] = m;
     }
-    __syncthreads();                                       // every wave's last stage reads are done
+    __syncthreads();                                       // every wave's reads of red (previous block) are done
     if (kb == 0) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) red[(wm * 64 + i * 16 + li) * WN + wn] = mx[i];
@@ -657,9 +689,9 @@ struct BigW8A8 {
   }
 };
 
-template <bool DUAL, int WN>
+template <bool DUAL, int WN, int CBW>
 __global__ __launch_bounds__(128 * WN, (WN == 2) ? 2 : 1) void k_gemm_w8a8(GemmProblem p) {
-  using K = BigW8A8<DUAL, WN>;
+  using K = BigW8A8<DUAL, WN, CBW>;
   extern __shared__ __attribute__((aligned(16))) uint8_t big_lds[];
   int tile, cb;
   if (!xcd_tile(p, tile, cb)) return;
@@ -687,13 +719,28 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmProblem p) {
     K::run(p, cb, td.e, row0, td.nrows, [&](int r) { return (int64_t)(row0 + r); }, big_lds);
 }
 
-template <bool DUAL, int WN>
+template <bool DUAL, int WN, int CBW>
 hipError_t launch_w8a8_wn(const GemmProblem& p, hipStream_t stream) {
-  using K = BigW8A8<DUAL, WN>;
-  const dim3 grid(p.n / K::BNO, (unsigned)((p.max_tiles + 7) / 8 * 8));
-  hipLaunchKernelGGL((k_gemm_w8a8<DUAL, WN>), grid, dim3(K::NT), K::lds_bytes(p.kdim / kGroup), stream, p);
+  using K = BigW8A8<DUAL, WN, CBW>;
+  const dim3 grid(p.n / (K::BNO * CBW), (unsigned)((p.max_tiles + 7) / 8 * 8));
+  hipLaunchKernelGGL((k_gemm_w8a8<DUAL, WN, CBW>), grid, dim3(K::NT), K::lds_bytes(p.kdim / kGroup), stream, p);
   return hipGetLastError();
 }
+
+// Column blocks per workgroup: as many as the width (whole groups of them)
+// and the LDS allow, up to C.
+template <bool DUAL, int WN, int C>
+hipError_t launch_w8a8_cbw(const GemmProblem& p, hipStream_t stream) {
+  using K = BigW8A8<DUAL, WN, C>;
+  if constexpr (C > 1) {
+    if (p.n % (K::BNO * C) != 0 || !K::fits(p.kdim / kGroup)) return launch_w8a8_cbw<DUAL, WN, C / 2>(p, stream);
+  }
+  return launch_w8a8_wn<DUAL, WN, C>(p, stream);
+}
+
+// Column blocks per workgroup: four for the down GEMM (its reduction is short,
+// so the ring's fill is a large part of one block), two for gate/up.
+constexpr int kGateUpCbw = 2, kDownCbw = 4;
 
 // Gate/up: the wide workgroup (128 outputs, one quantization group of h)
 // when the output width and the reduction allow it; it alone can quantize h
@@ -705,10 +752,10 @@ hipError_t launch_w8a8_cfg(const GemmProblem& p, hipStream_t stream) {
   const int ng = p.kdim / kGroup;
   if constexpr (DUAL) {
     using Wd = BigW8A8<true, 4>;
-    if (p.n % Wd::BNO == 0 && Wd::fits(ng)) return launch_w8a8_wn<true, 4>(p, stream);
+    if (p.n % Wd::BNO == 0 && Wd::fits(ng)) return launch_w8a8_cbw<true, 4, kGateUpCbw>(p, stream);
   }
   if (p.hq || p.n % Nw::BNO != 0 || !Nw::fits(ng)) return hipErrorInvalidValue;
-  return launch_w8a8_wn<DUAL, 2>(p, stream);
+  return launch_w8a8_cbw<DUAL, 2, DUAL ? 1 : kDownCbw>(p, stream);
 }
 
 template <int WB, bool A8, bool DUAL, int WM>

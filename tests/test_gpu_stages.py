@@ -122,6 +122,9 @@ STAGE_SHAPES = [
     # INT8 weights with INT8 activations: 128-output gate/up workgroups that
     # quantize h in their epilogue)
     (260, 384, 256, 20, 8),
+    # the same kernels with a 512-wide down GEMM: INT8 activations walk its
+    # four 128-column blocks in one workgroup (ragged row tiles)
+    (200, 512, 256, 12, 6),
 ]
 
 
