@@ -76,6 +76,8 @@ struct Big {
 
   __device__ static uint32_t lds_chunk(int row, int chunk) { return (uint32_t)(row * GB + ((chunk ^ swz(row)) << 4)); }
 
+  static constexpr float kOff = (WB == 4) ? 136.0f : 128.0f;   // BF16 operand offset of the codes
+
   // tile: rows [row0, row0 + nrows) of expert e; src(r) = A row of local row r
   template <class RowSrc>
   __device__ static void run(const GemmProblem& p, int cb, int e, int row0, int nrows, RowSrc src, uint8_t* lds) {
@@ -156,7 +158,7 @@ struct Big {
 #pragma unroll
           for (int w = 0; w < 4; ++w) t = add_bf16x2(v[k][w], t);
           t = row16_sum(t);                          // the 16 lanes of the row-group are one DPP row
-          if (sc == 0) aux[r] = t;
+          if (sc == 0) aux[r] = -kOff * t;           // the C operand of the group's first MFMA
         }
       }
     };
@@ -220,16 +222,13 @@ struct Big {
 #pragma unroll
       for (int j = 0; j < TN; ++j) ws[j] = half_bits_to_f32(wcur.s[j]);
       if constexpr (!A8) {
-        // the group's sums start from -offset * (row sum), so they leave the
-        // MFMAs without the 136 + q / 128 + q offset
-        constexpr float kOff = (WB == 4) ? 136.0f : 128.0f;
+        // the group's sums start from -offset * (row sum) (staged that way),
+        // so they leave the MFMAs without the 136 + q / 128 + q offset
         f32x4_t cinit[TM];
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           if (i >= live) continue;
-          const f32x4_t rsum = *reinterpret_cast<const f32x4_t*>(aux + wm * 64 + i * 16 + 4 * kb);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) cinit[i][v] = -kOff * rsum[v];
+          cinit[i] = *reinterpret_cast<const f32x4_t*>(aux + wm * 64 + i * 16 + 4 * kb);
         }
         f32x4_t part[TM][TN];
 #pragma unroll
