@@ -514,6 +514,11 @@ struct BigW8A8 {
     i32x4_t part[TM][TN];
     float xsv[TM];
     f32x4_t wsv[TN];
+    // a group's FP32 combination: acc += float(isum) * (xs * ws)
+    auto combine = [&](int i, int j) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = __builtin_fmaf((float)part[i][j][v], xsv[i] * wsv[j][v], acc[i][j][v]);
+    };
 
     // one stage: wait for it, refill the stage read last time, compute
     auto body = [&](int hg, auto stc) {
@@ -527,8 +532,24 @@ struct BigW8A8 {
       asm volatile("" ::: "memory");
       issue(hg + NS - 1, std::integral_constant<int, (st + NS - 1) % NS>{});
       const uint8_t* base = lds + st * STAGE;
+      u32x4_t bv[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int nj = DUAL ? ((j >> 1) * HW + (j & 1) * 16) : j * 16;   // DUAL: up rows start at HW
+        bv[j] = *reinterpret_cast<const u32x4_t*>(base + B_OFF + b_rd + nj * HB);
+      }
       if constexpr (t == 0) {
-        // a group past the reduction (the last round's): zero operands, zero scales
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const i32x4_t av = __builtin_bit_cast(i32x4_t, *reinterpret_cast<const u32x4_t*>(base + a_rd + i * 16 * HB));
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            part[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, bv[j]), av,
+                                                               i32x4_t{0, 0, 0, 0}, 0, 0, 0);
+        }
+        // this group's scales, for its combination after the second half (a
+        // group past the reduction, the last round's: zero operands, zero
+        // scales)
         const bool gin = (h >> 1) < NG;
         const int g = gin ? h >> 1 : NG - 1;
         const float* xsl = reinterpret_cast<const float*>(lds + XS_OFF) + g * BM + wm * 64 + li;
@@ -537,29 +558,18 @@ struct BigW8A8 {
         for (int i = 0; i < TM; ++i) xsv[i] = gin ? xsl[i * 16] : 0.f;
 #pragma unroll
         for (int j = 0; j < TN; ++j) wsv[j] = *reinterpret_cast<const f32x4_t*>(wsl + wrow0(wn, j));
-      }
-      u32x4_t bv[TN];
+      } else {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int nj = DUAL ? ((j >> 1) * HW + (j & 1) * 16) : j * 16;   // DUAL: up rows start at HW
-        bv[j] = *reinterpret_cast<const u32x4_t*>(base + B_OFF + b_rd + nj * HB);
-      }
+        for (int i = 0; i < TM; ++i) {
+          const i32x4_t av = __builtin_bit_cast(i32x4_t, *reinterpret_cast<const u32x4_t*>(base + a_rd + i * 16 * HB));
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const i32x4_t av = __builtin_bit_cast(i32x4_t, *reinterpret_cast<const u32x4_t*>(base + a_rd + i * 16 * HB));
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          part[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, bv[j]), av,
-                                                             t == 0 ? i32x4_t{0, 0, 0, 0} : part[i][j], 0, 0, 0);
-      }
-      if constexpr (t == 1) {
+          for (int j = 0; j < TN; ++j)
+            part[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, bv[j]), av, part[i][j], 0, 0, 0);
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              acc[i][j][v] = __builtin_fmaf((float)part[i][j][v], xsv[i] * wsv[j][v], acc[i][j][v]);
+          for (int j = 0; j < TN; ++j) combine(i, j);
       }
     };
 
