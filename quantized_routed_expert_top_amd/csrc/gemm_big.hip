@@ -17,10 +17,10 @@
 //  * the reduction is walked one 128-group at a time: the group's activation
 //    rows are staged into LDS (double-buffered, XOR-swizzled 16-byte chunks,
 //    already permuted into the operand order), together with one FP32 per row
-//    (the activation scale for INT8 activations, the row sum that removes the
-//    136 + q / 128 + q offset for BF16 activations); each wave loads its own
-//    weight columns straight into registers (16-byte buffer loads, next group
-//    in flight while the current one computes);
+//    (the activation scale for INT8 activations; for BF16 activations the
+//    row sum times -136 / -128, which removes the 136 + q / 128 + q offset);
+//    each wave loads its own weight columns straight into registers (16-byte
+//    buffer loads, next group in flight while the current one computes);
 //  * per group: MFMAs into a per-group accumulator, then one FP32 update of
 //    the running sums (INT8: acc += float(isum) * (xs * ws); BF16: the
 //    group's MFMAs start from -offset * rowsum, then acc += ws * gsum), one
