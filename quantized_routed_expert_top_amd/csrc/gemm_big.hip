@@ -204,6 +204,16 @@ struct Big {
       load_a(v, xs, 0, h);
       store_a(v, xs, 0, h);
     }
+    // BF16 activations with the weight look-ahead: the next group's loads go
+    // out before the barrier that opens a group (not after it)
+    constexpr bool kEarlyIssue = kAEarly && kWAhead;
+    u32x4_t vn[QH], vn2[QH];
+    float xsn[QH], xsn2[QH];
+    if (kEarlyIssue && NG > 1) {
+      load_a(vn, xsn, 1, 0);
+      load_a(vn2, xsn2, 1, 1);
+      load_w(wnxt, 1);
+    }
     __syncthreads();
 
     for (int g = 0; g < NG; ++g) {
@@ -211,11 +221,9 @@ struct Big {
       const bool more = g + 1 < NG;
       // the next group's activations are in flight during this whole group
       // (BF16: both halves requested here and staged after the last MFMA)
-      u32x4_t vn[QH], vn2[QH];
-      float xsn[QH], xsn2[QH];
-      if (more) load_a(vn, xsn, g + 1, 0);
-      if (kAEarly && more) load_a(vn2, xsn2, g + 1, 1);
-      if (kWAhead && more) load_w(wnxt, g + 1);
+      if (!kEarlyIssue && more) load_a(vn, xsn, g + 1, 0);
+      if (!kEarlyIssue && kAEarly && more) load_a(vn2, xsn2, g + 1, 1);
+      if (!kEarlyIssue && kWAhead && more) load_w(wnxt, g + 1);
       const uint8_t* base = lds + b * STAGE;
       const float* aux = reinterpret_cast<const float*>(base + A_STAGE);
       float ws[TN];
@@ -302,6 +310,11 @@ struct Big {
         store_a(vn, xsn, b ^ 1, NH - 1);
       }
       if (kWAhead && more) wcur = wnxt;
+      if (kEarlyIssue && g + 2 < NG) {
+        load_a(vn, xsn, g + 2, 0);
+        load_a(vn2, xsn2, g + 2, 1);
+        load_w(wnxt, g + 2);
+      }
       __syncthreads();
     }
 
