@@ -85,9 +85,22 @@ __global__ __launch_bounds__(NW * kWave) void k_route_small(const int32_t* __res
                   tiles_b, ntiles_b, bm_b);
 }
 
+// Rows [r0, r1) of the INT8 quantization of x by workgroup blk of nblk.
+__device__ __forceinline__ void quantize_x_rows(const QuantX& qx, int r0, int r1, int blk, int nblk) {
+  const int G = qx.cols / kGroup;
+  quantize_act_groups(qx.v + (int64_t)r0 * qx.cols, (int64_t)(r1 - r0) * G, G, qx.q + (int64_t)r0 * qx.cols,
+                      qx.s + (int64_t)r0 * G, blk, nblk);
+}
+
 // Three-kernel path.  ghist[gw][E]: per-wave counts, then per-wave bases.
+// The workgroups past the first nroute of each launch quantize a third of
+// the rows of x (qx.rows == 0: none), which no routing step reads.
 __global__ __launch_bounds__(256) void k_route_count(const int32_t* __restrict__ ids, int S, int E, int nbits,
-                                                     int32_t* ghist) {
+                                                     int32_t* ghist, int nroute, QuantX qx) {
+  if ((int)blockIdx.x >= nroute) {
+    quantize_x_rows(qx, 0, qx.rows / 3, (int)blockIdx.x - nroute, (int)gridDim.x - nroute);
+    return;
+  }
   extern __shared__ int lds[];
   const int w = threadIdx.x / kWave;
   int* row = lds + w * E;
@@ -107,7 +120,12 @@ __global__ __launch_bounds__(256) void k_route_count(const int32_t* __restrict__
 // partition, the partition sums are scanned in LDS, pass 2 rewrites the counts
 // as bases.
 constexpr int kPxE = 32, kPxP = 8;   // experts x partitions = 256 threads
-__global__ __launch_bounds__(256) void k_route_prefix(int32_t* ghist, int nwaves, int E, int32_t* counts) {
+__global__ __launch_bounds__(256) void k_route_prefix(int32_t* ghist, int nwaves, int E, int32_t* counts, int nroute,
+                                                      QuantX qx) {
+  if ((int)blockIdx.x >= nroute) {
+    quantize_x_rows(qx, qx.rows / 3, 2 * (qx.rows / 3), (int)blockIdx.x - nroute, (int)gridDim.x - nroute);
+    return;
+  }
   __shared__ int part[kPxP][kPxE];
   const int el = threadIdx.x % kPxE, q = threadIdx.x / kPxE;
   const int e = blockIdx.x * kPxE + el;
@@ -217,9 +235,7 @@ __global__ __launch_bounds__(256) void k_route_scatter_qx(const int32_t* __restr
                   bm_b, sorted_slot, slot_row, blockIdx.x, nscatter);
     return;
   }
-  const int G = qx.cols / kGroup;
-  quantize_act_groups(qx.v, (int64_t)qx.rows * G, G, qx.q, qx.s, (int)blockIdx.x - nscatter,
-                      (int)gridDim.x - nscatter);
+  quantize_x_rows(qx, 2 * (qx.rows / 3), qx.rows, (int)blockIdx.x - nscatter, (int)gridDim.x - nscatter);
 }
 
 __global__ __launch_bounds__(256) void k_build_tiles(const int32_t* offsets, int E, Tile* tiles_a,
@@ -282,21 +298,27 @@ hipError_t launch_route(const int32_t* ids, int T, int K, int E, int32_t* counts
   int32_t* ghist = static_cast<int32_t*>(ws);
   const int64_t nwaves = (S + kLargeChunk - 1) / kLargeChunk;
   const int nblocks = (int)((nwaves + 3) / 4);
-  hipLaunchKernelGGL(k_route_count, dim3(nblocks), dim3(256), sizeof(int) * 4 * E, stream, ids, (int)S, E, nbits,
-                     ghist);
+  // the quantization of x, a third of its rows in each of the three launches
+  const QuantX none = {nullptr, 0, kGroup, nullptr, nullptr};
+  const QuantX q3 = (qx && qx->rows > 0) ? *qx : none;
+  auto qblocks = [&](int r0, int r1) -> int64_t {
+    const int64_t ngroups = (int64_t)(r1 - r0) * (q3.cols / kGroup);
+    return std::min((ngroups + 15) / 16, kMaxQuantBlocks);
+  };
+  const int npx = (E + kPxE - 1) / kPxE;
+  hipLaunchKernelGGL(k_route_count, dim3((unsigned)(nblocks + qblocks(0, q3.rows / 3))), dim3(256),
+                     sizeof(int) * 4 * E, stream, ids, (int)S, E, nbits, ghist, nblocks, q3);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_route_prefix, dim3((unsigned)((E + kPxE - 1) / kPxE)), dim3(256), 0, stream, ghist, nblocks * 4, E,
-                     counts);
+  hipLaunchKernelGGL(k_route_prefix, dim3((unsigned)(npx + qblocks(q3.rows / 3, 2 * (q3.rows / 3)))), dim3(256), 0,
+                     stream, ghist, nblocks * 4, E, counts, npx, q3);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const size_t slds = sizeof(int) * (size_t)(7 * E + 5);
-  if (qx && qx->rows > 0) {
-    const int64_t ngroups = (int64_t)qx->rows * (qx->cols / kGroup);
-    const int64_t qblocks = std::min((ngroups + 15) / 16, kMaxQuantBlocks);
-    hipLaunchKernelGGL(k_route_scatter_qx, dim3((unsigned)(nblocks + qblocks)), dim3(256), slds, stream, ids, (int)S, E,
-                       nbits, ghist, counts, offsets, dropped, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b,
-                       sorted_slot, slot_row, nblocks, *qx);
+  if (q3.rows > 0) {
+    hipLaunchKernelGGL(k_route_scatter_qx, dim3((unsigned)(nblocks + qblocks(2 * (q3.rows / 3), q3.rows))), dim3(256),
+                       slds, stream, ids, (int)S, E, nbits, ghist, counts, offsets, dropped, tiles_a, ntiles_a, bm_a,
+                       tiles_b, ntiles_b, bm_b, sorted_slot, slot_row, nblocks, q3);
   } else {
     hipLaunchKernelGGL(k_route_scatter, dim3(nblocks), dim3(256), slds, stream, ids, (int)S, E, nbits, ghist, counts,
                        offsets, dropped, tiles_a, ntiles_a, bm_a, tiles_b, ntiles_b, bm_b, sorted_slot, slot_row);
