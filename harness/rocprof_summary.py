@@ -4,7 +4,7 @@
     python -m harness.rocprof_summary counters DIR [--kernel SUBSTR] [--dispatches]
 
 `kernels` prints, per kernel name, the number of dispatches and the average,
-minimum, maximum and total duration (from a --kernel-trace run); `counters`
+median, minimum, maximum and total duration (from a --kernel-trace run); `counters`
 prints, per kernel and counter, the mean value per dispatch (from a --pmc
 run), and with --dispatches every dispatch's value in dispatch order (to tell
 apart launches of one kernel with different sizes, such as the copies of a
@@ -28,16 +28,22 @@ def _dbs(d: str) -> list[str]:
     return paths
 
 
-def kernel_stats(d: str) -> list[tuple[str, int, float, float, float, float]]:
-    """(name, calls, avg_us, min_us, max_us, total_us), largest total first."""
+def _median(v: list[float]) -> float:
+    s = sorted(v)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def kernel_stats(d: str) -> list[tuple[str, int, float, float, float, float, float]]:
+    """(name, calls, avg_us, median_us, min_us, max_us, total_us), largest total first."""
     acc: dict[str, list[float]] = collections.defaultdict(list)
     for path in _dbs(d):
         con = sqlite3.connect(path)
         for name, dur in con.execute("select name, end - start from kernels"):
             acc[name].append(dur / 1000.0)
         con.close()
-    rows = [(n, len(v), sum(v) / len(v), min(v), max(v), sum(v)) for n, v in acc.items()]
-    rows.sort(key=lambda r: -r[5])
+    rows = [(n, len(v), sum(v) / len(v), _median(v), min(v), max(v), sum(v)) for n, v in acc.items()]
+    rows.sort(key=lambda r: -r[6])
     return rows
 
 
@@ -78,9 +84,9 @@ def main(argv=None) -> int:
     ap.add_argument("--dispatches", action="store_true")
     a = ap.parse_args(argv)
     if a.what == "kernels":
-        print(f"{'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'total_us':>11}  kernel")
-        for n, c, avg, mn, mx, tot in kernel_stats(a.dir)[: a.top]:
-            print(f"{c:6d} {avg:9.2f} {mn:9.2f} {mx:9.2f} {tot:11.1f}  {n}")
+        print(f"{'calls':>6} {'avg_us':>9} {'med_us':>9} {'min_us':>9} {'max_us':>9} {'total_us':>11}  kernel")
+        for n, c, avg, med, mn, mx, tot in kernel_stats(a.dir)[: a.top]:
+            print(f"{c:6d} {avg:9.2f} {med:9.2f} {mn:9.2f} {mx:9.2f} {tot:11.1f}  {n}")
     elif a.dispatches:
         for k, c, i, v in counter_dispatches(a.dir, a.kernel):
             print(f"{i:8d} {c:16s} {v:16.1f}  {k}")

@@ -137,11 +137,15 @@ int qre_moe_forward_noalloc(const qre_desc* desc, const void* x, const int32_t* 
                             const float* topk_w, const qre_weights* weights, void* out,
                             qre_stream_t stream);
 
-/* qre_moe_forward that also records events[i] (each a hipEvent_t created by the
- * caller, or NULL to skip it) on `stream` between its steps: [0] before the
- * permutation, [1] before the gate/up GEMM, [2] after it, [3] before the down
- * GEMM, [4] after it, [5] after the combine.  The kernels are the same as
- * qre_moe_forward's; this is a measurement aid (six event records per call). */
+/* qre_moe_forward that also records events[i] (host array of eight, each a
+ * hipEvent_t created by the caller, or NULL to skip it) on `stream` between
+ * its steps: [0] before the permutation, [1] before the gate/up GEMM, [2]
+ * after it, [3] before the down GEMM, [4] after it, [5] after the combine;
+ * [6] and [7] are handed to the launch of the gate/up GEMM kernel itself
+ * (hipExtLaunchKernelGGL), so they hold that dispatch's own begin and end,
+ * the interval a kernel trace reports, without the cost of an event record
+ * in between.  The kernels are the same as qre_moe_forward's; this is a
+ * measurement aid. */
 int qre_moe_forward_timed(const qre_desc* desc, const void* x, const int32_t* topk_ids,
                           const float* topk_w, const qre_weights* weights, void* out,
                           void* workspace, size_t workspace_bytes, void* const* events,
@@ -352,10 +356,12 @@ int qre_nvfp4_moe_forward(const qre_desc* desc, const void* x, const int32_t* to
                           const qre_nvfp4_weights* weights, void* out, void* workspace, size_t workspace_bytes,
                           qre_stream_t stream);
 
-/* Measurement aid: qre_nvfp4_moe_forward that also records six caller-created
- * hipEvent_t (events[0..5], host array; NULL entries skipped) on `stream`:
- * before the routing, after the routing and the quantization of x, after
- * gate/up, after the quantization of h, after down, after the combine. */
+/* Measurement aid: qre_nvfp4_moe_forward that also records caller-created
+ * hipEvent_t (events[0..7], host array of eight; NULL entries skipped) on
+ * `stream`: [0..5] before the routing, after the routing and the quantization
+ * of x, after gate/up, after the quantization of h, after down, after the
+ * combine; [6] and [7] the begin and end of the gate/up GEMM dispatch itself
+ * (as for qre_moe_forward_timed). */
 int qre_nvfp4_moe_forward_timed(const qre_desc* desc, const void* x, const int32_t* topk_ids, const float* topk_w,
                                 const qre_nvfp4_weights* weights, void* out, void* workspace, size_t workspace_bytes,
                                 void* const* events, qre_stream_t stream);

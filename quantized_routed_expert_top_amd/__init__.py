@@ -230,21 +230,22 @@ def moe_forward(x, topk_ids, topk_w, W: QuantizedExperts, act_int8=False, out=No
 
 
 def moe_forward_timed(x, topk_ids, topk_w, W: QuantizedExperts, events, act_int8=False, out=None, workspace=None):
-    """moe_forward that records six caller-created hipEvent_t handles (ints, or
-    None) between its steps; see qre_moe_forward_timed."""
+    """moe_forward that records eight caller-created hipEvent_t handles (ints,
+    or None): six between its steps and the gate/up kernel's own begin and
+    end; see qre_moe_forward_timed."""
     T, H = x.shape
     K = topk_ids.shape[1]
     _need(x, "x", torch.bfloat16, (T, H))
     _need(topk_ids, "topk_ids", torch.int32, (T, K))
     _need(topk_w, "topk_w", torch.float32, (T, K))
-    if len(events) != 6:
-        raise ValueError("six events")
+    if len(events) != 8:
+        raise ValueError("eight events")
     d = _desc(T, H, W.I, W.E, K, W.bits, act_int8)
     if workspace is None:
         workspace = _workspace(workspace_bytes(T, H, W.I, W.E, K, W.bits, act_int8), x.device)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
-    ev = (C.c_void_p * 6)(*[e if e else None for e in events])
+    ev = (C.c_void_p * 8)(*[e if e else None for e in events])
     ws_struct = W._struct()
     _check("qre_moe_forward_timed", _lib().qre_moe_forward_timed(
         C.byref(d), _ptr(x), _ptr(topk_ids), _ptr(topk_w), C.byref(ws_struct), _ptr(out), _ptr(workspace),
@@ -612,20 +613,21 @@ def nvfp4_moe_forward(x, topk_ids, topk_w, W: Nvfp4Experts, out=None, workspace=
 
 
 def nvfp4_moe_forward_timed(x, topk_ids, topk_w, W: Nvfp4Experts, events, out=None, workspace=None):
-    """nvfp4_moe_forward that records six caller-created hipEvent_t handles
-    (ints, or None) between its steps; see qre_nvfp4_moe_forward_timed."""
+    """nvfp4_moe_forward that records eight caller-created hipEvent_t handles
+    (ints, or None): six between its steps and the gate/up kernel's own begin
+    and end; see qre_nvfp4_moe_forward_timed."""
     T, H = x.shape
     K = topk_ids.shape[1]
     _need(x, "x", torch.bfloat16, (T, H))
     _need(topk_ids, "topk_ids", torch.int32, (T, K))
     _need(topk_w, "topk_w", torch.float32, (T, K))
-    if len(events) != 6:
-        raise ValueError("six events")
+    if len(events) != 8:
+        raise ValueError("eight events")
     if workspace is None:
         workspace = _workspace(nvfp4_workspace_bytes(T, H, W.I, W.E, K), x.device)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
-    ev = (C.c_void_p * 6)(*[e if e else None for e in events])
+    ev = (C.c_void_p * 8)(*[e if e else None for e in events])
     ws_struct = W._struct()
     _check("qre_nvfp4_moe_forward_timed", _lib().qre_nvfp4_moe_forward_timed(
         C.byref(_fp4_desc(T, H, W.I, W.E, K)), _ptr(x), _ptr(topk_ids), _ptr(topk_w), C.byref(ws_struct), _ptr(out),

@@ -653,7 +653,7 @@ template <int WB, bool A8, bool DUAL, int FN, int NG, int DEPTH, int BMR>
 hipError_t launch_dec(const GemmProblem& p, hipStream_t stream) {
   using K = Dec16<WB, A8, DUAL, FN, NG, DEPTH, BMR>;
   const dim3 grid((p.n + K::BN - 1) / K::BN, (unsigned)((p.max_tiles + 7) / 8 * 8));
-  hipLaunchKernelGGL((k_gemm_dec<WB, A8, DUAL, FN, NG, DEPTH, BMR>), grid, dim3(256), K::lds_bytes(), stream, p);
+  QRE_LAUNCH_GEMM((k_gemm_dec<WB, A8, DUAL, FN, NG, DEPTH, BMR>), grid, dim3(256), K::lds_bytes(), stream, p);
   return hipGetLastError();
 }
 
@@ -673,7 +673,7 @@ template <int WB, bool A8, bool DUAL, int FN, int GW>
 hipError_t launch_split(const GemmProblem& p, hipStream_t stream) {
   constexpr int BN = 16 * FN;
   const dim3 grid((p.n + BN - 1) / BN, (unsigned)p.max_tiles);
-  hipLaunchKernelGGL((k_gemm16<WB, A8, DUAL, FN, GW>), grid, dim3(256), 0, stream, p);
+  QRE_LAUNCH_GEMM((k_gemm16<WB, A8, DUAL, FN, GW>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -738,11 +738,11 @@ hipError_t launch_routed_ng(const GemmProblem& gu, const GemmProblem& dn, const 
   if (!down) {
     using K = Dec16<WB, A8, true, 1, NG, DEPTH, BMR>;
     const dim3 grid((gu.n + K::BN - 1) / K::BN, ro.E);
-    hipLaunchKernelGGL((k_gate_up_routed<WB, A8, NG, DEPTH, BMR>), grid, dim3(256), K::lds_bytes(), stream, gu, ro);
+    QRE_LAUNCH_GEMM((k_gate_up_routed<WB, A8, NG, DEPTH, BMR>), grid, dim3(256), K::lds_bytes(), stream, gu, ro);
   } else {
     using K = Dec16<WB, A8, false, 2, NG, DEPTH, BMR>;
     const dim3 grid((dn.n + K::BN - 1) / K::BN, ro.E);
-    hipLaunchKernelGGL((k_down_routed<WB, A8, NG, DEPTH, BMR>), grid, dim3(256), K::lds_bytes(), stream, dn,
+    QRE_LAUNCH_GEMM((k_down_routed<WB, A8, NG, DEPTH, BMR>), grid, dim3(256), K::lds_bytes(), stream, dn,
                        ro.counts, ro.offsets);
   }
   return hipGetLastError();

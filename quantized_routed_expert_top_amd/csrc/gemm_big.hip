@@ -745,7 +745,7 @@ template <bool DUAL, int WN, int CBW>
 hipError_t launch_w8a8_wn(const GemmProblem& p, hipStream_t stream) {
   using K = BigW8A8<DUAL, WN, CBW>;
   const dim3 grid(p.n / (K::BNO * CBW), (unsigned)((p.max_tiles + 7) / 8 * 8));
-  hipLaunchKernelGGL((k_gemm_w8a8<DUAL, WN, CBW>), grid, dim3(K::NT), K::lds_bytes(p.kdim / kGroup), stream, p);
+  QRE_LAUNCH_GEMM((k_gemm_w8a8<DUAL, WN, CBW>), grid, dim3(K::NT), K::lds_bytes(p.kdim / kGroup), stream, p);
   return hipGetLastError();
 }
 
@@ -785,7 +785,7 @@ hipError_t launch_big_cfg(const GemmProblem& p, hipStream_t stream) {
   using K = Big<WB, A8, DUAL, WM>;
   if (p.n % (DUAL ? 32 : 64) != 0 || p.bm != K::BM) return hipErrorInvalidValue;
   const dim3 grid((p.n + K::BNO - 1) / K::BNO, (unsigned)((p.max_tiles + 7) / 8 * 8));
-  hipLaunchKernelGGL((k_gemm_big<WB, A8, DUAL, WM>), grid, dim3(256), K::lds_bytes(), stream, p);
+  QRE_LAUNCH_GEMM((k_gemm_big<WB, A8, DUAL, WM>), grid, dim3(256), K::lds_bytes(), stream, p);
   return hipGetLastError();
 }
 

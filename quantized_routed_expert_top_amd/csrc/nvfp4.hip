@@ -410,7 +410,7 @@ hipError_t launch_fp4_ns(const Fp4Problem& p, hipStream_t s) {
   const size_t lds = G::lds_bytes(p.kdim);
   if (lds > kFp4MaxLds) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((p.n + G::BN - 1) / G::BN), (unsigned)p.max_tiles);
-  hipLaunchKernelGGL((k_fp4_gemm<DUAL, FN, BMR, DEPTH, NS>), grid, dim3(256), lds, s, p);
+  QRE_LAUNCH_GEMM((k_fp4_gemm<DUAL, FN, BMR, DEPTH, NS>), grid, dim3(256), lds, s, p);
   return hipGetLastError();
 }
 

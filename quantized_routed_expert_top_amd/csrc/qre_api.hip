@@ -12,6 +12,13 @@
 
 using namespace qre;
 
+namespace qre {
+KernelEvents& kernel_events() {
+  static thread_local KernelEvents ke{nullptr, nullptr};
+  return ke;
+}
+}  // namespace qre
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -413,7 +420,9 @@ static int moe_forward_impl(const qre_desc* desc, const void* x, const int32_t* 
                      d.act_int8 ? &qx : nullptr);
   if (e == hipSuccess && d.act_int8 && routed) e = launch_quantize_act(qx.v, qx.rows, qx.cols, qx.q, qx.s, s);
   if (e == hipSuccess) e = mark(1);
+  if (ev) kernel_events() = KernelEvents{ev[6], ev[7]};   // the gate/up kernel's own begin and end
   if (e == hipSuccess) e = routed ? launch_gate_up_routed(gu, ro, s) : launch_gemm(gu, s);
+  kernel_events() = KernelEvents{nullptr, nullptr};
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess && d.act_int8 && !fused_hq) e = launch_quantize_act(L.h, (int)S, d.I, L.hq, L.hs, s);
   if (e == hipSuccess) e = mark(3);
@@ -718,8 +727,10 @@ static int nvfp4_forward_impl(const qre_desc* desc, const void* x, const int32_t
     if (e == hipSuccess) e = launch_fp4_quantize_act(static_cast<const uint16_t*>(x), d.T, d.H, L.xq, L.xb, L.xr, s);
   }
   if (e == hipSuccess) e = mark(1);
+  if (ev) kernel_events() = KernelEvents{ev[6], ev[7]};   // the gate/up kernel's own begin and end
   if (e == hipSuccess)
     e = launch_fp4_gemm(fp4_gate_up_problem(d, L.xq, L.xb, L.xr, L.sorted_slot, *weights, st, L.h), s);
+  kernel_events() = KernelEvents{nullptr, nullptr};
   if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = launch_fp4_quantize_act(L.h, S, d.I, L.hq, L.hb, L.hr, s);
   if (e == hipSuccess) e = mark(3);

@@ -5,6 +5,7 @@
 // MFMA, LDS.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -200,5 +201,28 @@ hipError_t launch_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, hipSt
 // Router: top-K of E logits per token (one wave per token), softmax weights.
 hipError_t launch_topk_softmax(const float* logits, int T, int E, int K, int32_t* ids, float* w,
                                hipStream_t stream);
+
+// Start and stop events for the next GEMM launch of this thread: the timed
+// forward calls set them just before their gate/up step, and the first GEMM
+// launch takes (and clears) them, so they hold that kernel's own dispatch
+// begin and end (the interval a kernel trace reports).
+struct KernelEvents {
+  hipEvent_t start, stop;
+};
+KernelEvents& kernel_events();
+
+// hipLaunchKernelGGL for the GEMM kernels, or hipExtLaunchKernelGGL with the
+// pending events when there are any.
+#define QRE_LAUNCH_GEMM(kernel, grid, block, shm, stream, ...)                                           \
+  do {                                                                                                    \
+    ::qre::KernelEvents& ke_ = ::qre::kernel_events();                                                    \
+    if (ke_.start || ke_.stop) {                                                                          \
+      const hipEvent_t a_ = ke_.start, z_ = ke_.stop;                                                     \
+      ke_ = ::qre::KernelEvents{nullptr, nullptr};                                                        \
+      hipExtLaunchKernelGGL(kernel, grid, block, (std::uint32_t)(shm), stream, a_, z_, 0u, __VA_ARGS__); \
+    } else {                                                                                              \
+      hipLaunchKernelGGL(kernel, grid, block, shm, stream, __VA_ARGS__);                                  \
+    }                                                                                                     \
+  } while (0)
 
 }  // namespace qre

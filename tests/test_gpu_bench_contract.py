@@ -65,3 +65,78 @@ def test_router_stage_line_with_cpu_baseline():
     _check_common(j, 50, 3)
     cb = j["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+
+
+class _Events:
+    """hipEvent_t handles through ctypes, for the timed forward calls."""
+
+    def __init__(self):
+        import ctypes as C
+        self.C = C
+        self.lib = C.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [C.c_void_p]
+        self.made = []
+
+    def create(self):
+        h = self.C.c_void_p()
+        assert self.lib.hipEventCreate(self.C.byref(h)) == 0
+        self.made.append(h.value)
+        return h.value
+
+    def ms(self, a, b):
+        v = self.C.c_float()
+        assert self.lib.hipEventElapsedTime(self.C.byref(v), a, b) == 0
+        return v.value
+
+    def close(self):
+        for h in self.made:
+            self.lib.hipEventDestroy(h)
+
+
+@pytest.mark.parametrize("name,T,H,I,E,K,bits,a8,fmt", [
+    ("decode_routed", 32, 2048, 512, 256, 8, 4, False, "int"),   # permutation folded into gate/up
+    ("w8a8_big", 512, 512, 256, 16, 4, 8, True, "int"),           # routing launches, 128-row INT8 tiles
+    ("decode_nvfp4", 32, 512, 256, 64, 8, 4, False, "nvfp4"),
+])
+def test_timed_forward_kernel_events(name, T, H, I, E, K, bits, a8, fmt):
+    """The timed forward calls give the untimed call's output bit for bit; the
+    two events handed to the gate/up launch itself bracket a positive
+    interval that lies inside the interval of the events recorded around that
+    step (the dispatch begins after the step's first event and ends before
+    its second)."""
+    import torch
+    import quantized_routed_expert_top_amd as qre
+    from harness.inputs import Workload
+    from harness.synthetic import gpu_problem
+
+    print(f"[timed forward] {name}", flush=True)
+    wl = Workload(name, T=T, H=H, I=I, E=E, K=K, weight_bits=bits, act_int8=a8, fmt=fmt, seed=7)
+    P = gpu_problem(wl, torch.device("cuda:0"))
+    fp4 = fmt == "nvfp4"
+    if fp4:
+        ref = qre.nvfp4_moe_forward(P["x"], P["topk_ids"], P["topk_w"], P["W"])
+    else:
+        ref = qre.moe_forward(P["x"], P["topk_ids"], P["topk_w"], P["W"], act_int8=a8)
+    hip = _Events()
+    try:
+        for _ in range(3):
+            ev = [hip.create() for _ in range(8)]
+            if fp4:
+                out = qre.nvfp4_moe_forward_timed(P["x"], P["topk_ids"], P["topk_w"], P["W"], ev)
+            else:
+                out = qre.moe_forward_timed(P["x"], P["topk_ids"], P["topk_w"], P["W"], ev, act_int8=a8)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref)
+            kernel = hip.ms(ev[6], ev[7])
+            step = hip.ms(ev[1], ev[2])
+            print(f"[timed forward] {name}: gate/up kernel {kernel * 1e3:.2f} us, step {step * 1e3:.2f} us", flush=True)
+            assert kernel > 0
+            # 0.5 us of slack for the rounding of the two timestamp sources
+            assert hip.ms(ev[1], ev[6]) >= -5e-4 and hip.ms(ev[7], ev[2]) >= -5e-4
+        with pytest.raises(ValueError):
+            qre.moe_forward_timed(P["x"], P["topk_ids"], P["topk_w"], P["W"], [None] * 6) if not fp4 else \
+                qre.nvfp4_moe_forward_timed(P["x"], P["topk_ids"], P["topk_w"], P["W"], [None] * 6)
+    finally:
+        hip.close()
