@@ -140,7 +140,7 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(wl, x_bits, ids, w, budget_s=8.0, budget_1t_s=5.0):
+def cpu_baseline(wl, x_bits, ids, w, budget_s=10.0, budget_1t_s=5.0):
     """The oracle as it stands, on this host's cores, over whole blocks of the
     same workload (repeated until ~budget_s of wall time, at least once),
     with all the threads OpenMP gives it and again with one thread."""
