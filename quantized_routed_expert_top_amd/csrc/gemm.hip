@@ -633,9 +633,14 @@ __global__ __launch_bounds__(256) void k_gate_up_routed(GemmProblem p, RouteOut 
   }
 }
 
+// Columns per wave of the routed down GEMM: one 16-column fragment.  With one
+// or two rows per expert a workgroup streams 64 columns x the short
+// reduction, and more, smaller workgroups keep more of the weight stream in
+// flight than two fragments per wave did (about 1 us per decode step).
+constexpr int kDownRoutedFn = 1;
 template <int WB, bool A8, int NG, int DEPTH, int BMR>
 __global__ __launch_bounds__(256) void k_down_routed(GemmProblem p, const int32_t* counts, const int32_t* offsets) {
-  using K = Dec16<WB, A8, false, 2, NG, DEPTH, BMR>;
+  using K = Dec16<WB, A8, false, kDownRoutedFn, NG, DEPTH, BMR>;
   extern __shared__ __attribute__((aligned(16))) uint8_t dec_lds[];
   const int e = blockIdx.y;
   const int count = counts[e], off = offsets[e];
@@ -740,7 +745,7 @@ hipError_t launch_routed_ng(const GemmProblem& gu, const GemmProblem& dn, const 
     const dim3 grid((gu.n + K::BN - 1) / K::BN, ro.E);
     QRE_LAUNCH_GEMM((k_gate_up_routed<WB, A8, NG, DEPTH, BMR>), grid, dim3(256), K::lds_bytes(), stream, gu, ro);
   } else {
-    using K = Dec16<WB, A8, false, 2, NG, DEPTH, BMR>;
+    using K = Dec16<WB, A8, false, kDownRoutedFn, NG, DEPTH, BMR>;
     const dim3 grid((dn.n + K::BN - 1) / K::BN, ro.E);
     QRE_LAUNCH_GEMM((k_down_routed<WB, A8, NG, DEPTH, BMR>), grid, dim3(256), K::lds_bytes(), stream, dn,
                        ro.counts, ro.offsets);
